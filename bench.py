@@ -1,0 +1,227 @@
+"""Benchmark of the fused multi-LoRA MoE expert layer on one MI355X.
+
+One step = one full layer call (route, align, gate_up shrink, gate_up
+projection with fused LoRA expand + SwiGLU, down shrink, down projection with
+fused LoRA expand, weighted combine) over one batch of synthetic tokens whose
+inputs are already resident in HBM.
+
+Default workload: the decode-shaped layer (16 tokens, hidden = intermediate =
+2880, 32 experts top-4, 8 adapters of rank 32). The prefill-shaped layer
+(4 x 1600 tokens, same dims) is measured in the same run and reported in the
+"prefill" object of the same JSON line.
+
+Weight copies are rotated between calls so that the working set of
+consecutive calls exceeds the 256 MB Infinity Cache.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+WORKLOAD_NAMES = {"decode": "decode-shaped MoE-LoRA layer (T=16, H=I=2880, E=32 top-4, L=8, r=32)",
+                  "prefill": "prefill-shaped MoE-LoRA layer (T=6400=4x1600, H=I=2880, E=32 top-4, L=8, r=32)",
+                  "wide": "wide-expert layer (T=64, H=4096, I=11008, E=8 top-2, L=8, r=32)",
+                  "many": "many-adapter layer (T=512, H=I=2880, E=32 top-4, L=128, r=64)"}
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def routing_stats(case, ids):
+    """Touched experts / (expert, adapter) segments of the sampled routing."""
+    T, k, L = case.T, case.top_k, case.L
+    experts = np.unique(ids)
+    segs = set()
+    p_lora = 0
+    for t in range(T):
+        a = int(case.adapter_ids[t])
+        if 0 <= a < L:
+            p_lora += k
+            for e in ids[t]:
+                segs.add((a, int(e)))
+    return dict(n_experts=len(experts), n_segments=len(segs), P=T * k, P_lora=p_lora)
+
+
+def algorithmic(case, st):
+    """Algorithmic bytes / flops per kernel (inputs read once, outputs written
+    once, intermediates counted only where a kernel must read/write them)."""
+    H, I, r, T, k = case.H, case.I, case.r, case.T, case.top_k
+    P, PL, ne, ns = st["P"], st["P_lora"], st["n_experts"], st["n_segments"]
+    b = {}
+    b["shrink_gate_up"] = ns * r * H * 2 + PL * H * 2 + PL * r * 4
+    b["gemm_gate_up"] = ne * 2 * I * H * 2 + ns * 2 * I * r * 2 + T * H * 2 + PL * r * 4 + P * I * 2
+    b["shrink_down"] = ns * r * I * 2 + PL * I * 2 + PL * r * 4
+    b["gemm_down"] = ne * H * I * 2 + ns * H * r * 2 + P * I * 2 + PL * r * 4 + P * H * 4
+    b["combine"] = P * H * 4 + T * H * 4 + P * 8
+    b["route"] = T * case.E * 4 + P * 8
+    b["align"] = P * 4 + T * 4
+    f = {}
+    f["gemm_gate_up"] = 2.0 * P * 2 * I * H + 2.0 * PL * 2 * I * r
+    f["gemm_down"] = 2.0 * P * H * I + 2.0 * PL * H * r
+    f["shrink_gate_up"] = 2.0 * PL * r * H
+    f["shrink_down"] = 2.0 * PL * r * I
+    layer_bytes = ne * 3 * H * I * 2 + ns * r * (2 * H + 3 * I) * 2 + T * H * 2 + T * case.E * 4 + T * H * 4
+    layer_flops = 6.0 * H * I * P + 2.0 * r * (2 * H + 3 * I) * PL
+    return b, f, layer_bytes, layer_flops
+
+
+def run_workload(name, steps, warmup, rotate, dev):
+    import torch
+
+    import oracle
+    from lora_mixture_experts_amd import moe_lora as ml
+    from lora_mixture_experts_amd import workloads as wl
+
+    t0 = time.time()
+    case = wl.make_case(name)
+    ids, _ = oracle.route(case.logits, case.top_k)
+    st = routing_stats(case, ids)
+    log(f"[{name}] inputs drawn in {time.time() - t0:.1f}s; {st}")
+    base = wl.device_tensors(case, dev)
+    layers = []
+    for i in range(rotate):
+        tens = base if i == 0 else {k: v.clone() for k, v in base.items()}
+        layers.append((ml.Layer(case.T, case.H, case.I, case.E, case.top_k, case.L, case.r,
+                                tens["w_gate_up"], tens["w_down"], tens["a_gate_up"],
+                                tens["b_gate_up"], tens["a_down"], tens["b_down"]), tens))
+    out = torch.empty((case.T, case.H), dtype=torch.float32, device=dev)
+
+    def step(i):
+        layer, tens = layers[i % rotate]
+        layer(tens["x"], tens["logits"], tens["adapter_ids"], out=out)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for i in range(steps):
+        step(i)
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / steps
+
+    # per-kernel durations: HIP events recorded by the library around each
+    # kernel on the launch stream, over a second pass of the same steps
+    ml.timing_enable(steps)
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    kms, ncalls = ml.timing_read()
+    ml.timing_enable(0)
+    kernel_us = {n: 1000.0 * v / max(ncalls, 1) for n, v in zip(ml.kernel_names(), kms)}
+    b, f, layer_bytes, layer_flops = algorithmic(case, st)
+    del layers, base
+    torch.cuda.empty_cache()
+    return case, ids, st, ms, kernel_us, b, f, layer_bytes, layer_flops
+
+
+def cpu_baseline(case, ids, budget_s):
+    import oracle
+    w = None
+    ids_, w = oracle.route(case.logits, case.top_k)
+    cores = oracle.default_threads()
+    # bounded sample: whole token batches until the time budget is used
+    n_tok = case.T
+    toks = np.arange(n_tok, dtype=np.int32)
+    done, t0 = 0, time.perf_counter()
+    while True:
+        oracle.forward(case, ids_, w, tokens=toks, threads=cores)
+        done += n_tok
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return dict(value=done / dt, unit="tokens/s", cores=cores, kind="oracle",
+                sample=f"{done} tokens ({done // n_tok} full {case.name} batches of {n_tok}) "
+                       f"through the fp64 C oracle in {dt:.1f}s")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="decode", choices=list(WORKLOAD_NAMES))
+    ap.add_argument("--also", default="prefill", help="second workload reported in the same line ('' = none)")
+    ap.add_argument("--rotate", type=int, default=3)
+    ap.add_argument("--cpu-budget", type=float, default=10.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the layer's multi-GPU sharding is a design, not a built path)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    dev = torch.device("cuda:0")
+    case, ids, st, ms, kus, b, f, lbytes, lflops = run_workload(args.workload, args.steps, args.warmup,
+                                                               args.rotate, dev)
+    dom = max(("gemm_gate_up", "gemm_down"), key=lambda n: kus[n])
+    hbm_bound = case.T * case.top_k / max(st["n_experts"], 1) < 312
+    if hbm_bound:
+        achieved = b[dom] / (kus[dom] * 1e-6) / 1e9
+        roof = dict(kernel=dom, bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None,
+                    bytes_per_launch=b[dom], us_per_launch=round(kus[dom], 2))
+    else:
+        achieved = f[dom] / (kus[dom] * 1e-6) / 1e12
+        roof = dict(kernel=dom, bound="mfma", achieved=round(achieved, 1), peak=BF16_PEAK_TFLOPS,
+                    unit="TFLOP/s", frac=round(achieved / BF16_PEAK_TFLOPS, 4), traffic=None,
+                    flops_per_launch=f[dom], us_per_launch=round(kus[dom], 2))
+    layer_roof_us = max(lbytes / (HBM_PEAK_GBS * 1e9), lflops / (BF16_PEAK_TFLOPS * 1e12)) * 1e6
+    lora_us = kus["shrink_gate_up"] + kus["shrink_down"]
+    lora_bytes = b["shrink_gate_up"] + b["shrink_down"]
+    line = {
+        "metric": "MoE-LoRA layer tokens/s + us/call (decode 16 tok, prefill 6400 tok); % roofline",
+        "value": round(case.T / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "us_per_call": round(ms * 1e3, 2),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded, N(0,1) activations/logits, N(0,0.02) weights)",
+        "config": {"workload": WORKLOAD_NAMES[args.workload], "global_batch": case.T, "seq_len": 1,
+                   "parallelism": "none (1 GPU)", "rotated_weight_copies": args.rotate},
+        "layer_roofline_frac": round(layer_roof_us / (ms * 1e3), 4),
+        "kernel_us": {k: round(v, 2) for k, v in kus.items()},
+        "lora_shrink_hbm_frac": round(lora_bytes / (lora_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4) if lora_us else None,
+        "routing": st,
+        "roofline": roof,
+    }
+    if args.also:
+        c2, ids2, st2, ms2, kus2, b2, f2, lb2, lf2 = run_workload(args.also, max(5, args.steps // 5),
+                                                                   max(2, args.warmup // 2),
+                                                                   args.rotate, dev)
+        dom2 = max(("gemm_gate_up", "gemm_down"), key=lambda n: kus2[n])
+        gemm_us = kus2["gemm_gate_up"] + kus2["gemm_down"]
+        gemm_tf = (f2["gemm_gate_up"] + f2["gemm_down"]) / (gemm_us * 1e-6) / 1e12
+        lroof = max(lb2 / (HBM_PEAK_GBS * 1e9), lf2 / (BF16_PEAK_TFLOPS * 1e12)) * 1e6
+        line["prefill" if args.also == "prefill" else args.also] = {
+            "workload": WORKLOAD_NAMES[args.also], "value": round(c2.T / (ms2 * 1e-3), 1),
+            "unit": "tokens/s", "us_per_call": round(ms2 * 1e3, 2),
+            "layer_roofline_frac": round(lroof / (ms2 * 1e3), 4),
+            "kernel_us": {k: round(v, 2) for k, v in kus2.items()},
+            "base_gemms_tflops": round(gemm_tf, 1),
+            "base_gemms_mfma_frac": round(gemm_tf / BF16_PEAK_TFLOPS, 4),
+            "roofline": dict(kernel=dom2, bound="mfma",
+                             achieved=round(f2[dom2] / (kus2[dom2] * 1e-6) / 1e12, 1),
+                             peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
+                             frac=round(f2[dom2] / (kus2[dom2] * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                             traffic=None),
+        }
+    if args.cpu_budget > 0:
+        line["cpu_baseline"] = cpu_baseline(case, ids, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

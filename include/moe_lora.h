@@ -1,0 +1,159 @@
+/*
+ * moe_lora.h -- C ABI of libmoelora.so: the fused multi-LoRA Mixture-of-Experts
+ * expert layer for AMD Instinct MI355X (gfx950).
+ *
+ * The layer (AWS ML Blog post "Efficiently serve dozens of fine-tuned models
+ * with vLLM on Amazon SageMaker AI and Amazon Bedrock"; Korean summary on
+ * agentlenshq.com, section "Multi-LoRA serving for MoE"):
+ *   for every token t with adapter a_t (-1 or out of range = no adapter) and
+ *   each of its top_k experts e (weights w renormalised over the k chosen):
+ *     g  = W_gu[e] x_t + B_gu[a][e] (A_gu[a][e] x_t)        gate_up + LoRA
+ *     h  = silu(g[0:I]) * g[I:2I]                              SwiGLU
+ *     d  = W_d[e] h + B_d[a][e] (A_d[a][e] h)                  down + LoRA
+ *     out_t = sum_j w_j d                                      combine
+ *   The LoRA terms are skipped for tokens without an adapter; LoRA scale 1.
+ *
+ * Conventions shared by every entry point:
+ *  - All tensor pointers are DEVICE pointers owned by the caller. The library
+ *    never allocates device memory in these calls and never frees caller
+ *    memory; intermediates live in the caller's workspace.
+ *  - bf16 tensors are raw bf16 bit patterns (uint16). Layouts are row-major
+ *    with the reduction dimension contiguous, like a PyTorch Linear weight.
+ *  - `stream` is a hipStream_t (NULL = the default stream). Calls only enqueue
+ *    work on it; none synchronises the host.
+ *  - Calls sharing a workspace must be ordered on one stream; calls on
+ *    different streams need distinct workspaces.
+ *  - Return value: MOE_LORA_OK (0) or a negative error code; nothing is
+ *    enqueued when a call returns an argument error.
+ */
+#ifndef MOE_LORA_H
+#define MOE_LORA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_LORA_OK 0
+#define MOE_LORA_EINVAL (-1)     /* bad dimension, null/misaligned pointer, bad block size */
+#define MOE_LORA_EWORKSPACE (-2) /* workspace smaller than moe_lora_workspace_bytes() */
+#define MOE_LORA_EHIP (-3)       /* a HIP launch or runtime call failed */
+
+/* Shape of one layer call.
+ *   T tokens (T == 0 is a no-op), H hidden size, I expert intermediate size
+ *   (gate_up produces 2I), E experts, top_k experts per token (1..min(E,32)),
+ *   L adapter slots (0 = no adapters), r LoRA rank (one of 8,16,32,64,128).
+ *   H and I must be multiples of 64.
+ *   block_m_base / block_m_lora: rows per block of the two alignment views;
+ *   0 = library default; else a power of two in [16, 256].
+ *   flags: reserved, must be 0. */
+typedef struct moe_lora_desc {
+    int32_t T, H, I, E, top_k, L, r;
+    int32_t block_m_base, block_m_lora;
+    int32_t flags;
+} moe_lora_desc;
+
+/* Weights (device pointers, bf16 bits, 16-byte aligned).
+ *   w_gate_up [E][2I][H]   rows 0..I-1 = gate, rows I..2I-1 = up
+ *   w_down    [E][H][I]
+ *   a_gate_up [L][E][r][H]   LoRA shrink of gate_up (x . A^T)
+ *   b_gate_up [L][E][2I][r]  LoRA expand of gate_up
+ *   a_down    [L][E][r][I]
+ *   b_down    [L][E][H][r]
+ * The four LoRA pointers may be NULL when L == 0. */
+typedef struct moe_lora_weights {
+    const void *w_gate_up, *w_down;
+    const void *a_gate_up, *b_gate_up, *a_down, *b_down;
+} moe_lora_weights;
+
+/* Human-readable text of an error code (static storage). */
+const char *moe_lora_strerror(int code);
+
+/* Host-only argument check, touches no device. `w` may be NULL (then only the
+ * descriptor is checked); ws_bytes is compared against the workspace size
+ * unless it is (size_t)-1. */
+int moe_lora_validate(const moe_lora_desc *d, const moe_lora_weights *w, size_t ws_bytes);
+
+/* Block sizes the library uses for this descriptor (resolves the 0 defaults). */
+int moe_lora_block_sizes(const moe_lora_desc *d, int32_t *block_m_base, int32_t *block_m_lora);
+
+/* Workspace bytes moe_lora_forward needs for this descriptor. */
+int moe_lora_workspace_bytes(const moe_lora_desc *d, size_t *bytes);
+
+/* Capacities of the two alignment views (lengths of sorted_b / sorted_l):
+ *   C_b = roundup(P + min(E, P)(BMb - 1), BMb),
+ *   C_l = roundup(P + min(E L, P)(BMl - 1), BMl),   P = T top_k. */
+int moe_lora_align_capacity(const moe_lora_desc *d, int32_t *C_b, int32_t *C_l);
+
+/* Routing (AWS post, section "Implementing multi-LoRA inference for MoE models
+ * in vLLM": the router sends each token to its most relevant experts).
+ *   logits   f32 [T][E]  (finite values)
+ *   topk_ids i32 [T][k]  the k largest logits, largest first; on equal values
+ *                        the lower expert id comes first
+ *   topk_w   f32 [T][k]  softmax over the k selected logits */
+int moe_lora_route(const moe_lora_desc *d, const float *logits, int32_t *topk_ids,
+                   float *topk_w, void *stream);
+
+/* Alignment: the compound expert x adapter grouping (AWS post, section
+ * "Tuning kernel configurations for Amazon SageMaker AI and Amazon Bedrock":
+ * the LoRA kernels carry an extra grid axis over adapters and see the sparsity
+ * of several adapters on top of expert routing).
+ * Pairs p = t*k + j are ordered by (expert, a', p), a' = adapter if in [0,L)
+ * else L. Base view: per expert in id order, its pairs, padded with the
+ * sentinel P to a multiple of block_m_base. LoRA view: per (expert, adapter)
+ * segment with adapter < L, experts then adapters ascending, padded to
+ * block_m_lora. Output (device):
+ *   sorted_b i32 [C_b]        slot -> pair id (P = padding)
+ *   blk_e_b  i32 [C_b/BMb]    block -> expert (-1 past the used blocks)
+ *   n_b      i32 [1]          used length of sorted_b
+ *   sorted_l i32 [C_l], blk_e_l, blk_a_l i32 [C_l/BMl], n_l i32 [1]: LoRA view
+ * The result is deterministic (no order-dependent atomics).
+ * Limit: E*(L+1) <= 16384 and T*top_k <= 2^24. */
+int moe_lora_align(const moe_lora_desc *d, const int32_t *topk_ids, const int32_t *adapter_ids,
+                   int32_t *sorted_b, int32_t *blk_e_b, int32_t *n_b,
+                   int32_t *sorted_l, int32_t *blk_e_l, int32_t *blk_a_l, int32_t *n_l,
+                   void *stream);
+
+/* The whole layer.
+ *   x           bf16 [T][H]
+ *   logits      f32  [T][E]
+ *   adapter_ids i32  [T]   (-1 or any id outside [0, L) = no adapter)
+ *   out         f32  [T][H] (overwritten)
+ *   workspace   device buffer of >= moe_lora_workspace_bytes() bytes, 256-byte
+ *               aligned; it holds the routing, alignment and intermediates of
+ *               this call until the next call that uses it.
+ * The gate_up and down LoRA expands add into the base projections' results
+ * inside the projection kernels (AWS post, section "Kernel optimizations":
+ * the LoRA add is fused into the expand). */
+int moe_lora_forward(const moe_lora_desc *d, const moe_lora_weights *w, const void *x,
+                     const float *logits, const int32_t *adapter_ids, float *out,
+                     void *workspace, size_t ws_bytes, void *stream);
+
+/* Copy intermediates of the last moe_lora_forward on `workspace` out in pair
+ * order (row p = t*k + j); any output may be NULL.
+ *   topk_ids i32 [P], topk_w f32 [P]
+ *   s1 f32 [P][r]  gate_up shrink x.A^T   (0 rows for pairs without adapter)
+ *   h  bf16 [P][I] activation as fed to the down projection
+ *   s2 f32 [P][r]  down shrink h.A^T       (0 rows for pairs without adapter)
+ *   dn f32 [P][H]  down projection output incl. LoRA, before the weighting */
+int moe_lora_read_stages(const moe_lora_desc *d, const void *workspace, size_t ws_bytes,
+                         int32_t *topk_ids, float *topk_w, float *s1, uint16_t *h,
+                         float *s2, float *dn, void *stream);
+
+/* Per-kernel timing of moe_lora_forward, for profiling only (process-global,
+ * not thread-safe). moe_lora_timing_enable(n) makes the next n forward calls
+ * record HIP events around each of their kernels on their stream (n = 0 turns
+ * it off). moe_lora_timing_read synchronises those events and returns the
+ * summed milliseconds per kernel (ms[i], i < MOE_LORA_NKERNELS, in the order
+ * of moe_lora_kernel_name) and the number of calls recorded, then resets. */
+#define MOE_LORA_NKERNELS 7
+int moe_lora_timing_enable(int32_t max_calls);
+int moe_lora_timing_read(float *ms, int32_t *ncalls);
+const char *moe_lora_kernel_name(int32_t i);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_LORA_H */

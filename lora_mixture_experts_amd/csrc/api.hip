@@ -1,0 +1,360 @@
+// C ABI of libmoelora: argument checks, workspace layout and the launch
+// sequence of the multi-LoRA MoE expert layer (see include/moe_lora.h).
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+#include <vector>
+
+#include "../../include/moe_lora.h"
+#include "kernels.h"
+
+using namespace moelora;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+bool pow2_in(int v, int lo, int hi) { return v >= lo && v <= hi && (v & (v - 1)) == 0; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Plan {
+    int T, H, I, E, k, L, r, P;
+    int bm_b, bm_l, C_b, C_l, nblk_b, nblk_l, ns1, ns2;
+    size_t off_ids, off_w, off_sorted_b, off_blk_e_b, off_counts, off_sorted_l, off_blk_e_l,
+        off_blk_a_l, off_slot, off_lslot, off_s1, off_s2, off_h, off_d, total;
+};
+
+int roundup_i(long v, long m) { return static_cast<int>((v + m - 1) / m * m); }
+
+// K split of the shrink: enough workgroups to cover the chip, every split at
+// least 4 K steps of 32 (one per wave).
+int pick_split(int K, int nblk) {
+    const int steps = K / 32;
+    if (nblk <= 0) return 1;
+    const int target = nblk >= 1024 ? 1 : (1024 + nblk - 1) / nblk;
+    int best = 1;
+    for (int d = 1; d <= steps; ++d)
+        if (steps % d == 0 && d <= target && steps / d >= 4) best = d;
+    return best;
+}
+
+int default_bm_base(int P, int E) {
+    const long avg = (P + E - 1) / E;  // mean rows per expert
+    if (2 * avg <= 16) return 16;
+    if (2 * avg <= 32) return 32;
+    if (2 * avg <= 64) return 64;
+    return 128;
+}
+
+int default_bm_lora(int P, int E, int L) {
+    const long segs = std::min<long>(static_cast<long>(E) * (L > 0 ? L : 1), P > 0 ? P : 1);
+    const long avg = (P + segs - 1) / segs;
+    return avg >= 64 ? 64 : 16;
+}
+
+int check_desc(const moe_lora_desc* d) {
+    if (!d) return MOE_LORA_EINVAL;
+    if (d->T < 0 || d->H <= 0 || d->I <= 0 || d->E <= 0 || d->L < 0) return MOE_LORA_EINVAL;
+    if (d->H % 64 || d->I % 64) return MOE_LORA_EINVAL;
+    if (d->E > 1024 || d->top_k < 1 || d->top_k > d->E || d->top_k > 32) return MOE_LORA_EINVAL;
+    if (d->L > 0 && !(d->r == 8 || d->r == 16 || d->r == 32 || d->r == 64 || d->r == 128))
+        return MOE_LORA_EINVAL;
+    if (d->flags != 0) return MOE_LORA_EINVAL;
+    if (d->block_m_base != 0 && !pow2_in(d->block_m_base, 16, 256)) return MOE_LORA_EINVAL;
+    if (d->block_m_lora != 0 && !pow2_in(d->block_m_lora, 16, 256)) return MOE_LORA_EINVAL;
+    const long P = static_cast<long>(d->T) * d->top_k;
+    if (P > (1L << 24)) return MOE_LORA_EINVAL;
+    if (static_cast<long>(d->E) * (d->L + 1) > 16384) return MOE_LORA_EINVAL;
+    if (align_hist_waves(d->E, d->L) <= 0) return MOE_LORA_EINVAL;
+    return MOE_LORA_OK;
+}
+
+int make_plan(const moe_lora_desc* d, Plan* p) {
+    const int rc = check_desc(d);
+    if (rc) return rc;
+    p->T = d->T; p->H = d->H; p->I = d->I; p->E = d->E; p->k = d->top_k; p->L = d->L;
+    p->r = d->L > 0 ? d->r : 8;
+    p->P = d->T * d->top_k;
+    p->bm_b = d->block_m_base ? d->block_m_base : default_bm_base(p->P, p->E);
+    p->bm_l = d->block_m_lora ? d->block_m_lora : default_bm_lora(p->P, p->E, p->L);
+    if (!gemm_supported(p->I, p->H, 1, p->bm_b) || !gemm_supported(p->H, p->I, 0, p->bm_b))
+        return MOE_LORA_EINVAL;
+    const long P = p->P;
+    p->C_b = roundup_i(P + std::min<long>(p->E, P) * (p->bm_b - 1), p->bm_b);
+    p->C_l = roundup_i(P + std::min<long>(static_cast<long>(p->E) * p->L, P) * (p->bm_l - 1), p->bm_l);
+    p->nblk_b = p->C_b / p->bm_b;
+    p->nblk_l = p->C_l / p->bm_l;
+    p->ns1 = pick_split(p->H, p->nblk_l);
+    p->ns2 = pick_split(p->I, p->nblk_l);
+    size_t o = 0;
+    auto take = [&](size_t bytes) { const size_t at = o; o += up(bytes); return at; };
+    p->off_ids = take(4 * P);
+    p->off_w = take(4 * P);
+    p->off_sorted_b = take(4ul * p->C_b);
+    p->off_blk_e_b = take(4ul * p->nblk_b);
+    p->off_counts = take(64);
+    p->off_sorted_l = take(4ul * p->C_l);
+    p->off_blk_e_l = take(4ul * p->nblk_l);
+    p->off_blk_a_l = take(4ul * p->nblk_l);
+    p->off_slot = take(4 * P);
+    p->off_lslot = take(4 * P);
+    p->off_s1 = take(p->L > 0 ? 4ul * p->ns1 * p->C_b * p->r : 0);
+    p->off_s2 = take(p->L > 0 ? 4ul * p->ns2 * p->C_b * p->r : 0);
+    p->off_h = take(2ul * p->C_b * p->I);
+    p->off_d = take(4ul * p->C_b * p->H);
+    p->total = o;
+    return MOE_LORA_OK;
+}
+
+int check_weights(const moe_lora_desc* d, const moe_lora_weights* w) {
+    if (!w) return MOE_LORA_EINVAL;
+    if (!w->w_gate_up || !w->w_down || !aligned16(w->w_gate_up) || !aligned16(w->w_down))
+        return MOE_LORA_EINVAL;
+    if (d->L > 0) {
+        const void* l[4] = {w->a_gate_up, w->b_gate_up, w->a_down, w->b_down};
+        for (const void* q : l)
+            if (!q || !aligned16(q)) return MOE_LORA_EINVAL;
+    }
+    return MOE_LORA_OK;
+}
+
+template <typename T>
+T* at(void* base, size_t off) {
+    return reinterpret_cast<T*>(static_cast<char*>(base) + off);
+}
+
+// ---- per-kernel timing --------------------------------------------------
+const char* kKernelNames[MOE_LORA_NKERNELS] = {"route", "align", "shrink_gate_up", "gemm_gate_up",
+                                               "shrink_down", "gemm_down", "combine"};
+struct Timing {
+    int max_calls = 0;
+    int ncalls = 0;
+    std::vector<hipEvent_t> ev;  // [max_calls][NKERNELS + 1]
+} g_timing;
+
+void timing_mark(int call, int i, hipStream_t s) {
+    if (call >= 0) hipEventRecord(g_timing.ev[static_cast<size_t>(call) * (MOE_LORA_NKERNELS + 1) + i], s);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_lora_strerror(int code) {
+    switch (code) {
+        case MOE_LORA_OK: return "ok";
+        case MOE_LORA_EINVAL: return "invalid argument (dimension, pointer, alignment or block size)";
+        case MOE_LORA_EWORKSPACE: return "workspace too small";
+        case MOE_LORA_EHIP: return "HIP runtime or launch error";
+        default: return "unknown error";
+    }
+}
+
+int moe_lora_validate(const moe_lora_desc* d, const moe_lora_weights* w, size_t ws_bytes) {
+    Plan p;
+    int rc = make_plan(d, &p);
+    if (rc) return rc;
+    if (w && (rc = check_weights(d, w))) return rc;
+    if (ws_bytes != static_cast<size_t>(-1) && ws_bytes < p.total) return MOE_LORA_EWORKSPACE;
+    return MOE_LORA_OK;
+}
+
+int moe_lora_block_sizes(const moe_lora_desc* d, int32_t* bm_b, int32_t* bm_l) {
+    Plan p;
+    const int rc = make_plan(d, &p);
+    if (rc) return rc;
+    if (bm_b) *bm_b = p.bm_b;
+    if (bm_l) *bm_l = p.bm_l;
+    return MOE_LORA_OK;
+}
+
+int moe_lora_workspace_bytes(const moe_lora_desc* d, size_t* bytes) {
+    Plan p;
+    const int rc = make_plan(d, &p);
+    if (rc) return rc;
+    if (!bytes) return MOE_LORA_EINVAL;
+    *bytes = p.total;
+    return MOE_LORA_OK;
+}
+
+int moe_lora_align_capacity(const moe_lora_desc* d, int32_t* C_b, int32_t* C_l) {
+    Plan p;
+    const int rc = make_plan(d, &p);
+    if (rc) return rc;
+    if (C_b) *C_b = p.C_b;
+    if (C_l) *C_l = p.C_l;
+    return MOE_LORA_OK;
+}
+
+int moe_lora_route(const moe_lora_desc* d, const float* logits, int32_t* ids, float* w,
+                   void* stream) {
+    const int rc = check_desc(d);
+    if (rc) return rc;
+    if (d->T == 0) return MOE_LORA_OK;
+    if (!logits || !ids || !w) return MOE_LORA_EINVAL;
+    return launch_route(logits, d->T, d->E, d->top_k, ids, w, static_cast<hipStream_t>(stream)) ==
+                   hipSuccess
+               ? MOE_LORA_OK
+               : MOE_LORA_EHIP;
+}
+
+int moe_lora_align(const moe_lora_desc* d, const int32_t* topk_ids, const int32_t* adapter_ids,
+                   int32_t* sorted_b, int32_t* blk_e_b, int32_t* n_b, int32_t* sorted_l,
+                   int32_t* blk_e_l, int32_t* blk_a_l, int32_t* n_l, void* stream) {
+    Plan p;
+    const int rc = make_plan(d, &p);
+    if (rc) return rc;
+    if (d->T == 0) return MOE_LORA_OK;
+    if (!topk_ids || !adapter_ids || !sorted_b || !blk_e_b || !n_b || !sorted_l || !blk_e_l ||
+        !blk_a_l || !n_l)
+        return MOE_LORA_EINVAL;
+    return launch_align(topk_ids, adapter_ids, p.T, p.k, p.E, p.L, p.bm_b, p.bm_l, p.C_b, p.C_l,
+                        sorted_b, blk_e_b, n_b, sorted_l, blk_e_l, blk_a_l, n_l, nullptr,
+                        nullptr, static_cast<hipStream_t>(stream)) == hipSuccess
+               ? MOE_LORA_OK
+               : MOE_LORA_EHIP;
+}
+
+int moe_lora_forward(const moe_lora_desc* d, const moe_lora_weights* w, const void* x,
+                     const float* logits, const int32_t* adapter_ids, float* out,
+                     void* workspace, size_t ws_bytes, void* stream) {
+    Plan p;
+    int rc = make_plan(d, &p);
+    if (rc) return rc;
+    if ((rc = check_weights(d, w))) return rc;
+    if (p.T == 0) return MOE_LORA_OK;
+    if (!x || !logits || !adapter_ids || !out || !workspace) return MOE_LORA_EINVAL;
+    if (!aligned16(x) || !aligned16(out) || (reinterpret_cast<uintptr_t>(workspace) % kAlign))
+        return MOE_LORA_EINVAL;
+    if (ws_bytes < p.total) return MOE_LORA_EWORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+
+    int32_t* ids = at<int32_t>(workspace, p.off_ids);
+    float* tw = at<float>(workspace, p.off_w);
+    int32_t* sorted_b = at<int32_t>(workspace, p.off_sorted_b);
+    int32_t* blk_e_b = at<int32_t>(workspace, p.off_blk_e_b);
+    int32_t* counts = at<int32_t>(workspace, p.off_counts);
+    int32_t* sorted_l = at<int32_t>(workspace, p.off_sorted_l);
+    int32_t* blk_e_l = at<int32_t>(workspace, p.off_blk_e_l);
+    int32_t* blk_a_l = at<int32_t>(workspace, p.off_blk_a_l);
+    int32_t* slot = at<int32_t>(workspace, p.off_slot);
+    int32_t* lslot = at<int32_t>(workspace, p.off_lslot);
+    float* s1 = at<float>(workspace, p.off_s1);
+    float* s2 = at<float>(workspace, p.off_s2);
+    uint16_t* h = at<uint16_t>(workspace, p.off_h);
+    float* dn = at<float>(workspace, p.off_d);
+
+    int call = -1;
+    if (g_timing.max_calls > 0 && g_timing.ncalls < g_timing.max_calls) call = g_timing.ncalls++;
+
+    hipError_t e = hipSuccess;
+    auto ok = [&](hipError_t v) { if (e == hipSuccess) e = v; };
+    timing_mark(call, 0, s);
+    ok(launch_route(logits, p.T, p.E, p.k, ids, tw, s));
+    timing_mark(call, 1, s);
+    ok(launch_align(ids, adapter_ids, p.T, p.k, p.E, p.L, p.bm_b, p.bm_l, p.C_b, p.C_l, sorted_b,
+                    blk_e_b, counts, sorted_l, blk_e_l, blk_a_l, counts + 1, slot, lslot, s));
+    timing_mark(call, 2, s);
+
+    ShrinkArgs sa{};
+    sa.top_k = p.k; sa.P = p.P; sa.sorted_l = sorted_l; sa.blk_e_l = blk_e_l;
+    sa.blk_a_l = blk_a_l; sa.slot_of_pair = slot; sa.E = p.E; sa.r = p.r; sa.bm_l = p.bm_l;
+    sa.n_blocks = p.nblk_l; sa.C_b = p.C_b;
+    if (p.L > 0) {
+        sa.X = static_cast<const uint16_t*>(x); sa.gather_token = 1; sa.K = p.H;
+        sa.A = static_cast<const uint16_t*>(w->a_gate_up); sa.nsplit = p.ns1; sa.S_part = s1;
+        ok(launch_shrink(sa, s));
+    }
+    timing_mark(call, 3, s);
+
+    GemmArgs ga{};
+    ga.sorted_b = sorted_b; ga.blk_e_b = blk_e_b; ga.P = p.P; ga.top_k = p.k; ga.bm_b = p.bm_b;
+    ga.n_blocks = p.nblk_b; ga.adapter_ids = adapter_ids; ga.L = p.L; ga.E = p.E; ga.r = p.r;
+    ga.C_b = p.C_b; ga.h_out = h; ga.d_out = dn;
+    ga.X = static_cast<const uint16_t*>(x); ga.gate_up = 1;
+    ga.W = static_cast<const uint16_t*>(w->w_gate_up); ga.N_out = p.I; ga.K = p.H;
+    ga.S_part = s1; ga.nsplit = p.ns1; ga.Bl = static_cast<const uint16_t*>(w->b_gate_up);
+    ok(launch_gemm(ga, s));
+    timing_mark(call, 4, s);
+
+    if (p.L > 0) {
+        sa.X = h; sa.gather_token = 0; sa.K = p.I;
+        sa.A = static_cast<const uint16_t*>(w->a_down); sa.nsplit = p.ns2; sa.S_part = s2;
+        ok(launch_shrink(sa, s));
+    }
+    timing_mark(call, 5, s);
+
+    ga.X = h; ga.gate_up = 0; ga.W = static_cast<const uint16_t*>(w->w_down); ga.N_out = p.H;
+    ga.K = p.I; ga.S_part = s2; ga.nsplit = p.ns2; ga.Bl = static_cast<const uint16_t*>(w->b_down);
+    ok(launch_gemm(ga, s));
+    timing_mark(call, 6, s);
+
+    ok(launch_combine(dn, slot, tw, p.T, p.k, p.H, out, s));
+    timing_mark(call, 7, s);
+    return e == hipSuccess ? MOE_LORA_OK : MOE_LORA_EHIP;
+}
+
+int moe_lora_read_stages(const moe_lora_desc* d, const void* workspace, size_t ws_bytes,
+                         int32_t* topk_ids, float* topk_w, float* s1, uint16_t* h, float* s2,
+                         float* dn, void* stream) {
+    Plan p;
+    const int rc = make_plan(d, &p);
+    if (rc) return rc;
+    if (p.T == 0) return MOE_LORA_OK;
+    if (!workspace) return MOE_LORA_EINVAL;
+    if (ws_bytes < p.total) return MOE_LORA_EWORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    void* ws = const_cast<void*>(workspace);
+    const int32_t* slot = at<int32_t>(ws, p.off_slot);
+    hipError_t e = hipSuccess;
+    auto ok = [&](hipError_t v) { if (e == hipSuccess) e = v; };
+    if (topk_ids)
+        ok(hipMemcpyAsync(topk_ids, at<int32_t>(ws, p.off_ids), 4ul * p.P, hipMemcpyDeviceToDevice, s));
+    if (topk_w)
+        ok(hipMemcpyAsync(topk_w, at<float>(ws, p.off_w), 4ul * p.P, hipMemcpyDeviceToDevice, s));
+    const int32_t* lslot = at<int32_t>(ws, p.off_lslot);  // -1 = pair without adapter
+    // with L == 0 every mask entry is -1 and the (empty) S buffers are never read
+    if (s1) ok(launch_gather_rows_f32(at<float>(ws, p.off_s1), p.ns1, p.C_b, p.r, slot, lslot, p.P, s1, s));
+    if (s2) ok(launch_gather_rows_f32(at<float>(ws, p.off_s2), p.ns2, p.C_b, p.r, slot, lslot, p.P, s2, s));
+    if (h) ok(launch_gather_rows_bf16(at<uint16_t>(ws, p.off_h), p.I, slot, p.P, h, s));
+    if (dn) ok(launch_gather_rows_f32(at<float>(ws, p.off_d), 1, p.C_b, p.H, slot, nullptr, p.P, dn, s));
+    return e == hipSuccess ? MOE_LORA_OK : MOE_LORA_EHIP;
+}
+
+int moe_lora_timing_enable(int32_t max_calls) {
+    for (hipEvent_t ev : g_timing.ev) hipEventDestroy(ev);
+    g_timing.ev.clear();
+    g_timing.ncalls = 0;
+    g_timing.max_calls = 0;
+    if (max_calls <= 0) return MOE_LORA_OK;
+    g_timing.ev.resize(static_cast<size_t>(max_calls) * (MOE_LORA_NKERNELS + 1));
+    for (auto& ev : g_timing.ev)
+        if (hipEventCreate(&ev) != hipSuccess) return MOE_LORA_EHIP;
+    g_timing.max_calls = max_calls;
+    return MOE_LORA_OK;
+}
+
+int moe_lora_timing_read(float* ms, int32_t* ncalls) {
+    if (!ms || !ncalls) return MOE_LORA_EINVAL;
+    for (int i = 0; i < MOE_LORA_NKERNELS; ++i) ms[i] = 0.f;
+    const int n = g_timing.ncalls;
+    for (int c = 0; c < n; ++c) {
+        hipEvent_t* ev = &g_timing.ev[static_cast<size_t>(c) * (MOE_LORA_NKERNELS + 1)];
+        if (hipEventSynchronize(ev[MOE_LORA_NKERNELS]) != hipSuccess) return MOE_LORA_EHIP;
+        for (int i = 0; i < MOE_LORA_NKERNELS; ++i) {
+            float t = 0.f;
+            if (hipEventElapsedTime(&t, ev[i], ev[i + 1]) != hipSuccess) return MOE_LORA_EHIP;
+            ms[i] += t;
+        }
+    }
+    *ncalls = n;
+    g_timing.ncalls = 0;
+    return MOE_LORA_OK;
+}
+
+const char* moe_lora_kernel_name(int32_t i) {
+    return (i >= 0 && i < MOE_LORA_NKERNELS) ? kKernelNames[i] : "";
+}
+
+}  // extern "C"

@@ -1,0 +1,82 @@
+// Top-k weighted combine and the stage readers.
+//
+// Combine: out[t] = sum_j w[t][j] * D[slot(t, j)], j ascending, no atomics
+// (AWS ML Blog post "Efficiently serve dozens of fine-tuned models with vLLM
+// on Amazon SageMaker AI and Amazon Bedrock", section "Implementing multi-LoRA
+// inference for MoE models in vLLM": the chosen experts' outputs are
+// aggregated). Each thread owns four consecutive hidden columns of one token.
+#include "common.h"
+#include "kernels.h"
+
+namespace moelora {
+
+__global__ __launch_bounds__(256) void k_combine(const float* __restrict__ D,
+                                                 const int32_t* __restrict__ slot_of_pair,
+                                                 const float* __restrict__ w, int k, int H,
+                                                 float* __restrict__ out) {
+    const int t = blockIdx.x;
+    const int n = (blockIdx.y * 256 + threadIdx.x) * 4;
+    if (n >= H) return;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < k; ++j) {
+        const int slot = slot_of_pair[t * k + j];
+        const float wj = w[t * k + j];
+        const f32x4 d = *reinterpret_cast<const f32x4*>(D + static_cast<size_t>(slot) * H + n);
+        acc += wj * d;
+    }
+    *reinterpret_cast<f32x4*>(out + static_cast<size_t>(t) * H + n) = acc;
+}
+
+hipError_t launch_combine(const float* D, const int32_t* slot_of_pair, const float* topk_w,
+                          int T, int k, int H, float* out, hipStream_t s) {
+    if (T == 0) return hipSuccess;
+    const dim3 grid(T, (H / 4 + 255) / 256), block(256);
+    hipLaunchKernelGGL(k_combine, grid, block, 0, s, D, slot_of_pair, topk_w, k, H, out);
+    return hipGetLastError();
+}
+
+// dst[p][c] = sum_s src[s][slot(p)][c]; 0 for pairs with mask[p] < 0.
+__global__ __launch_bounds__(256) void k_gather_f32(const float* __restrict__ src, int nsplit,
+                                                    int C_b, int ncols,
+                                                    const int32_t* __restrict__ slot_of_pair,
+                                                    const int32_t* __restrict__ mask,
+                                                    float* __restrict__ dst) {
+    const int p = blockIdx.x;
+    const int c = blockIdx.y * 256 + threadIdx.x;
+    if (c >= ncols) return;
+    float v = 0.f;
+    if (!mask || mask[p] >= 0) {
+        const int slot = slot_of_pair[p];
+        for (int s = 0; s < nsplit; ++s) v += src[(static_cast<size_t>(s) * C_b + slot) * ncols + c];
+    }
+    dst[static_cast<size_t>(p) * ncols + c] = v;
+}
+
+hipError_t launch_gather_rows_f32(const float* src_part, int nsplit, int C_b, int ncols,
+                                  const int32_t* slot_of_pair, const int32_t* mask, int P,
+                                  float* dst, hipStream_t s) {
+    if (P == 0) return hipSuccess;
+    const dim3 grid(P, (ncols + 255) / 256), block(256);
+    hipLaunchKernelGGL(k_gather_f32, grid, block, 0, s, src_part, nsplit, C_b, ncols, slot_of_pair,
+                       mask, dst);
+    return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void k_gather_bf16(const uint16_t* __restrict__ src, int ncols,
+                                                     const int32_t* __restrict__ slot_of_pair,
+                                                     uint16_t* __restrict__ dst) {
+    const int p = blockIdx.x;
+    const int c = blockIdx.y * 256 + threadIdx.x;
+    if (c >= ncols) return;
+    dst[static_cast<size_t>(p) * ncols + c] = src[static_cast<size_t>(slot_of_pair[p]) * ncols + c];
+}
+
+hipError_t launch_gather_rows_bf16(const uint16_t* src, int ncols, const int32_t* slot_of_pair,
+                                   int P, uint16_t* dst, hipStream_t s) {
+    if (P == 0) return hipSuccess;
+    const dim3 grid(P, (ncols + 255) / 256), block(256);
+    hipLaunchKernelGGL(k_gather_bf16, grid, block, 0, s, src, ncols, slot_of_pair, dst);
+    return hipGetLastError();
+}
+
+}  // namespace moelora

@@ -1,0 +1,79 @@
+// Host-side launchers of the gfx950 kernels (internal to libmoelora).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moelora {
+
+// ---- route + align --------------------------------------------------------
+hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* w,
+                        hipStream_t s);
+
+// Largest number of waves whose per-wave key histograms fit the align kernel's
+// LDS for this key count (0 = does not fit).
+int align_hist_waves(int E, int L);
+
+hipError_t launch_align(const int32_t* topk_ids, const int32_t* adapter_ids, int T, int k,
+                        int E, int L, int bm_b, int bm_l, int C_b, int C_l,
+                        int32_t* sorted_b, int32_t* blk_e_b, int32_t* n_b,
+                        int32_t* sorted_l, int32_t* blk_e_l, int32_t* blk_a_l, int32_t* n_l,
+                        int32_t* slot_of_pair, int32_t* lslot_of_pair, hipStream_t s);
+
+// ---- LoRA shrink ----------------------------------------------------------
+// S_part[split][slot][j] = sum over the split's K range of X[row] . A[a][e][j]
+// for the real rows of each LoRA-view block. gather_token: X row of pair p is
+// x[p / top_k] (else h[slot_of_pair[p]]).
+struct ShrinkArgs {
+    const uint16_t* X;   // x [T][K] or h [C_b][K]
+    int gather_token;
+    int K, top_k, P;
+    const int32_t* sorted_l;
+    const int32_t* blk_e_l;
+    const int32_t* blk_a_l;
+    const int32_t* slot_of_pair;
+    const uint16_t* A;   // [L][E][r][K]
+    int E, r, bm_l, n_blocks;
+    int nsplit;          // K split factor; K / nsplit is a multiple of 32
+    float* S_part;       // [nsplit][C_b][r]
+    int C_b;
+};
+hipError_t launch_shrink(const ShrinkArgs& a, hipStream_t s);
+
+// ---- grouped expert GEMM with fused LoRA expand (+ SwiGLU) ---------------
+struct GemmArgs {
+    const uint16_t* X;        // gate_up: x [T][K]; down: h [C_b][K]
+    int gate_up;              // 1: W = W_gu, epilogue SwiGLU -> h; 0: W = W_d -> D
+    const int32_t* sorted_b;
+    const int32_t* blk_e_b;
+    int P, top_k, bm_b, n_blocks;
+    const uint16_t* W;        // gate_up: [E][2I][H]; down: [E][H][I]
+    int N_out;                // gate_up: I (h columns); down: H
+    int K;                    // gate_up: H; down: I
+    // LoRA expand
+    const int32_t* adapter_ids;
+    int L, E, r;
+    const float* S_part;      // [nsplit][C_b][r] (may be null when L == 0)
+    int nsplit, C_b;
+    const uint16_t* Bl;       // gate_up: [L][E][2I][r]; down: [L][E][H][r]
+    // outputs
+    uint16_t* h_out;          // [C_b][I]
+    float* d_out;             // [C_b][H]
+};
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
+// Whether a tile configuration exists for these sizes.
+bool gemm_supported(int N_out, int K, int gate_up, int bm_b);
+
+// ---- combine + stage readers --------------------------------------------
+hipError_t launch_combine(const float* D, const int32_t* slot_of_pair, const float* topk_w,
+                          int T, int k, int H, float* out, hipStream_t s);
+
+// dst[p][c] = sum_s src_part[s][slot(p)][c]; rows with mask[p] < 0 are 0
+// (mask may be null).
+hipError_t launch_gather_rows_f32(const float* src_part, int nsplit, int C_b, int ncols,
+                                  const int32_t* slot_of_pair, const int32_t* mask, int P,
+                                  float* dst, hipStream_t s);
+hipError_t launch_gather_rows_bf16(const uint16_t* src, int ncols, const int32_t* slot_of_pair,
+                                   int P, uint16_t* dst, hipStream_t s);
+
+}  // namespace moelora

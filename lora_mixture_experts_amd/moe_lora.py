@@ -1,0 +1,210 @@
+"""ctypes binding of libmoelora.so (the C ABI declared in include/moe_lora.h).
+
+Argument marshalling only: every step of the layer runs in the library's HIP
+kernels. PyTorch is used for device memory and the current stream. There is
+no fallback: if the library is missing, loading fails with an error.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoelora.so")
+
+OK, EINVAL, EWORKSPACE, EHIP = 0, -1, -2, -3
+NKERNELS = 7
+
+
+class MoeLoraError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        super().__init__(f"{what}: {strerror(code)} ({code})")
+        self.code = code
+
+
+class Desc(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("T", "H", "I", "E", "top_k", "L", "r", "block_m_base", "block_m_lora", "flags")]
+
+
+class Weights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("w_gate_up", "w_down", "a_gate_up", "b_gate_up", "a_down", "b_down")]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it first "
+                               "(python -c 'import __graft_entry__ as g; g.build()')")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        pD, pW = ctypes.POINTER(Desc), ctypes.POINTER(Weights)
+        pI32, pSZ = ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_size_t)
+        sig = {
+            "moe_lora_strerror": ([ctypes.c_int], ctypes.c_char_p),
+            "moe_lora_validate": ([pD, pW, SZ], ctypes.c_int),
+            "moe_lora_block_sizes": ([pD, pI32, pI32], ctypes.c_int),
+            "moe_lora_workspace_bytes": ([pD, pSZ], ctypes.c_int),
+            "moe_lora_align_capacity": ([pD, pI32, pI32], ctypes.c_int),
+            "moe_lora_route": ([pD, P, P, P, P], ctypes.c_int),
+            "moe_lora_align": ([pD, P, P, P, P, P, P, P, P, P, P], ctypes.c_int),
+            "moe_lora_forward": ([pD, pW, P, P, P, P, P, SZ, P], ctypes.c_int),
+            "moe_lora_read_stages": ([pD, P, SZ, P, P, P, P, P, P, P], ctypes.c_int),
+            "moe_lora_timing_enable": ([I32], ctypes.c_int),
+            "moe_lora_timing_read": ([ctypes.POINTER(ctypes.c_float), pI32], ctypes.c_int),
+            "moe_lora_kernel_name": ([I32], ctypes.c_char_p),
+        }
+        for name, (args, res) in sig.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = L
+    return _lib
+
+
+EXPORTED = ("moe_lora_strerror", "moe_lora_validate", "moe_lora_block_sizes",
+            "moe_lora_workspace_bytes", "moe_lora_align_capacity", "moe_lora_route",
+            "moe_lora_align", "moe_lora_forward", "moe_lora_read_stages",
+            "moe_lora_timing_enable", "moe_lora_timing_read", "moe_lora_kernel_name")
+
+
+def strerror(code: int) -> str:
+    return lib().moe_lora_strerror(code).decode()
+
+
+def _check(rc: int, what: str):
+    if rc != OK:
+        raise MoeLoraError(rc, what)
+
+
+def make_desc(T, H, I, E, top_k, L, r, block_m_base=0, block_m_lora=0, flags=0) -> Desc:
+    return Desc(T, H, I, E, top_k, L, r, block_m_base, block_m_lora, flags)
+
+
+def validate(desc: Desc, weights: Weights | None = None, ws_bytes: int = -1) -> int:
+    """Host-only check; returns the library's code (0 = valid)."""
+    wp = ctypes.byref(weights) if weights is not None else None
+    sz = ctypes.c_size_t(ws_bytes if ws_bytes >= 0 else (1 << 64) - 1)
+    return lib().moe_lora_validate(ctypes.byref(desc), wp, sz)
+
+
+def block_sizes(desc: Desc):
+    a, b = ctypes.c_int32(), ctypes.c_int32()
+    _check(lib().moe_lora_block_sizes(ctypes.byref(desc), ctypes.byref(a), ctypes.byref(b)), "block_sizes")
+    return a.value, b.value
+
+
+def workspace_bytes(desc: Desc) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().moe_lora_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)), "workspace_bytes")
+    return n.value
+
+
+def align_capacity(desc: Desc):
+    a, b = ctypes.c_int32(), ctypes.c_int32()
+    _check(lib().moe_lora_align_capacity(ctypes.byref(desc), ctypes.byref(a), ctypes.byref(b)),
+           "align_capacity")
+    return a.value, b.value
+
+
+# ------------------------------------------------------------------ tensor calls
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is not None:
+        return ctypes.c_void_p(stream)
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def route(desc, logits, topk_ids, topk_w, stream=None):
+    _check(lib().moe_lora_route(ctypes.byref(desc), _ptr(logits), _ptr(topk_ids), _ptr(topk_w),
+                                _stream(stream)), "route")
+
+
+def align(desc, topk_ids, adapter_ids, sorted_b, blk_e_b, n_b, sorted_l, blk_e_l, blk_a_l, n_l,
+          stream=None):
+    _check(lib().moe_lora_align(ctypes.byref(desc), _ptr(topk_ids), _ptr(adapter_ids),
+                                _ptr(sorted_b), _ptr(blk_e_b), _ptr(n_b), _ptr(sorted_l),
+                                _ptr(blk_e_l), _ptr(blk_a_l), _ptr(n_l), _stream(stream)), "align")
+
+
+def weights_struct(w_gate_up, w_down, a_gate_up=None, b_gate_up=None, a_down=None, b_down=None):
+    return Weights(*(None if t is None or t.numel() == 0 else t.data_ptr()
+                     for t in (w_gate_up, w_down, a_gate_up, b_gate_up, a_down, b_down)))
+
+
+def forward(desc, weights: Weights, x, logits, adapter_ids, out, workspace, stream=None):
+    _check(lib().moe_lora_forward(ctypes.byref(desc), ctypes.byref(weights), _ptr(x), _ptr(logits),
+                                  _ptr(adapter_ids), _ptr(out), _ptr(workspace),
+                                  ctypes.c_size_t(workspace.numel() * workspace.element_size()),
+                                  _stream(stream)), "forward")
+
+
+def read_stages(desc, workspace, topk_ids=None, topk_w=None, s1=None, h=None, s2=None, dn=None,
+                stream=None):
+    _check(lib().moe_lora_read_stages(ctypes.byref(desc), _ptr(workspace),
+                                      ctypes.c_size_t(workspace.numel() * workspace.element_size()),
+                                      _ptr(topk_ids), _ptr(topk_w), _ptr(s1), _ptr(h), _ptr(s2),
+                                      _ptr(dn), _stream(stream)), "read_stages")
+
+
+def timing_enable(max_calls: int):
+    _check(lib().moe_lora_timing_enable(max_calls), "timing_enable")
+
+
+def timing_read():
+    ms = (ctypes.c_float * NKERNELS)()
+    n = ctypes.c_int32()
+    _check(lib().moe_lora_timing_read(ms, ctypes.byref(n)), "timing_read")
+    return list(ms), n.value
+
+
+def kernel_names():
+    return [lib().moe_lora_kernel_name(i).decode() for i in range(NKERNELS)]
+
+
+# ------------------------------------------------------------------ convenience
+
+class Layer:
+    """Device-resident weights + descriptor + workspace for repeated calls."""
+
+    def __init__(self, T, H, I, E, top_k, L, r, w_gate_up, w_down, a_gate_up=None, b_gate_up=None,
+                 a_down=None, b_down=None, block_m_base=0, block_m_lora=0):
+        import torch
+        self.desc = make_desc(T, H, I, E, top_k, L, r, block_m_base, block_m_lora)
+        self.tensors = (w_gate_up, w_down, a_gate_up, b_gate_up, a_down, b_down)
+        self.weights = weights_struct(*self.tensors)
+        _check(validate(self.desc, self.weights), "validate")
+        self.workspace = torch.empty(workspace_bytes(self.desc), dtype=torch.uint8, device=w_gate_up.device)
+        self.device = w_gate_up.device
+
+    def __call__(self, x, logits, adapter_ids, out=None, stream=None):
+        import torch
+        if out is None:
+            out = torch.empty((self.desc.T, self.desc.H), dtype=torch.float32, device=self.device)
+        forward(self.desc, self.weights, x, logits, adapter_ids, out, self.workspace, stream)
+        return out
+
+    def stages(self, stream=None):
+        import torch
+        d, dev = self.desc, self.device
+        P = d.T * d.top_k
+        r = d.r if d.L > 0 else 8
+        st = dict(topk_ids=torch.empty(P, dtype=torch.int32, device=dev),
+                  topk_w=torch.empty(P, dtype=torch.float32, device=dev),
+                  s1=torch.empty((P, r), dtype=torch.float32, device=dev),
+                  h=torch.empty((P, d.I), dtype=torch.bfloat16, device=dev),
+                  s2=torch.empty((P, r), dtype=torch.float32, device=dev),
+                  dn=torch.empty((P, d.H), dtype=torch.float32, device=dev))
+        read_stages(d, self.workspace, stream=stream, **st)
+        return st

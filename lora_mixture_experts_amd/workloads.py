@@ -240,3 +240,18 @@ def random_dims(rng: np.random.Generator):
     return dict(T=int(rng.integers(1, 40)), H=64 * int(rng.integers(1, 5)),
                 I=64 * int(rng.integers(1, 5)), E=E, top_k=min(k, 8),
                 L=int(rng.integers(0, 4)), r=int(rng.choice([8, 16, 32])))
+
+
+def device_tensors(case: Case, device="cuda"):
+    """Copy a case to device tensors (bf16 arrays as torch.bfloat16)."""
+    import torch
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(device)
+
+    return dict(
+        x=bf(case.x), logits=torch.from_numpy(np.ascontiguousarray(case.logits)).to(device),
+        adapter_ids=torch.from_numpy(np.ascontiguousarray(case.adapter_ids, dtype=np.int32)).to(device),
+        w_gate_up=bf(case.w_gate_up), w_down=bf(case.w_down),
+        a_gate_up=bf(case.a_gate_up), b_gate_up=bf(case.b_gate_up),
+        a_down=bf(case.a_down), b_down=bf(case.b_down))

@@ -1,0 +1,297 @@
+"""Parity of the HIP path (called through the C ABI) against the CPU oracle.
+
+Integer work (routing ids, alignment) is compared bit for bit; the layer
+output must satisfy max|gpu-ref|/max|ref| <= 1e-2 and
+mean|gpu-ref|/mean|ref| <= 2e-3 (bf16 inputs, fp32 accumulation, h in bf16).
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from lora_mixture_experts_amd import moe_lora as ml
+from lora_mixture_experts_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+MAX_TOL, MEAN_TOL = 1e-2, 2e-3
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "the gpu tests need a GPU"
+    return torch.device("cuda:0")
+
+
+def metrics(gpu, ref):
+    gpu = np.asarray(gpu, np.float64)
+    ref = np.asarray(ref, np.float64)
+    err = np.abs(gpu - ref)
+    return err.max() / np.abs(ref).max(), err.mean() / np.abs(ref).mean()
+
+
+def build_case(name, dims=None, seed=None, touched_only=True):
+    """Draw a case; with touched_only only the experts / LoRA blocks the routing
+    uses get values (the rest hold bf16 NaN, so a stray read shows up)."""
+    if dims is None:
+        dims = wl.CONFIGS[name]
+    logits, x, ad, _ = wl.routing_only(name, seed=seed, dims=dims)
+    ids, _ = oracle.route(logits, dims["top_k"])
+    experts = set(np.unique(ids).tolist())
+    blocks = set()
+    for t in range(dims["T"]):
+        a = int(ad[t])
+        if 0 <= a < dims["L"]:
+            for e in ids[t]:
+                blocks.add((a, int(e)))
+    if not touched_only:
+        experts, blocks = None, None
+    return wl.make_case(name, seed=seed, dims=dims, experts=experts, lora_blocks=blocks)
+
+
+def run_gpu(case, dev, bm_b=0, bm_l=0):
+    t = wl.device_tensors(case, dev)
+    layer = ml.Layer(case.T, case.H, case.I, case.E, case.top_k, case.L, case.r,
+                     t["w_gate_up"], t["w_down"], t["a_gate_up"], t["b_gate_up"], t["a_down"],
+                     t["b_down"], block_m_base=bm_b, block_m_lora=bm_l)
+    out = layer(t["x"], t["logits"], t["adapter_ids"])
+    torch.cuda.synchronize()
+    return layer, t, out
+
+
+def sample_tokens(case, n):
+    if case.T <= n:
+        return np.arange(case.T, dtype=np.int32)
+    rng = np.random.default_rng(1234)
+    pick = set(rng.choice(case.T, size=n - 2, replace=False).tolist()) | {0, case.T - 1}
+    return np.array(sorted(pick), dtype=np.int32)
+
+
+# ----------------------------------------------------------------------------- route / align
+
+ROUTE_CASES = [("tiny", {}), ("decode", {}), ("prefill", {}), ("wide", {}), ("many", {}),
+               ("odd", dict(T=37, H=64, I=64, E=70, top_k=7, L=3, r=8)),
+               ("one", dict(T=1, H=64, I=64, E=1, top_k=1, L=0, r=8))]
+
+
+@pytest.mark.parametrize("name,dims", ROUTE_CASES)
+def test_route_parity(dev, name, dims):
+    log(f"route {name}")
+    dims = dims or wl.CONFIGS[name]
+    logits, _, _, _ = wl.routing_only(name, dims=dims)
+    ref_ids, ref_w = oracle.route(logits, dims["top_k"])
+    d = ml.make_desc(dims["T"], dims["H"], dims["I"], dims["E"], dims["top_k"], dims["L"], dims["r"])
+    lg = torch.from_numpy(logits).to(dev)
+    ids = torch.empty((dims["T"], dims["top_k"]), dtype=torch.int32, device=dev)
+    w = torch.empty((dims["T"], dims["top_k"]), dtype=torch.float32, device=dev)
+    ml.route(d, lg, ids, w)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(ids.cpu().numpy(), ref_ids)
+    np.testing.assert_allclose(w.cpu().numpy(), ref_w, rtol=0, atol=2e-6)
+
+
+def test_route_ties(dev):
+    log("route ties")
+    logits = np.array([[1.0, 3.0, 3.0, 2.0, 3.0, 3.0],
+                       [0.5] * 6,
+                       [-1.0, -2.0, -1.0, -2.0, -3.0, -1.0]], np.float32)
+    logits = np.concatenate([logits, np.repeat(logits[:1], 70, axis=0)])
+    for k in (1, 2, 4, 6):
+        ref_ids, _ = oracle.route(logits, k)
+        d = ml.make_desc(logits.shape[0], 64, 64, 6, k, 0, 8)
+        ids = torch.empty((logits.shape[0], k), dtype=torch.int32, device=dev)
+        w = torch.empty((logits.shape[0], k), dtype=torch.float32, device=dev)
+        ml.route(d, torch.from_numpy(logits).to(dev), ids, w)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(ids.cpu().numpy(), ref_ids)
+
+
+def gpu_align(dev, ids, ad, dims, bm_b, bm_l):
+    d = ml.make_desc(dims["T"], dims["H"], dims["I"], dims["E"], dims["top_k"], dims["L"], dims["r"],
+                     bm_b, bm_l)
+    C_b, C_l = ml.align_capacity(d)
+    bb, bl = ml.block_sizes(d)
+    z = lambda n: torch.full((n,), -7, dtype=torch.int32, device=dev)
+    out = dict(sorted_b=z(C_b), blk_e_b=z(C_b // bb), n_b=z(1), sorted_l=z(C_l), blk_e_l=z(C_l // bl),
+               blk_a_l=z(C_l // bl), n_l=z(1))
+    ml.align(d, torch.from_numpy(ids).to(dev), torch.from_numpy(ad).to(dev), **out)
+    torch.cuda.synchronize()
+    return {k: v.cpu().numpy() for k, v in out.items()}, (bb, bl)
+
+
+ALIGN_CASES = [("tiny", {}, (16, 16)), ("decode", {}, (16, 16)), ("decode", {}, (64, 32)),
+               ("prefill", {}, (128, 64)), ("prefill", {}, (16, 256)), ("wide", {}, (32, 16)),
+               ("many", {}, (128, 16)), ("many", {}, (16, 64)),
+               ("odd", dict(T=37, H=64, I=64, E=70, top_k=7, L=3, r=8), (16, 16)),
+               ("noL", dict(T=300, H=64, I=64, E=5, top_k=2, L=0, r=8), (32, 16)),
+               ("big", dict(T=20000, H=64, I=64, E=64, top_k=8, L=16, r=8), (256, 128))]
+
+
+@pytest.mark.parametrize("name,dims,bm", ALIGN_CASES)
+def test_align_parity(dev, name, dims, bm):
+    log(f"align {name} {bm}")
+    dims = dims or wl.CONFIGS[name]
+    logits, _, ad, _ = wl.routing_only(name, dims=dims)
+    ids, _ = oracle.route(logits, dims["top_k"])
+    if name in ("odd", "big"):  # out-of-range adapter ids count as "none"
+        ad = ad.copy()
+        ad[::5] = dims["L"] + 3
+        ad[1::7] = -9
+    got, (bb, bl) = gpu_align(dev, ids, ad, dims, *bm)
+    ref = oracle.align(ids, ad, dims["E"], dims["L"], bb, bl)
+    for key in ("sorted_b", "blk_e_b", "sorted_l", "blk_e_l", "blk_a_l"):
+        np.testing.assert_array_equal(got[key], ref[key], err_msg=key)
+    assert int(got["n_b"][0]) == ref["n_b"] and int(got["n_l"][0]) == ref["n_l"]
+    again, _ = gpu_align(dev, ids, ad, dims, *bm)
+    for key in got:
+        np.testing.assert_array_equal(again[key], got[key])
+
+
+# ----------------------------------------------------------------------------- the layer
+
+def check_layer(case, dev, ntok=64, bm=(0, 0), stages=False):
+    ids, w = oracle.route(case.logits, case.top_k)
+    toks = sample_tokens(case, ntok)
+    layer, t, out = run_gpu(case, dev, *bm)
+    ref, st = oracle.forward(case, ids, w, tokens=toks, stages=True)
+    got = out.cpu().numpy()[toks]
+    mx, mean = metrics(got, ref)
+    log(f"  {case.name} bm={ml.block_sizes(layer.desc)} tokens={len(toks)}: max {mx:.2e} mean {mean:.2e}")
+    assert np.all(np.isfinite(got))
+    assert mx <= MAX_TOL and mean <= MEAN_TOL, (mx, mean)
+    if stages:
+        gs = {k: v.cpu() for k, v in layer.stages().items()}
+        rows = (toks[:, None] * case.top_k + np.arange(case.top_k)[None, :]).reshape(-1)
+        np.testing.assert_array_equal(gs["topk_ids"].numpy().reshape(case.T, case.top_k), ids)
+        s1 = gs["s1"].numpy()[rows]
+        s2 = gs["s2"].numpy()[rows]
+        h = gs["h"].float().numpy()[rows]
+        dn = gs["dn"].numpy()[rows]
+        if case.L > 0 and np.abs(st["s1"]).max() > 0:
+            m1 = metrics(s1, st["s1"])
+            assert m1[0] < 1e-4, ("s1", m1)
+            m2 = metrics(s2, st["s2"])
+            assert m2[0] < 2e-2 and m2[1] < 4e-3, ("s2", m2)
+        mh = metrics(h, st["h"])
+        assert mh[0] < 1e-2 and mh[1] < 4e-3, ("h", mh)
+        md = metrics(dn, st["d"])
+        assert md[0] < MAX_TOL and md[1] < MEAN_TOL, ("d", md)
+        # pairs without adapter have zero shrink rows
+        noad = np.array([not (0 <= case.adapter_ids[r // case.top_k] < case.L) for r in rows])
+        assert np.all(s1[noad] == 0) and np.all(s2[noad] == 0)
+    return out
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode", "wide"])
+def test_layer_parity_full(dev, name):
+    log(f"layer {name}")
+    case = build_case(name)
+    check_layer(case, dev, ntok=case.T, stages=True)
+
+
+def test_layer_parity_prefill_sampled(dev):
+    log("layer prefill")
+    case = build_case("prefill")
+    check_layer(case, dev, ntok=48, stages=True)
+
+
+def test_layer_parity_many_sampled(dev):
+    log("layer many")
+    case = build_case("many")
+    check_layer(case, dev, ntok=96, stages=True)
+
+
+@pytest.mark.parametrize("bm", [(16, 16), (32, 16), (64, 64), (128, 32), (256, 256)])
+def test_layer_block_sizes(dev, bm):
+    log(f"layer block sizes {bm}")
+    dims = dict(T=150, H=192, I=320, E=6, top_k=3, L=3, r=16)
+    case = build_case("blocks", dims=dims, seed=5)
+    check_layer(case, dev, ntok=150, bm=bm, stages=True)
+
+
+RANDOM_DIMS = [dict(T=1, H=64, I=64, E=1, top_k=1, L=1, r=8),
+               dict(T=3, H=128, I=64, E=4, top_k=4, L=2, r=16),
+               dict(T=33, H=64, I=192, E=9, top_k=2, L=4, r=64),
+               dict(T=70, H=256, I=128, E=3, top_k=2, L=1, r=128),
+               dict(T=19, H=320, I=448, E=16, top_k=5, L=0, r=8),
+               dict(T=257, H=128, I=128, E=40, top_k=8, L=5, r=32)]
+
+
+@pytest.mark.parametrize("i", range(len(RANDOM_DIMS)))
+def test_layer_shapes(dev, i):
+    dims = RANDOM_DIMS[i]
+    log(f"layer shape {dims}")
+    case = build_case(f"shape{i}", dims=dims, seed=40 + i)
+    check_layer(case, dev, ntok=dims["T"], stages=True)
+
+
+def test_no_adapter_and_zero_b_agree(dev):
+    log("layer no-adapter variants")
+    case = build_case("decode", touched_only=False)
+    case.adapter_ids[:] = -1
+    _, _, out_none = run_gpu(case, dev)
+    check_layer(case, dev, ntok=case.T)
+    case2 = build_case("decode", touched_only=False)
+    case2.b_gate_up[:] = 0
+    case2.b_down[:] = 0
+    _, _, out_zero_b = run_gpu(case2, dev)
+    # B = 0 adds exact zeros, so the result is bitwise the base-only one
+    assert torch.equal(out_none, out_zero_b)
+
+
+def test_pure_lora(dev):
+    """Base weights zero: the output is the LoRA path alone."""
+    log("layer pure LoRA")
+    case = build_case("decode")
+    case.w_gate_up[:] = 0
+    case.w_down[:] = 0
+    check_layer(case, dev, ntok=case.T, stages=True)
+
+
+def test_single_expert(dev):
+    log("layer single expert")
+    dims = dict(T=40, H=256, I=512, E=1, top_k=1, L=2, r=32)
+    case = build_case("single", dims=dims, seed=9)
+    check_layer(case, dev, ntok=40, stages=True)
+
+
+def test_repeat_calls_reuse_workspace(dev):
+    log("layer repeat")
+    case = build_case("tiny")
+    layer, t, out1 = run_gpu(case, dev)
+    out2 = layer(t["x"], t["logits"], t["adapter_ids"])
+    torch.cuda.synchronize()
+    # same inputs, same block plan: bitwise identical (no atomics in the path)
+    assert torch.equal(out1, out2)
+
+
+def test_zero_tokens_is_noop(dev):
+    d = ml.make_desc(0, 64, 64, 2, 1, 0, 8)
+    w = torch.zeros(2 * 2 * 64 * 64, dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(max(ml.workspace_bytes(d), 256), dtype=torch.uint8, device=dev)
+    out = torch.empty(1, dtype=torch.float32, device=dev)
+    x = torch.empty(8, dtype=torch.bfloat16, device=dev)
+    lg = torch.empty(2, dtype=torch.float32, device=dev)
+    ad = torch.empty(1, dtype=torch.int32, device=dev)
+    ml.forward(d, ml.weights_struct(w, w), x, lg, ad, out, ws)
+    torch.cuda.synchronize()
+
+
+def test_forward_rejects_small_workspace(dev):
+    case = build_case("tiny")
+    t = wl.device_tensors(case, dev)
+    d = ml.make_desc(case.T, case.H, case.I, case.E, case.top_k, case.L, case.r)
+    ws = torch.empty(ml.workspace_bytes(d) - 256, dtype=torch.uint8, device=dev)
+    out = torch.empty((case.T, case.H), dtype=torch.float32, device=dev)
+    wts = ml.weights_struct(t["w_gate_up"], t["w_down"], t["a_gate_up"], t["b_gate_up"], t["a_down"],
+                            t["b_down"])
+    with pytest.raises(ml.MoeLoraError) as ei:
+        ml.forward(d, wts, t["x"], t["logits"], t["adapter_ids"], out, ws)
+    assert ei.value.code == ml.EWORKSPACE

@@ -155,6 +155,9 @@ def main():
     ap.add_argument("--also", default="prefill", help="second workload reported in the same line ('' = none)")
     ap.add_argument("--rotate", type=int, default=3)
     ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MiB",
+                    help="first run one plain device-to-device copy of this size, as the "
+                         "reference dispatch for scaling HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -163,6 +166,14 @@ def main():
 
     import torch
     dev = torch.device("cuda:0")
+    if args.calibrate_copy > 0:
+        n = args.calibrate_copy << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     case, ids, st, ms, kus, b, f, lbytes, lflops = run_workload(args.workload, args.steps, args.warmup,
                                                                args.rotate, dev)
     dom = max(("gemm_gate_up", "gemm_down"), key=lambda n: kus[n])

@@ -20,24 +20,12 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 struct Plan {
     int T, H, I, E, k, L, r, P;
-    int bm_b, bm_l, C_b, C_l, nblk_b, nblk_l, ns1, ns2;
+    int bm_b, bm_l, C_b, C_l, nblk_b, nblk_l;
     size_t off_ids, off_w, off_sorted_b, off_blk_e_b, off_counts, off_sorted_l, off_blk_e_l,
-        off_blk_a_l, off_slot, off_lslot, off_s1, off_s2, off_h, off_d, total;
+        off_blk_a_l, off_slot, off_lslot, off_sad, off_s1, off_s2, off_h, off_d, total;
 };
 
 int roundup_i(long v, long m) { return static_cast<int>((v + m - 1) / m * m); }
-
-// K split of the shrink: enough workgroups to cover the chip, every split at
-// least 4 K steps of 32 (one per wave).
-int pick_split(int K, int nblk) {
-    const int steps = K / 32;
-    if (nblk <= 0) return 1;
-    const int target = nblk >= 1024 ? 1 : (1024 + nblk - 1) / nblk;
-    int best = 1;
-    for (int d = 1; d <= steps; ++d)
-        if (steps % d == 0 && d <= target && steps / d >= 4) best = d;
-    return best;
-}
 
 int default_bm_base(int P, int E) {
     const long avg = (P + E - 1) / E;  // mean rows per expert
@@ -85,8 +73,6 @@ int make_plan(const moe_lora_desc* d, Plan* p) {
     p->C_l = roundup_i(P + std::min<long>(static_cast<long>(p->E) * p->L, P) * (p->bm_l - 1), p->bm_l);
     p->nblk_b = p->C_b / p->bm_b;
     p->nblk_l = p->C_l / p->bm_l;
-    p->ns1 = pick_split(p->H, p->nblk_l);
-    p->ns2 = pick_split(p->I, p->nblk_l);
     size_t o = 0;
     auto take = [&](size_t bytes) { const size_t at = o; o += up(bytes); return at; };
     p->off_ids = take(4 * P);
@@ -99,8 +85,10 @@ int make_plan(const moe_lora_desc* d, Plan* p) {
     p->off_blk_a_l = take(4ul * p->nblk_l);
     p->off_slot = take(4 * P);
     p->off_lslot = take(4 * P);
-    p->off_s1 = take(p->L > 0 ? 4ul * p->ns1 * p->C_b * p->r : 0);
-    p->off_s2 = take(p->L > 0 ? 4ul * p->ns2 * p->C_b * p->r : 0);
+    p->off_sad = take(4ul * p->C_b);
+    const size_t sbytes = p->L > 0 ? 4ul * p->C_b * p->r : 0;
+    p->off_s1 = take(sbytes);
+    p->off_s2 = take(sbytes);
     p->off_h = take(2ul * p->C_b * p->I);
     p->off_d = take(4ul * p->C_b * p->H);
     p->total = o;
@@ -134,7 +122,7 @@ struct Timing {
 } g_timing;
 
 void timing_mark(int call, int i, hipStream_t s) {
-    if (call >= 0) hipEventRecord(g_timing.ev[static_cast<size_t>(call) * (MOE_LORA_NKERNELS + 1) + i], s);
+    if (call >= 0) (void)hipEventRecord(g_timing.ev[static_cast<size_t>(call) * (MOE_LORA_NKERNELS + 1) + i], s);
 }
 
 }  // namespace
@@ -211,7 +199,7 @@ int moe_lora_align(const moe_lora_desc* d, const int32_t* topk_ids, const int32_
         return MOE_LORA_EINVAL;
     return launch_align(topk_ids, adapter_ids, p.T, p.k, p.E, p.L, p.bm_b, p.bm_l, p.C_b, p.C_l,
                         sorted_b, blk_e_b, n_b, sorted_l, blk_e_l, blk_a_l, n_l, nullptr,
-                        nullptr, static_cast<hipStream_t>(stream)) == hipSuccess
+                        nullptr, nullptr, nullptr, 0, static_cast<hipStream_t>(stream)) == hipSuccess
                ? MOE_LORA_OK
                : MOE_LORA_EHIP;
 }
@@ -240,6 +228,7 @@ int moe_lora_forward(const moe_lora_desc* d, const moe_lora_weights* w, const vo
     int32_t* blk_a_l = at<int32_t>(workspace, p.off_blk_a_l);
     int32_t* slot = at<int32_t>(workspace, p.off_slot);
     int32_t* lslot = at<int32_t>(workspace, p.off_lslot);
+    int32_t* sad = at<int32_t>(workspace, p.off_sad);
     float* s1 = at<float>(workspace, p.off_s1);
     float* s2 = at<float>(workspace, p.off_s2);
     uint16_t* h = at<uint16_t>(workspace, p.off_h);
@@ -254,39 +243,40 @@ int moe_lora_forward(const moe_lora_desc* d, const moe_lora_weights* w, const vo
     ok(launch_route(logits, p.T, p.E, p.k, ids, tw, s));
     timing_mark(call, 1, s);
     ok(launch_align(ids, adapter_ids, p.T, p.k, p.E, p.L, p.bm_b, p.bm_l, p.C_b, p.C_l, sorted_b,
-                    blk_e_b, counts, sorted_l, blk_e_l, blk_a_l, counts + 1, slot, lslot, s));
+                    blk_e_b, counts, sorted_l, blk_e_l, blk_a_l, counts + 1, slot, lslot, sad,
+                    nullptr, 0, s));
     timing_mark(call, 2, s);
 
     ShrinkArgs sa{};
     sa.top_k = p.k; sa.P = p.P; sa.sorted_l = sorted_l; sa.blk_e_l = blk_e_l;
     sa.blk_a_l = blk_a_l; sa.slot_of_pair = slot; sa.E = p.E; sa.r = p.r; sa.bm_l = p.bm_l;
-    sa.n_blocks = p.nblk_l; sa.C_b = p.C_b;
+    sa.n_blocks = p.nblk_l;
     if (p.L > 0) {
         sa.X = static_cast<const uint16_t*>(x); sa.gather_token = 1; sa.K = p.H;
-        sa.A = static_cast<const uint16_t*>(w->a_gate_up); sa.nsplit = p.ns1; sa.S_part = s1;
+        sa.A = static_cast<const uint16_t*>(w->a_gate_up); sa.S = s1;
         ok(launch_shrink(sa, s));
     }
     timing_mark(call, 3, s);
 
     GemmArgs ga{};
     ga.sorted_b = sorted_b; ga.blk_e_b = blk_e_b; ga.P = p.P; ga.top_k = p.k; ga.bm_b = p.bm_b;
-    ga.n_blocks = p.nblk_b; ga.adapter_ids = adapter_ids; ga.L = p.L; ga.E = p.E; ga.r = p.r;
+    ga.n_blocks = p.nblk_b; ga.slot_adapter = sad; ga.L = p.L; ga.E = p.E; ga.r = p.r;
     ga.C_b = p.C_b; ga.h_out = h; ga.d_out = dn;
     ga.X = static_cast<const uint16_t*>(x); ga.gate_up = 1;
     ga.W = static_cast<const uint16_t*>(w->w_gate_up); ga.N_out = p.I; ga.K = p.H;
-    ga.S_part = s1; ga.nsplit = p.ns1; ga.Bl = static_cast<const uint16_t*>(w->b_gate_up);
+    ga.S = s1; ga.Bl = static_cast<const uint16_t*>(w->b_gate_up);
     ok(launch_gemm(ga, s));
     timing_mark(call, 4, s);
 
     if (p.L > 0) {
         sa.X = h; sa.gather_token = 0; sa.K = p.I;
-        sa.A = static_cast<const uint16_t*>(w->a_down); sa.nsplit = p.ns2; sa.S_part = s2;
+        sa.A = static_cast<const uint16_t*>(w->a_down); sa.S = s2;
         ok(launch_shrink(sa, s));
     }
     timing_mark(call, 5, s);
 
     ga.X = h; ga.gate_up = 0; ga.W = static_cast<const uint16_t*>(w->w_down); ga.N_out = p.H;
-    ga.K = p.I; ga.S_part = s2; ga.nsplit = p.ns2; ga.Bl = static_cast<const uint16_t*>(w->b_down);
+    ga.K = p.I; ga.S = s2; ga.Bl = static_cast<const uint16_t*>(w->b_down);
     ok(launch_gemm(ga, s));
     timing_mark(call, 6, s);
 
@@ -315,15 +305,15 @@ int moe_lora_read_stages(const moe_lora_desc* d, const void* workspace, size_t w
         ok(hipMemcpyAsync(topk_w, at<float>(ws, p.off_w), 4ul * p.P, hipMemcpyDeviceToDevice, s));
     const int32_t* lslot = at<int32_t>(ws, p.off_lslot);  // -1 = pair without adapter
     // with L == 0 every mask entry is -1 and the (empty) S buffers are never read
-    if (s1) ok(launch_gather_rows_f32(at<float>(ws, p.off_s1), p.ns1, p.C_b, p.r, slot, lslot, p.P, s1, s));
-    if (s2) ok(launch_gather_rows_f32(at<float>(ws, p.off_s2), p.ns2, p.C_b, p.r, slot, lslot, p.P, s2, s));
+    if (s1) ok(launch_gather_rows_f32(at<float>(ws, p.off_s1), 1, p.C_b, p.r, slot, lslot, p.P, s1, s));
+    if (s2) ok(launch_gather_rows_f32(at<float>(ws, p.off_s2), 1, p.C_b, p.r, slot, lslot, p.P, s2, s));
     if (h) ok(launch_gather_rows_bf16(at<uint16_t>(ws, p.off_h), p.I, slot, p.P, h, s));
     if (dn) ok(launch_gather_rows_f32(at<float>(ws, p.off_d), 1, p.C_b, p.H, slot, nullptr, p.P, dn, s));
     return e == hipSuccess ? MOE_LORA_OK : MOE_LORA_EHIP;
 }
 
 int moe_lora_timing_enable(int32_t max_calls) {
-    for (hipEvent_t ev : g_timing.ev) hipEventDestroy(ev);
+    for (hipEvent_t ev : g_timing.ev) (void)hipEventDestroy(ev);
     g_timing.ev.clear();
     g_timing.ncalls = 0;
     g_timing.max_calls = 0;

@@ -14,6 +14,12 @@ constexpr int kWave = 64;
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
+// Wave index within the workgroup, marked wave-uniform (scalar) so that loops
+// bounded by it compile as scalar loops with exact memory wait counts.
+__device__ __forceinline__ int wave_id() {
+    return __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
     return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }

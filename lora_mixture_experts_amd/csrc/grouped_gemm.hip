@@ -28,12 +28,7 @@ __device__ __forceinline__ int w_row_of_frag(int f, int c0, int I) {
     return c0 + 16 * f;
 }
 
-__device__ __forceinline__ int row_adapter(const GemmArgs& a, int slot) {
-    const int p = a.sorted_b[slot];
-    if (p >= a.P) return -1;
-    const int ad = a.adapter_ids[p / a.top_k];
-    return (ad >= 0 && ad < a.L) ? ad : -1;
-}
+__device__ __forceinline__ int row_adapter(const GemmArgs& a, int slot) { return a.slot_adapter[slot]; }
 
 // S row chunk (8 values starting at j0) as hi/lo bf16 operands; zero when the
 // row is not in the current adapter run or j is past r.
@@ -43,15 +38,13 @@ __device__ __forceinline__ void load_s_hilo(const GemmArgs& a, int slot, bool in
 #pragma unroll
     for (int q = 0; q < 8; ++q) v[q] = 0.f;
     if (in_run && j0 < a.r) {
-        for (int s = 0; s < a.nsplit; ++s) {
-            const float* src = a.S_part + (static_cast<size_t>(s) * a.C_b + slot) * a.r + j0;
-            const f32x4 x0 = *reinterpret_cast<const f32x4*>(src);
-            const f32x4 x1 = *reinterpret_cast<const f32x4*>(src + 4);
+        const float* src = a.S + static_cast<size_t>(slot) * a.r + j0;
+        const f32x4 x0 = *reinterpret_cast<const f32x4*>(src);
+        const f32x4 x1 = *reinterpret_cast<const f32x4*>(src + 4);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                v[q] += x0[q];
-                v[4 + q] += x1[q];
-            }
+        for (int q = 0; q < 4; ++q) {
+            v[q] = x0[q];
+            v[4 + q] = x1[q];
         }
     }
     hi = pack_bf16x8(v);
@@ -73,80 +66,77 @@ __device__ __forceinline__ u32x4 load_lora_b(const GemmArgs& a, int Nw, int ad, 
 }
 
 // ===========================================================================
-// Skinny variant: 16-row blocks (few rows per expert, weight streaming bound).
-// 4 waves split the K steps; each wave keeps 4 fragments (64 columns).
-template <bool GATEUP>
-__global__ __launch_bounds__(256) void k_gemm_skinny(GemmArgs a) {
-    constexpr int FN = 4;
-    const int b = blockIdx.x;
+// Skinny variant: 16-row blocks (few rows per expert: the weights are
+// streamed from HBM once and each byte feeds at most 16 rows).
+//
+// One wave is one workgroup and owns a 16-row x (16 FN)-column output tile
+// over the whole K range, so there is no cross-wave reduction, no LDS and no
+// barrier; thousands of independent waves fill the chip in a single round.
+// In each 64-wide K chunk lane (n, g) reads 32 contiguous bytes of weight row
+// n (elements 16 g .. 16 g + 15), so a wave-wide pair of loads consumes whole
+// 128-byte lines of 16 rows; the two 16-byte halves feed two MFMA K steps and
+// the activation operand uses the same K assignment. Loads of chunk q+1 are in
+// flight while chunk q is multiplied.
+template <bool GATEUP, int FN>
+__global__ __launch_bounds__(64) void k_gemm_skinny(GemmArgs a) {
+    const int b = blockIdx.y, tile = blockIdx.x;
     const int e = a.blk_e_b[b];
     if (e < 0) return;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int kc = lane >> 4, lrow = lane & 15;
+    const int lane = threadIdx.x & 63;
+    const int g = lane >> 4, lrow = lane & 15;
     const int I = GATEUP ? a.N_out : 0;
     const int Nw = GATEUP ? 2 * a.N_out : a.N_out;
-    const int c0 = blockIdx.y * (GATEUP ? 32 : 64);
+    constexpr int kCols = GATEUP ? FN * 8 : FN * 16;  // output columns per wave
+    const int c0 = tile * kCols;
     const int K = a.K;
 
     const int slot = b * 16 + lrow;
-    const int p = a.sorted_b[slot];
-    const uint16_t* xrow = nullptr;
+    // Padding rows (sentinel P) re-read the block's first row, which is always
+    // a real row: the duplicate addresses merge into the same memory request,
+    // MFMA output rows depend only on their own A row, and padding rows are
+    // never consumed, so no masking is needed and every load is issued
+    // unconditionally (exact wait counts).
+    const uint16_t* xrow;
     if (GATEUP) {
-        if (p < a.P) xrow = a.X + static_cast<size_t>(p / a.top_k) * K + kc * 8;
+        int p = a.sorted_b[slot];
+        if (p >= a.P) p = a.sorted_b[b * 16];
+        xrow = a.X + static_cast<size_t>(p / a.top_k) * K + g * 16;
     } else {
-        xrow = a.X + static_cast<size_t>(slot) * K + kc * 8;
+        xrow = a.X + static_cast<size_t>(slot) * K + g * 16;
     }
     const uint16_t* wrow[FN];
 #pragma unroll
     for (int f = 0; f < FN; ++f)
         wrow[f] = a.W + (static_cast<size_t>(e) * Nw + w_row_of_frag<GATEUP>(f, c0, I) + lrow) * K +
-                  kc * 8;
+                  g * 16;
 
     f32x4 acc[FN];
 #pragma unroll
     for (int f = 0; f < FN; ++f) acc[f] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const int nsteps = K / 32;
-    int s = wave;
-    for (; s + 12 < nsteps; s += 16) {
-        u32x4 xa[4], wb[4][FN];
+    u32x4 xb[2][2], wb[2][FN][2];
+    auto load = [&](int buf, int q) {
+        const int k0 = q * 64;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int k0 = (s + 4 * u) * 32;
-            xa[u] = xrow ? ld16(xrow + k0) : u32x4{0, 0, 0, 0};
+        for (int h = 0; h < 2; ++h) xb[buf][h] = ld16(xrow + k0 + 8 * h);
 #pragma unroll
-            for (int f = 0; f < FN; ++f) wb[u][f] = ld16_nt(wrow[f] + k0);
-        }
+        for (int f = 0; f < FN; ++f)
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
+            for (int h = 0; h < 2; ++h) wb[buf][f][h] = ld16(wrow[f] + k0 + 8 * h);
+    };
+    auto compute = [&](int buf) {
 #pragma unroll
-            for (int f = 0; f < FN; ++f) acc[f] = mfma16x16x32(xa[u], wb[u][f], acc[f]);
-    }
-    for (; s < nsteps; s += 4) {
-        const int k0 = s * 32;
-        const u32x4 xa = xrow ? ld16(xrow + k0) : u32x4{0, 0, 0, 0};
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int f = 0; f < FN; ++f) acc[f] = mfma16x16x32(xa, ld16_nt(wrow[f] + k0), acc[f]);
-    }
+            for (int f = 0; f < FN; ++f) acc[f] = mfma16x16x32(xb[buf][h], wb[buf][f][h], acc[f]);
+    };
 
-    __shared__ f32x4 red[4][FN][64];
-#pragma unroll
-    for (int f = 0; f < FN; ++f) red[wave][f][lane] = acc[f];
-    __syncthreads();
+    const int nq = K / 64;
+    load(0, 0);
+    __builtin_amdgcn_sched_barrier(0);
 
-    // finalising wave: gate_up -> wave w < 2 owns fragments (2w, 2w+1); down -> wave w owns w
-    constexpr int kOwn = GATEUP ? 2 : 1;
-    if (GATEUP && wave >= 2) return;
-    f32x4 v[kOwn];
-    int fidx[kOwn];
-#pragma unroll
-    for (int o = 0; o < kOwn; ++o) {
-        fidx[o] = wave * kOwn + o;
-        v[o] = red[0][fidx[o]][lane];
-#pragma unroll
-        for (int w = 1; w < 4; ++w) v[o] += red[w][fidx[o]][lane];
-    }
-
-    // LoRA expand, one pass per adapter present in the block
+    // LoRA expand first (its inputs are ready before this kernel starts), so
+    // its latency overlaps the first weight loads: acc += S . B^T for every
+    // adapter present among the 16 rows.
     if (a.L > 0) {
         const int my_a = row_adapter(a, slot);
         bool pending = my_a >= 0;
@@ -158,31 +148,55 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(GemmArgs a) {
             const bool in_run = pending && my_a == acur;
             pending = pending && !in_run;
             for (int kk = 0; kk < a.r; kk += 32) {
-                const int j0 = kk + kc * 8;
-                u32x4 hi, lo;
+                const int j0 = kk + g * 8;
+                u32x4 hi, lo, bb[FN];
+#pragma unroll
+                for (int f = 0; f < FN; ++f)
+                    bb[f] = load_lora_b(a, Nw, acur, e, w_row_of_frag<GATEUP>(f, c0, I) + lrow, j0);
                 load_s_hilo(a, slot, in_run, j0, hi, lo);
 #pragma unroll
-                for (int o = 0; o < kOwn; ++o) {
-                    const u32x4 bb = load_lora_b(a, Nw, acur, e,
-                                                 w_row_of_frag<GATEUP>(fidx[o], c0, I) + lrow, j0);
-                    v[o] = mfma16x16x32(hi, bb, v[o]);
-                    v[o] = mfma16x16x32(lo, bb, v[o]);
+                for (int f = 0; f < FN; ++f) {
+                    acc[f] = mfma16x16x32(hi, bb[f], acc[f]);
+                    acc[f] = mfma16x16x32(lo, bb[f], acc[f]);
                 }
             }
         }
     }
 
-    const int orow0 = b * 16 + 4 * kc;
+    // Two-stage register pipeline with one back edge and no early exit, so
+    // the prefetch stays in flight across iterations; scheduling barriers stop
+    // the compiler from sinking loads next to their use. A prefetch past the
+    // end re-reads the last chunk (in bounds) and is discarded.
+    int q = 0;
+    for (int i = 0; i + 1 < nq; i += 2, q += 2) {
+        load(1, q + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(0);
+        __builtin_amdgcn_sched_barrier(0);
+        load(0, min(q + 2, nq - 1));
+        __builtin_amdgcn_sched_barrier(0);
+        compute(1);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    if (nq & 1) compute(0);
+
+    const int orow0 = b * 16 + 4 * g;
     if (GATEUP) {
-        const int col = c0 + 16 * wave + lrow;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            a.h_out[static_cast<size_t>(orow0 + i) * a.N_out + col] =
-                f32_to_bf16_rne(silu(v[0][i]) * v[1][i]);
+        for (int u = 0; u < FN / 2; ++u) {
+            const int col = c0 + 16 * u + lrow;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                a.h_out[static_cast<size_t>(orow0 + i) * a.N_out + col] =
+                    f32_to_bf16_rne(silu(acc[2 * u][i]) * acc[2 * u + 1][i]);
+        }
     } else {
-        const int col = c0 + 16 * wave + lrow;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) a.d_out[static_cast<size_t>(orow0 + i) * a.N_out + col] = v[0][i];
+        for (int f = 0; f < FN; ++f) {
+            const int col = c0 + 16 * f + lrow;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a.d_out[static_cast<size_t>(orow0 + i) * a.N_out + col] = acc[f][i];
+        }
     }
 }
 
@@ -208,7 +222,7 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(GemmArgs a) {
     const int b = blockIdx.x;
     const int e = a.blk_e_b[b];
     if (e < 0) return;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
     const int wm = wave >> 1, wn = wave & 1;
     const int kc = lane >> 4, lrow = lane & 15;
     const int I = GATEUP ? a.N_out : 0;
@@ -222,14 +236,17 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(GemmArgs a) {
 
     // global -> LDS assignment: thread owns rows tid/8 + 32*i, chunk tid%8
     const int ld_row = tid >> 3, ld_chunk = tid & 7;
+    // padding rows re-read the block's first (real) row; their outputs are
+    // never consumed
     const uint16_t* asrc[C::A_LD];
+    const int p_first = a.sorted_b[row0];
 #pragma unroll
     for (int i = 0; i < C::A_LD; ++i) {
         const int r = ld_row + 32 * i;
         const int slot = row0 + r;
         if (GATEUP) {
             const int p = a.sorted_b[slot];
-            asrc[i] = p < a.P ? a.X + static_cast<size_t>(p / a.top_k) * K + ld_chunk * 8 : nullptr;
+            asrc[i] = a.X + static_cast<size_t>((p < a.P ? p : p_first) / a.top_k) * K + ld_chunk * 8;
         } else {
             asrc[i] = a.X + static_cast<size_t>(slot) * K + ld_chunk * 8;
         }
@@ -246,7 +263,7 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(GemmArgs a) {
     auto gload = [&](int kt) {
         const int k0 = kt * 64;
 #pragma unroll
-        for (int i = 0; i < C::A_LD; ++i) ra[i] = asrc[i] ? ld16(asrc[i] + k0) : u32x4{0, 0, 0, 0};
+        for (int i = 0; i < C::A_LD; ++i) ra[i] = ld16(asrc[i] + k0);
 #pragma unroll
         for (int i = 0; i < C::B_LD; ++i) rb[i] = ld16(bsrc[i] + k0);
     };
@@ -272,6 +289,7 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(GemmArgs a) {
     for (int kt = 0; kt < nk; ++kt) {
         const int buf = kt & 1;
         if (kt + 1 < nk) gload(kt + 1);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
             const int chunk = kk * 4 + kc;
@@ -289,6 +307,7 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(GemmArgs a) {
 #pragma unroll
                 for (int j = 0; j < FN; ++j) acc[i][j] = mfma16x16x32(fa[i], fb[j], acc[i][j]);
         }
+        __builtin_amdgcn_sched_barrier(0);
         if (kt + 1 < nk) lstore(buf ^ 1);
         __syncthreads();
     }
@@ -374,6 +393,16 @@ static int pick_bnt(int N_out, int gate_up, int bm) {
     return 0;
 }
 
+#ifndef MOELORA_SKINNY_FN
+#define MOELORA_SKINNY_FN 4
+#endif
+
+// fragments per skinny workgroup: 8 when the column count allows, else 4
+static int skinny_fn(int N_out, int gate_up) {
+    const int cols8 = gate_up ? 64 : 128;
+    return (MOELORA_SKINNY_FN == 8 && N_out % cols8 == 0) ? 8 : 4;
+}
+
 bool gemm_supported(int N_out, int K, int gate_up, int bm_b) {
     if (K % 64 != 0 || N_out % 32 != 0) return false;
     if (bm_b == 16) return N_out % (gate_up ? 32 : 64) == 0;
@@ -411,12 +440,17 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
     if (a.n_blocks == 0) return hipSuccess;
     if (!gemm_supported(a.N_out, a.K, a.gate_up, a.bm_b)) return hipErrorInvalidValue;
     if (a.bm_b == 16) {
-        const int cols = a.gate_up ? 32 : 64;
-        const dim3 grid(a.n_blocks, a.N_out / cols), block(256);
-        if (a.gate_up)
-            hipLaunchKernelGGL(k_gemm_skinny<true>, grid, block, 0, s, a);
-        else
-            hipLaunchKernelGGL(k_gemm_skinny<false>, grid, block, 0, s, a);
+        const int fn = skinny_fn(a.N_out, a.gate_up);
+        const int cols = a.gate_up ? fn * 8 : fn * 16;
+        if (a.n_blocks > 65535) return hipErrorInvalidValue;
+        const dim3 grid(a.N_out / cols, a.n_blocks), block(64);
+        if (fn == 8) {
+            if (a.gate_up) hipLaunchKernelGGL((k_gemm_skinny<true, 8>), grid, block, 0, s, a);
+            else hipLaunchKernelGGL((k_gemm_skinny<false, 8>), grid, block, 0, s, a);
+        } else {
+            if (a.gate_up) hipLaunchKernelGGL((k_gemm_skinny<true, 4>), grid, block, 0, s, a);
+            else hipLaunchKernelGGL((k_gemm_skinny<false, 4>), grid, block, 0, s, a);
+        }
         return hipGetLastError();
     }
     const int bnt = pick_bnt(a.N_out, a.gate_up, a.bm_b);

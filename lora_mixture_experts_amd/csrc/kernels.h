@@ -18,12 +18,12 @@ hipError_t launch_align(const int32_t* topk_ids, const int32_t* adapter_ids, int
                         int E, int L, int bm_b, int bm_l, int C_b, int C_l,
                         int32_t* sorted_b, int32_t* blk_e_b, int32_t* n_b,
                         int32_t* sorted_l, int32_t* blk_e_l, int32_t* blk_a_l, int32_t* n_l,
-                        int32_t* slot_of_pair, int32_t* lslot_of_pair, hipStream_t s);
+                        int32_t* slot_of_pair, int32_t* lslot_of_pair, int32_t* slot_adapter,
+                        int32_t* zero_buf, int zero_n, hipStream_t s);
 
 // ---- LoRA shrink ----------------------------------------------------------
-// S_part[split][slot][j] = sum over the split's K range of X[row] . A[a][e][j]
-// for the real rows of each LoRA-view block. gather_token: X row of pair p is
-// x[p / top_k] (else h[slot_of_pair[p]]).
+// S[slot][j] = X[row] . A[a][e][j] for the real rows of each LoRA-view block.
+// gather_token: X row of pair p is x[p / top_k] (else h[slot_of_pair[p]]).
 struct ShrinkArgs {
     const uint16_t* X;   // x [T][K] or h [C_b][K]
     int gather_token;
@@ -34,9 +34,7 @@ struct ShrinkArgs {
     const int32_t* slot_of_pair;
     const uint16_t* A;   // [L][E][r][K]
     int E, r, bm_l, n_blocks;
-    int nsplit;          // K split factor; K / nsplit is a multiple of 32
-    float* S_part;       // [nsplit][C_b][r]
-    int C_b;
+    float* S;            // [C_b][r]
 };
 hipError_t launch_shrink(const ShrinkArgs& a, hipStream_t s);
 
@@ -51,10 +49,10 @@ struct GemmArgs {
     int N_out;                // gate_up: I (h columns); down: H
     int K;                    // gate_up: H; down: I
     // LoRA expand
-    const int32_t* adapter_ids;
+    const int32_t* slot_adapter;  // [C_b] adapter of each base slot, -1 = none / padding
     int L, E, r;
-    const float* S_part;      // [nsplit][C_b][r] (may be null when L == 0)
-    int nsplit, C_b;
+    const float* S;           // [C_b][r] shrink output (unused when L == 0)
+    int C_b;
     const uint16_t* Bl;       // gate_up: [L][E][2I][r]; down: [L][E][H][r]
     // outputs
     uint16_t* h_out;          // [C_b][I]

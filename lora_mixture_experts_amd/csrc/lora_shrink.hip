@@ -1,121 +1,114 @@
-// LoRA shrink S = X . A^T (rank r) over the LoRA-view blocks, split along K.
+// LoRA shrink S = X . A^T (rank r) over the LoRA-view blocks.
 //
 // Shrink is the skinny "xA" product of the AWS ML Blog post "Efficiently serve
 // dozens of fine-tuned models with vLLM on Amazon SageMaker AI and Amazon
 // Bedrock", section "Kernel optimizations": splitting the K reduction across
-// thread groups balances the load of such skinny products. Here each
-// workgroup owns (LoRA block, K split); the four waves of a workgroup share
-// the block's rows and interleave 32-wide K steps; partial sums go to a
-// per-split slice of S_part instead of atomics, and the consumer (the expand
-// fused into the projection kernel) adds the slices in a fixed order, so the
-// result is deterministic.
+// thread groups balances the load of such skinny products. Here one
+// 1024-thread workgroup owns a LoRA block (rows of one expert x adapter
+// segment); its 16 waves split the block into (16-row fragment, K part) pairs,
+// so even a block with a single real row keeps 16 waves streaming A. The K
+// parts are added through LDS in a fixed order: no atomics, no cross-workgroup
+// traffic, and the result is deterministic. Each output element is written
+// once, in base-slot order, for the expand fused into the projection kernel.
 #include "common.h"
 #include "kernels.h"
 
 namespace moelora {
 
-constexpr int kShrinkMaxFN = 8;  // r <= 128
+constexpr int kShrinkThreads = 1024;
+constexpr int kShrinkWaves = kShrinkThreads / 64;
 
 template <int FN>
-__global__ __launch_bounds__(256) void k_shrink(ShrinkArgs a) {
-    const int b = blockIdx.x, split = blockIdx.y;
+__global__ __launch_bounds__(kShrinkThreads) void k_shrink(ShrinkArgs a) {
+    const int b = blockIdx.x;
     const int e = a.blk_e_l[b];
     if (e < 0) return;
     const int ad = a.blk_a_l[b];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = wave_id();
     const int kc = lane >> 4, lrow = lane & 15;
-    const int Ks = a.K / a.nsplit;
-    const int k_begin = split * Ks;
-    const int nsteps = Ks / 32;
-    const uint16_t* Abase = a.A + (static_cast<size_t>(ad) * a.E + e) * a.r * a.K;
+    const int nfm = a.bm_l / 16;               // 16-row fragments in the block (1..16)
+    const int nkp = kShrinkWaves / nfm;        // K parts per fragment
+    const int fm = wave / nkp, kp = wave % nkp;
+    const int nsteps = a.K / 32;
+    const int s0 = kp * nsteps / nkp, s1 = (kp + 1) * nsteps / nkp;
 
-    // B operand rows (LoRA A rows j = fn*16 + lrow), zero past r
+    // A operand row (block row fm*16 + lrow); padding rows re-read the
+    // block's first (real) row, merging into the same memory requests, and
+    // their outputs are never stored
+    int p = a.sorted_l[b * a.bm_l + fm * 16 + lrow];
+    if (p >= a.P) p = a.sorted_l[b * a.bm_l];
+    const size_t row = a.gather_token ? static_cast<size_t>(p / a.top_k)
+                                      : static_cast<size_t>(a.slot_of_pair[p]);
+    const uint16_t* xrow = a.X + row * a.K + kc * 8;
+    // B operand rows (LoRA A rows j = fn*16 + lrow); columns j >= r (r = 8)
+    // re-read row j - 8 and are never stored, so loads stay unconditional
+    const uint16_t* Abase = a.A + (static_cast<size_t>(ad) * a.E + e) * a.r * a.K;
     const uint16_t* brow[FN];
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn) {
         const int j = fn * 16 + lrow;
-        brow[fn] = j < a.r ? Abase + static_cast<size_t>(j) * a.K + k_begin + kc * 8 : nullptr;
+        brow[fn] = Abase + static_cast<size_t>(j < a.r ? j : j - 8) * a.K + kc * 8;
     }
 
-    __shared__ f32x4 red[3][kShrinkMaxFN][64];
-    const int nfm_total = a.bm_l / 16;
-    for (int fm = 0; fm < nfm_total; ++fm) {
-        // A operand row (block row fm*16 + lrow)
-        const int p = a.sorted_l[b * a.bm_l + fm * 16 + lrow];
-        const uint16_t* xrow = nullptr;
-        if (p < a.P) {
-            const size_t row = a.gather_token ? static_cast<size_t>(p / a.top_k)
-                                              : static_cast<size_t>(a.slot_of_pair[p]);
-            xrow = a.X + row * a.K + k_begin + kc * 8;
-        }
-        // a whole 16-row fragment of padding contributes nothing
-        if (!__any(xrow != nullptr)) continue;
-
-        f32x4 acc[FN];
+    f32x4 acc[FN];
 #pragma unroll
-        for (int fn = 0; fn < FN; ++fn) acc[fn] = f32x4{0.f, 0.f, 0.f, 0.f};
-        int s = wave;
-        for (; s + 12 < nsteps; s += 16) {  // four steps per round, loads first
+    for (int fn = 0; fn < FN; ++fn) acc[fn] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // skip fragments made only of padding (the decision is uniform per wave)
+    const bool live = a.sorted_l[b * a.bm_l + fm * 16] < a.P;
+    if (live) {
+        int s = s0;
+        for (; s + 3 < s1; s += 4) {  // four steps per round, loads first
             u32x4 xa[4], wb[4][FN];
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                const int k0 = (s + 4 * u) * 32;
-                xa[u] = xrow ? ld16(xrow + k0) : u32x4{0, 0, 0, 0};
+                const int k0 = (s + u) * 32;
+                xa[u] = ld16(xrow + k0);
 #pragma unroll
-                for (int fn = 0; fn < FN; ++fn)
-                    wb[u][fn] = brow[fn] ? ld16(brow[fn] + k0) : u32x4{0, 0, 0, 0};
+                for (int fn = 0; fn < FN; ++fn) wb[u][fn] = ld16(brow[fn] + k0);
             }
 #pragma unroll
             for (int u = 0; u < 4; ++u)
 #pragma unroll
                 for (int fn = 0; fn < FN; ++fn) acc[fn] = mfma16x16x32(xa[u], wb[u][fn], acc[fn]);
         }
-        for (; s < nsteps; s += 4) {
+        for (; s < s1; ++s) {
             const int k0 = s * 32;
-            const u32x4 xa = xrow ? ld16(xrow + k0) : u32x4{0, 0, 0, 0};
+            const u32x4 xa = ld16(xrow + k0);
 #pragma unroll
-            for (int fn = 0; fn < FN; ++fn) {
-                const u32x4 wb = brow[fn] ? ld16(brow[fn] + k0) : u32x4{0, 0, 0, 0};
-                acc[fn] = mfma16x16x32(xa, wb, acc[fn]);
-            }
+            for (int fn = 0; fn < FN; ++fn) acc[fn] = mfma16x16x32(xa, ld16(brow[fn] + k0), acc[fn]);
         }
-        // reduce the four waves' partial sums (fixed order) and store
-        if (wave > 0) {
+    }
+
+    // add the K parts of each fragment in order 0..nkp-1 and store
+    __shared__ f32x4 red[kShrinkWaves][FN][64];
 #pragma unroll
-            for (int fn = 0; fn < FN; ++fn) red[wave - 1][fn][lane] = acc[fn];
+    for (int fn = 0; fn < FN; ++fn) red[wave][fn][lane] = acc[fn];
+    __syncthreads();
+    if (kp != 0 || !live) return;
+    int oslot[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int q = a.sorted_l[b * a.bm_l + fm * 16 + 4 * kc + i];
+        oslot[i] = q < a.P ? a.slot_of_pair[q] : -1;
+    }
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) {
+        f32x4 v = red[wave][fn][lane];
+        for (int w = 1; w < nkp; ++w) v += red[wave + w][fn][lane];
+        const int j = fn * 16 + lrow;
+        if (j < a.r) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (oslot[i] >= 0) a.S[static_cast<size_t>(oslot[i]) * a.r + j] = v[i];
         }
-        __syncthreads();
-        if (wave == 0) {
-            // output rows of this lane: 4*kc + i
-            int oslot[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int q = a.sorted_l[b * a.bm_l + fm * 16 + 4 * kc + i];
-                oslot[i] = q < a.P ? a.slot_of_pair[q] : -1;
-            }
-#pragma unroll
-            for (int fn = 0; fn < FN; ++fn) {
-                f32x4 v = acc[fn];
-#pragma unroll
-                for (int w = 0; w < 3; ++w) v += red[w][fn][lane];
-                const int j = fn * 16 + lrow;
-                if (j < a.r) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        if (oslot[i] >= 0)
-                            a.S_part[(static_cast<size_t>(split) * a.C_b + oslot[i]) * a.r + j] = v[i];
-                }
-            }
-        }
-        __syncthreads();
     }
 }
 
 hipError_t launch_shrink(const ShrinkArgs& a, hipStream_t s) {
     if (a.n_blocks == 0) return hipSuccess;
-    const dim3 grid(a.n_blocks, a.nsplit), block(256);
-    const int fn = (a.r + 15) / 16;
-    switch (fn) {
+    if (a.bm_l < 16 || a.bm_l > 256 || (kShrinkWaves % (a.bm_l / 16)) != 0) return hipErrorInvalidValue;
+    const dim3 grid(a.n_blocks), block(kShrinkThreads);
+    switch ((a.r + 15) / 16) {
         case 1: hipLaunchKernelGGL(k_shrink<1>, grid, block, 0, s, a); break;
         case 2: hipLaunchKernelGGL(k_shrink<2>, grid, block, 0, s, a); break;
         case 4: hipLaunchKernelGGL(k_shrink<4>, grid, block, 0, s, a); break;

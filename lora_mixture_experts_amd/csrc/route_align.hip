@@ -163,7 +163,8 @@ __global__ __launch_bounds__(kAlignThreads) void k_align(
     int32_t* __restrict__ sorted_b, int32_t* __restrict__ blk_e_b, int32_t* __restrict__ n_b_out,
     int32_t* __restrict__ sorted_l, int32_t* __restrict__ blk_e_l, int32_t* __restrict__ blk_a_l,
     int32_t* __restrict__ n_l_out, int32_t* __restrict__ slot_of_pair,
-    int32_t* __restrict__ lslot_of_pair) {
+    int32_t* __restrict__ lslot_of_pair, int32_t* __restrict__ slot_adapter,
+    int32_t* __restrict__ zero_buf, int zero_n) {
     __shared__ int lds[kAlignLdsInts];
     const int L1 = L + 1;
     const int nkeys = E * L1, nseg = E * L, P = T * k;
@@ -173,7 +174,7 @@ __global__ __launch_bounds__(kAlignThreads) void k_align(
     int* lpos = bpos + nkeys;        // [nseg]   LoRA-view start of each segment
     int* ne = lpos + nseg;           // [E]      pairs per expert
     int* red = ne + E;               // [64]
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
     const int nbits = nkeys > 1 ? 32 - __clz(nkeys - 1) : 0;
 
     auto pair_key = [&](int p) {
@@ -185,6 +186,7 @@ __global__ __launch_bounds__(kAlignThreads) void k_align(
 
     for (int i = tid; i < nw * nkeys; i += kAlignThreads) hist[i] = 0;
     for (int i = tid; i < E; i += kAlignThreads) ne[i] = 0;
+    for (int i = tid; i < zero_n; i += kAlignThreads) zero_buf[i] = 0;
     __syncthreads();
 
     // 1. per-wave key histograms
@@ -229,9 +231,15 @@ __global__ __launch_bounds__(kAlignThreads) void k_align(
     for (int idx = tid; idx < E * bm_b; idx += kAlignThreads) {
         const int e = idx / bm_b, i = idx % bm_b;
         const int last = e * L1 + L;
-        if (i < roundup_i(ne[e], bm_b) - ne[e]) sorted_b[bpos[last] + cnt[last] + i] = P;
+        if (i < roundup_i(ne[e], bm_b) - ne[e]) {
+            sorted_b[bpos[last] + cnt[last] + i] = P;
+            if (slot_adapter) slot_adapter[bpos[last] + cnt[last] + i] = -1;
+        }
     }
-    for (int i = n_b + tid; i < C_b; i += kAlignThreads) sorted_b[i] = P;
+    for (int i = n_b + tid; i < C_b; i += kAlignThreads) {
+        sorted_b[i] = P;
+        if (slot_adapter) slot_adapter[i] = -1;
+    }
     for (int idx = tid; idx < nseg * bm_l; idx += kAlignThreads) {
         const int s = idx / bm_l, i = idx % bm_l;
         const int c = cnt[(s / L) * L1 + s % L];
@@ -295,6 +303,7 @@ __global__ __launch_bounds__(kAlignThreads) void k_align(
                     sorted_l[lslot] = p;
                 }
                 if (lslot_of_pair) lslot_of_pair[p] = lslot;
+                if (slot_adapter) slot_adapter[slot] = ap < L ? ap : -1;
             }
         }
     }
@@ -304,7 +313,8 @@ hipError_t launch_align(const int32_t* topk_ids, const int32_t* adapter_ids, int
                         int E, int L, int bm_b, int bm_l, int C_b, int C_l,
                         int32_t* sorted_b, int32_t* blk_e_b, int32_t* n_b,
                         int32_t* sorted_l, int32_t* blk_e_l, int32_t* blk_a_l, int32_t* n_l,
-                        int32_t* slot_of_pair, int32_t* lslot_of_pair, hipStream_t s) {
+                        int32_t* slot_of_pair, int32_t* lslot_of_pair, int32_t* slot_adapter,
+                        int32_t* zero_buf, int zero_n, hipStream_t s) {
     const int nw = align_hist_waves(E, L);
     if (nw <= 0) return hipErrorInvalidValue;
     const int P = T * k;
@@ -312,7 +322,8 @@ hipError_t launch_align(const int32_t* topk_ids, const int32_t* adapter_ids, int
     const int R = ((per + 63) / 64) * 64;
     hipLaunchKernelGGL(k_align, dim3(1), dim3(kAlignThreads), 0, s, topk_ids, adapter_ids, T, k,
                        E, L, bm_b, bm_l, C_b, C_l, nw, R > 0 ? R : 64, sorted_b, blk_e_b, n_b,
-                       sorted_l, blk_e_l, blk_a_l, n_l, slot_of_pair, lslot_of_pair);
+                       sorted_l, blk_e_l, blk_a_l, n_l, slot_of_pair, lslot_of_pair, slot_adapter,
+                       zero_buf, zero_n);
     return hipGetLastError();
 }
 

@@ -201,119 +201,59 @@ __global__ __launch_bounds__(64) void k_gemm_skinny(GemmArgs a) {
 }
 
 // ===========================================================================
-// Tiled variant: BM x BNT tile (BNT = GEMM columns), BK = 64, LDS double
-// buffer with an XOR swizzle of the 16-byte chunks, 2 x 2 waves.
-template <int BM, int BNT>
+// Tiled variant: BM x BNT tile (BNT = GEMM columns), BK = 64, 2 x 2 waves,
+// LDS double buffer with an XOR swizzle of the 16-byte chunks, and global
+// loads issued two K steps ahead through two register sets, so a load has two
+// steps of MFMA work to arrive.
+//
+// Tile order (the MI355X form of CTA swizzling, AWS ML Blog post "Efficiently
+// serve dozens of fine-tuned models with vLLM on Amazon SageMaker AI and
+// Amazon Bedrock", Korean summary, section "Kernel-level optimization"): the
+// 1-D grid is dealt round-robin to the 8 XCDs, each with its own L2, so
+// workgroup i is mapped to logical tile (i % 8) * chunk + i / 8: every XCD
+// walks its own contiguous range of logical tiles. Logically, N tiles are
+// taken in groups of kGroupN; inside a group, M blocks (consecutive blocks
+// belong to one expert) run major and N tiles minor. The workgroups resident
+// on one XCD then share the same expert's weight tiles and the same
+// activation rows, and reread them from L2 instead of HBM.
+template <int BM, int BNT, int WM, int WN>
 struct TileCfg {
-    static constexpr int FM = BM / 32;   // 16-row fragments per wave
-    static constexpr int FN = BNT / 32;  // 16-col fragments per wave
-    static constexpr int A_LD = BM / 32;   // 16-byte chunks per thread per stage
-    static constexpr int B_LD = BNT / 32;
+    static constexpr int NT = 64 * WM * WN;      // threads
+    static constexpr int FM = BM / (16 * WM);    // 16-row fragments per wave
+    static constexpr int FN = BNT / (16 * WN);   // 16-col fragments per wave
+    static constexpr int A_LD = BM * 8 / NT;     // 16-byte chunks per thread per stage
+    static constexpr int B_LD = BNT * 8 / NT;
+    static constexpr int ROWS_PER_PASS = NT / 8;
     static constexpr int A_ELEMS = BM * 64;
     static constexpr int B_ELEMS = BNT * 64;
+    static_assert(FM >= 1 && FN >= 1 && A_LD >= 1 && B_LD >= 1, "tile too small");
 };
+constexpr int kGroupN = 8;
+constexpr int kXcds = 8;
 
 __device__ __forceinline__ int swz(int row, int chunk) { return row * 64 + ((chunk ^ (row & 7)) << 3); }
 
-template <int BM, int BNT, bool GATEUP>
-__global__ __launch_bounds__(256) void k_gemm_tiled(GemmArgs a) {
-    using C = TileCfg<BM, BNT>;
-    constexpr int FM = C::FM, FN = C::FN;
-    const int b = blockIdx.x;
-    const int e = a.blk_e_b[b];
-    if (e < 0) return;
-    const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
-    const int wm = wave >> 1, wn = wave & 1;
-    const int kc = lane >> 4, lrow = lane & 15;
-    const int I = GATEUP ? a.N_out : 0;
+// output columns of a tile and the number of tiles (the last may be partial)
+template <int BNT, bool GATEUP>
+__host__ __device__ constexpr int tile_cols() { return GATEUP ? BNT / 2 : BNT; }
+
+// grid size for n_blocks x n_tiles logical tiles
+static inline int tiled_grid(int n_blocks, int n_tiles) {
+    const int groups = (n_tiles + kGroupN - 1) / kGroupN;
+    const long total = static_cast<long>(groups) * n_blocks * kGroupN;
+    return static_cast<int>((total + kXcds - 1) / kXcds * kXcds);
+}
+
+// Tile epilogue shared by the LDS kernels: the LoRA expand for every adapter
+// present among the wave's rows (extra MFMA K steps on the accumulators), then
+// SwiGLU + bf16 store (gate_up) or the fp32 store (down). wrow_of maps a tile
+// row (GEMM column) to its weight row.
+template <int FM, int FN, bool GATEUP, typename WRowOf>
+__device__ __forceinline__ void tile_epilogue(const GemmArgs& a, f32x4 (&acc)[FM][FN], bool wlive,
+                                              int wrow_base, int wn, int c0, int e, int kc,
+                                              int lrow, WRowOf wrow_of) {
+    if (!wlive) return;
     const int Nw = GATEUP ? 2 * a.N_out : a.N_out;
-    const int c0 = blockIdx.y * (GATEUP ? BNT / 2 : BNT);
-    const int K = a.K;
-    const int row0 = b * BM;
-
-    __shared__ __attribute__((aligned(16))) uint16_t As[2][C::A_ELEMS];
-    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][C::B_ELEMS];
-
-    // global -> LDS assignment: thread owns rows tid/8 + 32*i, chunk tid%8
-    const int ld_row = tid >> 3, ld_chunk = tid & 7;
-    // padding rows re-read the block's first (real) row; their outputs are
-    // never consumed
-    const uint16_t* asrc[C::A_LD];
-    const int p_first = a.sorted_b[row0];
-#pragma unroll
-    for (int i = 0; i < C::A_LD; ++i) {
-        const int r = ld_row + 32 * i;
-        const int slot = row0 + r;
-        if (GATEUP) {
-            const int p = a.sorted_b[slot];
-            asrc[i] = a.X + static_cast<size_t>((p < a.P ? p : p_first) / a.top_k) * K + ld_chunk * 8;
-        } else {
-            asrc[i] = a.X + static_cast<size_t>(slot) * K + ld_chunk * 8;
-        }
-    }
-    const uint16_t* bsrc[C::B_LD];
-#pragma unroll
-    for (int i = 0; i < C::B_LD; ++i) {
-        const int r = ld_row + 32 * i;
-        const int wr = w_row_of_frag<GATEUP>(r >> 4, c0, I) + (r & 15);
-        bsrc[i] = a.W + (static_cast<size_t>(e) * Nw + wr) * K + ld_chunk * 8;
-    }
-
-    u32x4 ra[C::A_LD], rb[C::B_LD];
-    auto gload = [&](int kt) {
-        const int k0 = kt * 64;
-#pragma unroll
-        for (int i = 0; i < C::A_LD; ++i) ra[i] = ld16(asrc[i] + k0);
-#pragma unroll
-        for (int i = 0; i < C::B_LD; ++i) rb[i] = ld16(bsrc[i] + k0);
-    };
-    auto lstore = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < C::A_LD; ++i)
-            *reinterpret_cast<u32x4*>(&As[buf][swz(ld_row + 32 * i, ld_chunk)]) = ra[i];
-#pragma unroll
-        for (int i = 0; i < C::B_LD; ++i)
-            *reinterpret_cast<u32x4*>(&Bs[buf][swz(ld_row + 32 * i, ld_chunk)]) = rb[i];
-    };
-
-    f32x4 acc[FM][FN];
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    const int nk = K / 64;
-    gload(0);
-    lstore(0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-        const int buf = kt & 1;
-        if (kt + 1 < nk) gload(kt + 1);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            const int chunk = kk * 4 + kc;
-            u32x4 fa[FM], fb[FN];
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-                fa[i] = *reinterpret_cast<const u32x4*>(
-                    &As[buf][swz(wm * (BM / 2) + i * 16 + lrow, chunk)]);
-#pragma unroll
-            for (int j = 0; j < FN; ++j)
-                fb[j] = *reinterpret_cast<const u32x4*>(
-                    &Bs[buf][swz(wn * (BNT / 2) + j * 16 + lrow, chunk)]);
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j) acc[i][j] = mfma16x16x32(fa[i], fb[j], acc[i][j]);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        if (kt + 1 < nk) lstore(buf ^ 1);
-        __syncthreads();
-    }
-
-    // LoRA expand: per distinct adapter among this wave's rows
-    const int wrow_base = row0 + wm * (BM / 2);
     if (a.L > 0) {
         int my_a[FM];
         bool pending[FM];
@@ -335,8 +275,7 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(GemmArgs a) {
                 u32x4 bb[FN];
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
-                    bb[j] = load_lora_b(a, Nw, cand, e,
-                                        w_row_of_frag<GATEUP>(wn * FN + j, c0, I) + lrow, j0);
+                    bb[j] = load_lora_b(a, Nw, cand, e, wrow_of((wn * FN + j) * 16 + lrow), j0);
 #pragma unroll
                 for (int i = 0; i < FM; ++i) {
                     const bool in_run = pending[i] && my_a[i] == cand;
@@ -355,8 +294,6 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(GemmArgs a) {
                 if (pending[i] && my_a[i] == cand) pending[i] = false;
         }
     }
-
-    // epilogue
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
         const int orow0 = wrow_base + i * 16 + 4 * kc;
@@ -364,6 +301,7 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(GemmArgs a) {
 #pragma unroll
             for (int j = 0; j < FN; j += 2) {
                 const int col = c0 + 16 * ((wn * FN + j) >> 1) + lrow;
+                if (col >= a.N_out) continue;
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
                     a.h_out[static_cast<size_t>(orow0 + q) * a.N_out + col] =
@@ -373,6 +311,7 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(GemmArgs a) {
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
                 const int col = c0 + 16 * (wn * FN + j) + lrow;
+                if (col >= a.N_out) continue;
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
                     a.d_out[static_cast<size_t>(orow0 + q) * a.N_out + col] = acc[i][j][q];
@@ -381,16 +320,364 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(GemmArgs a) {
     }
 }
 
-// ---------------------------------------------------------------------------
-static int pick_bnt(int N_out, int gate_up, int bm) {
-    // GEMM columns per tile; gate_up tiles cover BNT/2 activation columns
-    const int prefs_big[] = {192, 128, 64};
-    for (int bnt : prefs_big) {
-        if (bm == 256 && bnt > 128) continue;
-        const int cols = gate_up ? bnt / 2 : bnt;
-        if (N_out % cols == 0) return bnt;
+template <int BM, int BNT, int WM, int WN, bool GATEUP>
+__global__ __launch_bounds__(64 * WM * WN) void k_gemm_tiled(GemmArgs a) {
+    using C = TileCfg<BM, BNT, WM, WN>;
+    constexpr int FM = C::FM, FN = C::FN;
+    static_assert(!GATEUP || FN % 2 == 0, "gate/up fragments come in pairs");
+    constexpr int kCols = tile_cols<BNT, GATEUP>();
+    const int n_tiles = (a.N_out + kCols - 1) / kCols;
+    // physical -> logical tile
+    const int chunk = gridDim.x / kXcds;
+    const int t = (blockIdx.x % kXcds) * chunk + blockIdx.x / kXcds;
+    const int per_group = a.n_blocks * kGroupN;
+    const int ng = t / per_group, rem = t % per_group;
+    const int b = rem / kGroupN, tile = ng * kGroupN + rem % kGroupN;
+    if (tile >= n_tiles) return;
+    const int e = a.blk_e_b[b];
+    if (e < 0) return;
+    const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+    const int wm = wave / WN, wn = wave % WN;
+    const int kc = lane >> 4, lrow = lane & 15;
+    const int I = GATEUP ? a.N_out : 0;
+    const int Nw = GATEUP ? 2 * a.N_out : a.N_out;
+    const int c0 = tile * kCols;
+    const int K = a.K;
+    const int row0 = b * BM;
+    // weight row of tile row r (columns past N_out, in a partial last tile,
+    // re-read the last valid row; their results are not stored)
+    auto wrow_of = [&](int r) {
+        const int f = r >> 4;
+        int col = c0 + 16 * (GATEUP ? (f >> 1) : f) + (r & 15);
+        col = min(col, a.N_out - 1);
+        return (GATEUP && (f & 1)) ? I + col : col;
+    };
+
+    __shared__ __attribute__((aligned(16))) uint16_t As[2][C::A_ELEMS];
+    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][C::B_ELEMS];
+
+    // global -> LDS assignment: thread owns rows tid/8 + (NT/8)*i, chunk tid%8
+    const int ld_row = tid >> 3, ld_chunk = tid & 7;
+    // padding rows re-read the block's first (real) row; their outputs are
+    // never consumed
+    const uint16_t* asrc[C::A_LD];
+    const int p_first = a.sorted_b[row0];
+#pragma unroll
+    for (int i = 0; i < C::A_LD; ++i) {
+        const int r = ld_row + C::ROWS_PER_PASS * i;
+        const int slot = row0 + r;
+        if (GATEUP) {
+            const int p = a.sorted_b[slot];
+            asrc[i] = a.X + static_cast<size_t>((p < a.P ? p : p_first) / a.top_k) * K + ld_chunk * 8;
+        } else {
+            asrc[i] = a.X + static_cast<size_t>(slot) * K + ld_chunk * 8;
+        }
     }
-    return 0;
+    const uint16_t* bsrc[C::B_LD];
+#pragma unroll
+    for (int i = 0; i < C::B_LD; ++i) {
+        const int r = ld_row + C::ROWS_PER_PASS * i;
+        bsrc[i] = a.W + (static_cast<size_t>(e) * Nw + wrow_of(r)) * K + ld_chunk * 8;
+    }
+
+    // A wave whose first row is padding holds no real row (rows are real
+    // first, then padding): it skips its MFMAs and stores. The test is uniform
+    // per wave and sits outside the K loop's inner loops, which stay
+    // branch-free so that LDS reads overlap the MFMAs.
+    const int wrow_base = row0 + wm * (BM / WM);
+    const bool wlive = a.sorted_b[wrow_base] < a.P;
+    u32x4 ra[2][C::A_LD], rb[2][C::B_LD];
+    const int nk = K / 64;
+    auto gload = [&](int set, int kt) {
+        const int k0 = kt * 64;
+#pragma unroll
+        for (int i = 0; i < C::A_LD; ++i) ra[set][i] = ld16(asrc[i] + k0);
+#pragma unroll
+        for (int i = 0; i < C::B_LD; ++i) rb[set][i] = ld16(bsrc[i] + k0);
+    };
+    auto lstore = [&](int buf, int set) {
+#pragma unroll
+        for (int i = 0; i < C::A_LD; ++i)
+            *reinterpret_cast<u32x4*>(&As[buf][swz(ld_row + C::ROWS_PER_PASS * i, ld_chunk)]) = ra[set][i];
+#pragma unroll
+        for (int i = 0; i < C::B_LD; ++i)
+            *reinterpret_cast<u32x4*>(&Bs[buf][swz(ld_row + C::ROWS_PER_PASS * i, ld_chunk)]) = rb[set][i];
+    };
+
+    f32x4 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto compute = [&](int buf) {
+        if (!wlive) return;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            const int chunk = kk * 4 + kc;
+            u32x4 fa[FM], fb[FN];
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                fb[j] = *reinterpret_cast<const u32x4*>(
+                    &Bs[buf][swz(wn * (BNT / WN) + j * 16 + lrow, chunk)]);
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+                fa[i] = *reinterpret_cast<const u32x4*>(
+                    &As[buf][swz(wm * (BM / WM) + i * 16 + lrow, chunk)]);
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j) acc[i][j] = mfma16x16x32(fa[i], fb[j], acc[i][j]);
+        }
+    };
+
+    // Stage s sits in LDS buffer s & 1. Loads past the last stage re-read it
+    // (in bounds) so that every load and LDS store is unconditional and the
+    // compiler keeps exact wait counts across the unrolled loop.
+    gload(0, 0);
+    lstore(0, 0);
+    gload(1, min(1, nk - 1));
+    __syncthreads();
+    int kt = 0;
+    for (; kt + 1 < nk; kt += 2) {
+        gload(0, min(kt + 2, nk - 1));
+        __builtin_amdgcn_sched_barrier(0);
+        compute(0);
+        __builtin_amdgcn_sched_barrier(0);
+        lstore(1, 1);
+        __syncthreads();
+        gload(1, min(kt + 3, nk - 1));
+        __builtin_amdgcn_sched_barrier(0);
+        compute(1);
+        __builtin_amdgcn_sched_barrier(0);
+        lstore(0, 0);
+        __syncthreads();
+    }
+    if (nk & 1) compute(0);
+
+    tile_epilogue<FM, FN, GATEUP>(a, acc, wlive, wrow_base, wn, c0, e, kc, lrow, wrow_of);
+}
+
+// ===========================================================================
+// DMA variant for large blocks: the same tile order, fragment layout and
+// epilogue as the tiled variant, but the global -> LDS copy uses gfx950's
+// direct loads (global_load_lds_dwordx4): each wave-wide load deposits 64 x
+// 16 bytes into a contiguous 1 KiB of LDS in lane order, so no registers hold
+// staged tiles and no LDS store instructions are issued. A lane picks the
+// global chunk that its LDS slot must hold under the XOR swizzle. NS LDS
+// stages form a ring: stage k+NS-1 is requested while stage k is multiplied.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    // s_waitcnt with vmcnt = N (gfx9 encoding: bits 3:0 and 15:14); expcnt and
+    // lgkmcnt at their maximum, i.e. not waited on
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int FM, int FN, int A_PW, int B_PW>
+struct DmaCtx {
+    const uint16_t* const* asrc;
+    const uint16_t* const* bsrc;
+    int wave, arow0, brow0, kc, lrow;
+    bool wlive;
+};
+
+// One direct global -> LDS load of 16 bytes per lane: lane l's data lands at
+// LDS byte offset lds + 16 l. Written as inline assembly so that the compiler
+// does not see an LDS write it cannot disambiguate from the reads of the
+// other pipeline stages (it would otherwise drain every load in flight before
+// each LDS read); the kernel orders these loads itself with explicit vmcnt
+// waits and barriers.
+__device__ __forceinline__ void dma16(const void* g, const uint16_t* lds) {
+    const uint32_t l = static_cast<uint32_t>(
+        reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)(lds)));
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(l), "v"(g) : "m0", "memory");
+}
+
+// workgroup barrier without the memory fence of __syncthreads (that fence
+// would wait for the stages requested ahead); the memory clobber keeps the
+// compiler from moving LDS accesses across it
+__device__ __forceinline__ void bare_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+template <int A_PW, int B_PW>
+__device__ __forceinline__ void dma_issue(const uint16_t* const* asrc, const uint16_t* const* bsrc,
+                                          uint16_t* ab, uint16_t* bb, int wave, int k0) {
+#pragma unroll
+    for (int i = 0; i < A_PW; ++i) dma16(asrc[i] + k0, ab + (wave * A_PW + i) * 512);
+#pragma unroll
+    for (int i = 0; i < B_PW; ++i) dma16(bsrc[i] + k0, bb + (wave * B_PW + i) * 512);
+}
+
+// Request the stage at K offset k_next (if >= 0) into (na, nb) and multiply
+// the stage held in (ca, cb). The restrict qualifiers tell the compiler that
+// the buffers being filled and the buffers being read do not overlap, so it
+// does not wait for the new requests before the LDS reads.
+template <int FM, int FN, int A_PW, int B_PW>
+__device__ __forceinline__ void dma_step(const DmaCtx<FM, FN, A_PW, B_PW>& c, f32x4 (&acc)[FM][FN],
+                                         const uint16_t* __restrict__ ca,
+                                         const uint16_t* __restrict__ cb, uint16_t* __restrict__ na,
+                                         uint16_t* __restrict__ nb, int k_next) {
+    if (k_next >= 0) dma_issue<A_PW, B_PW>(c.asrc, c.bsrc, na, nb, c.wave, k_next);
+    __builtin_amdgcn_sched_barrier(0);
+    if (!c.wlive) return;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+        const int ch = kk * 4 + c.kc;
+        u32x4 fa[FM], fb[FN];
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+            fb[j] = *reinterpret_cast<const u32x4*>(&cb[swz(c.brow0 + j * 16 + c.lrow, ch)]);
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+            fa[i] = *reinterpret_cast<const u32x4*>(&ca[swz(c.arow0 + i * 16 + c.lrow, ch)]);
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) acc[i][j] = mfma16x16x32(fa[i], fb[j], acc[i][j]);
+    }
+}
+
+template <int BM, int BNT, int WM, int WN, int NS, bool GATEUP>
+__global__ __launch_bounds__(64 * WM * WN) void k_gemm_dma(GemmArgs a) {
+    constexpr int NW = WM * WN;
+    constexpr int FM = BM / (16 * WM), FN = BNT / (16 * WN);
+    constexpr int A_PW = BM / 8 / NW, B_PW = BNT / 8 / NW;  // 1 KiB blocks per wave per stage
+    constexpr int LPS = A_PW + B_PW;                          // loads per wave per stage
+    static_assert(A_PW * NW * 8 == BM && B_PW * NW * 8 == BNT, "tile rows must split over waves");
+    static_assert(!GATEUP || FN % 2 == 0, "gate/up fragments come in pairs");
+    static_assert(NS == 2 || NS == 3, "two or three LDS stages");
+    constexpr int kCols = tile_cols<BNT, GATEUP>();
+    const int n_tiles = (a.N_out + kCols - 1) / kCols;
+    const int chunk = gridDim.x / kXcds;
+    const int t = (blockIdx.x % kXcds) * chunk + blockIdx.x / kXcds;
+    const int per_group = a.n_blocks * kGroupN;
+    const int ng = t / per_group, rem = t % per_group;
+    const int b = rem / kGroupN, tile = ng * kGroupN + rem % kGroupN;
+    if (tile >= n_tiles) return;
+    const int e = a.blk_e_b[b];
+    if (e < 0) return;
+    const int lane = threadIdx.x & 63, wave = wave_id();
+    const int wm = wave / WN, wn = wave % WN;
+    const int kc = lane >> 4, lrow = lane & 15;
+    const int I = GATEUP ? a.N_out : 0;
+    const int Nw = GATEUP ? 2 * a.N_out : a.N_out;
+    const int c0 = tile * kCols;
+    const int K = a.K;
+    const int row0 = b * BM;
+    auto wrow_of = [&](int r) {
+        const int f = r >> 4;
+        int col = c0 + 16 * (GATEUP ? (f >> 1) : f) + (r & 15);
+        col = min(col, a.N_out - 1);
+        return (GATEUP && (f & 1)) ? I + col : col;
+    };
+
+    __shared__ __attribute__((aligned(1024))) uint16_t As0[BM * 64], As1[BM * 64], As2[NS > 2 ? BM * 64 : 8];
+    __shared__ __attribute__((aligned(1024))) uint16_t Bs0[BNT * 64], Bs1[BNT * 64], Bs2[NS > 2 ? BNT * 64 : 8];
+
+    // lane l of a 1 KiB block fills row 8*blk + l/8, physical chunk l%8, which
+    // holds logical chunk (l%8) ^ (row & 7) under the swizzle used by swz()
+    const int lr = lane >> 3, pc = lane & 7;
+    const uint16_t* asrc[A_PW];
+    const int p_first = a.sorted_b[row0];
+#pragma unroll
+    for (int i = 0; i < A_PW; ++i) {
+        const int r = 8 * (wave * A_PW + i) + lr;
+        const int c = pc ^ (r & 7);
+        size_t xr;
+        if (GATEUP) {
+            const int p = a.sorted_b[row0 + r];
+            xr = static_cast<size_t>((p < a.P ? p : p_first) / a.top_k);
+        } else {
+            xr = static_cast<size_t>(row0 + r);
+        }
+        asrc[i] = a.X + xr * K + c * 8;
+    }
+    const uint16_t* bsrc[B_PW];
+#pragma unroll
+    for (int i = 0; i < B_PW; ++i) {
+        const int r = 8 * (wave * B_PW + i) + lr;
+        const int c = pc ^ (r & 7);
+        bsrc[i] = a.W + (static_cast<size_t>(e) * Nw + wrow_of(r)) * K + c * 8;
+    }
+
+    const int wrow_base = row0 + wm * (BM / WM);
+    const bool wlive = a.sorted_b[wrow_base] < a.P;
+
+    f32x4 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int nk = K / 64;
+    DmaCtx<FM, FN, A_PW, B_PW> ctx{asrc, bsrc, wave, wm * (BM / WM), wn * (BNT / WN), kc, lrow, wlive};
+    uint16_t* const abufs[3] = {As0, As1, As2};
+    uint16_t* const bbufs[3] = {Bs0, Bs1, Bs2};
+#pragma unroll
+    for (int s = 0; s < NS - 1; ++s)
+        if (s < nk) dma_issue<A_PW, B_PW>(ctx.asrc, ctx.bsrc, abufs[s], bbufs[s], wave, s * 64);
+    // one pipeline step: stage k (buffer k % NS) is complete for this wave once
+    // at most the loads of the stage requested after it are in flight; the
+    // barrier then makes every wave's part visible and frees the buffer that
+    // the next request overwrites (it was multiplied one step earlier)
+    for (int k = 0; k < nk; k += NS) {
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            if (k + s >= nk) break;
+            if (k + s + 1 < nk)
+                wait_vmcnt<(NS - 2) * LPS>();
+            else
+                wait_vmcnt<0>();
+            bare_barrier();
+            dma_step(ctx, acc, abufs[s], bbufs[s], abufs[(s + NS - 1) % NS], bbufs[(s + NS - 1) % NS],
+                     k + s + NS - 1 < nk ? (k + s + NS - 1) * 64 : -1);
+        }
+    }
+
+    tile_epilogue<FM, FN, GATEUP>(a, acc, wlive, wrow_base, wn, c0, e, kc, lrow, wrow_of);
+}
+
+// ---------------------------------------------------------------------------
+// Tile shapes of the LDS kernel, by block height. Large blocks (many rows per
+// expert) take 256-wide tiles: per unit of work they move the least data from
+// L2 and LDS. The column count may leave a partial last tile.
+#ifndef MOELORA_DMA_CFG
+#define MOELORA_DMA_CFG 3
+#endif
+#ifndef MOELORA_BIG_WM
+#define MOELORA_BIG_WM 2
+#endif
+#ifndef MOELORA_BIG_BNT
+#define MOELORA_BIG_BNT 256
+#endif
+
+template <int BM, int BNT, int WM, int WN, int NS>
+static hipError_t launch_dma(const GemmArgs& a, hipStream_t s) {
+    const int cols = a.gate_up ? BNT / 2 : BNT;
+    const int n_tiles = (a.N_out + cols - 1) / cols;
+    const dim3 grid(tiled_grid(a.n_blocks, n_tiles)), block(64 * WM * WN);
+    if (a.gate_up)
+        hipLaunchKernelGGL((k_gemm_dma<BM, BNT, WM, WN, NS, true>), grid, block, 0, s, a);
+    else
+        hipLaunchKernelGGL((k_gemm_dma<BM, BNT, WM, WN, NS, false>), grid, block, 0, s, a);
+    return hipGetLastError();
+}
+
+template <int BM, int BNT, int WM, int WN>
+static hipError_t launch_tiled(const GemmArgs& a, hipStream_t s) {
+    const int cols = a.gate_up ? BNT / 2 : BNT;
+    const int n_tiles = (a.N_out + cols - 1) / cols;
+    const dim3 grid(tiled_grid(a.n_blocks, n_tiles)), block(64 * WM * WN);
+    if (a.gate_up)
+        hipLaunchKernelGGL((k_gemm_tiled<BM, BNT, WM, WN, true>), grid, block, 0, s, a);
+    else
+        hipLaunchKernelGGL((k_gemm_tiled<BM, BNT, WM, WN, false>), grid, block, 0, s, a);
+    return hipGetLastError();
+}
+
+bool gemm_supported(int N_out, int K, int gate_up, int bm_b) {
+    if (K % 64 != 0 || N_out % 32 != 0) return false;
+    if (bm_b == 16) return N_out % (gate_up ? 32 : 64) == 0;
+    return bm_b == 32 || bm_b == 64 || bm_b == 128 || bm_b == 256;
 }
 
 #ifndef MOELORA_SKINNY_FN
@@ -401,39 +688,6 @@ static int pick_bnt(int N_out, int gate_up, int bm) {
 static int skinny_fn(int N_out, int gate_up) {
     const int cols8 = gate_up ? 64 : 128;
     return (MOELORA_SKINNY_FN == 8 && N_out % cols8 == 0) ? 8 : 4;
-}
-
-bool gemm_supported(int N_out, int K, int gate_up, int bm_b) {
-    if (K % 64 != 0 || N_out % 32 != 0) return false;
-    if (bm_b == 16) return N_out % (gate_up ? 32 : 64) == 0;
-    if (bm_b == 32 || bm_b == 64 || bm_b == 128 || bm_b == 256) return pick_bnt(N_out, gate_up, bm_b) != 0;
-    return false;
-}
-
-template <int BM, int BNT>
-static void launch_tiled(const GemmArgs& a, hipStream_t s) {
-    const int cols = a.gate_up ? BNT / 2 : BNT;
-    const dim3 grid(a.n_blocks, a.N_out / cols), block(256);
-    if (a.gate_up)
-        hipLaunchKernelGGL((k_gemm_tiled<BM, BNT, true>), grid, block, 0, s, a);
-    else
-        hipLaunchKernelGGL((k_gemm_tiled<BM, BNT, false>), grid, block, 0, s, a);
-}
-
-template <int BM>
-static hipError_t launch_tiled_bm(const GemmArgs& a, hipStream_t s, int bnt) {
-    switch (bnt) {
-        case 64: launch_tiled<BM, 64>(a, s); break;
-        case 128: launch_tiled<BM, 128>(a, s); break;
-        case 192:
-            if constexpr (BM <= 128) {
-                launch_tiled<BM, 192>(a, s);
-                break;
-            }
-            return hipErrorInvalidValue;
-        default: return hipErrorInvalidValue;
-    }
-    return hipGetLastError();
 }
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
@@ -453,12 +707,22 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
         }
         return hipGetLastError();
     }
-    const int bnt = pick_bnt(a.N_out, a.gate_up, a.bm_b);
     switch (a.bm_b) {
-        case 32: return launch_tiled_bm<32>(a, s, bnt);
-        case 64: return launch_tiled_bm<64>(a, s, bnt);
-        case 128: return launch_tiled_bm<128>(a, s, bnt);
-        case 256: return launch_tiled_bm<256>(a, s, bnt);
+        case 32: return launch_tiled<32, 128, 1, 4>(a, s);
+        case 64: return launch_tiled<64, 128, 2, 2>(a, s);
+#if MOELORA_DMA_CFG == 1
+        case 128: return launch_dma<128, 192, 2, 2, 3>(a, s);
+        case 256: return launch_dma<256, 256, 2, 2, 2>(a, s);
+#elif MOELORA_DMA_CFG == 2
+        case 128: return launch_dma<128, 256, 2, 2, 3>(a, s);
+        case 256: return launch_dma<256, 128, 4, 2, 3>(a, s);
+#elif MOELORA_DMA_CFG == 3
+        case 128: return launch_dma<128, 192, 2, 2, 2>(a, s);
+        case 256: return launch_dma<256, 192, 2, 2, 2>(a, s);
+#else
+        case 128: return launch_tiled<128, 192, 2, 2>(a, s);
+        case 256: return launch_tiled<256, MOELORA_BIG_BNT, MOELORA_BIG_WM, 2>(a, s);
+#endif
         default: return hipErrorInvalidValue;
     }
 }

@@ -110,7 +110,7 @@ int moe_lora_route(const moe_lora_desc *d, const float *logits, int32_t *topk_id
  *   n_b      i32 [1]          used length of sorted_b
  *   sorted_l i32 [C_l], blk_e_l, blk_a_l i32 [C_l/BMl], n_l i32 [1]: LoRA view
  * The result is deterministic (no order-dependent atomics).
- * Limit: E*(L+1) <= 16384 and T*top_k <= 2^24. */
+ * Limit: E*(L+1) <= 9712 and T*top_k <= 2^24. */
 int moe_lora_align(const moe_lora_desc *d, const int32_t *topk_ids, const int32_t *adapter_ids,
                    int32_t *sorted_b, int32_t *blk_e_b, int32_t *n_b,
                    int32_t *sorted_l, int32_t *blk_e_l, int32_t *blk_a_l, int32_t *n_l,
@@ -141,6 +141,13 @@ int moe_lora_forward(const moe_lora_desc *d, const moe_lora_weights *w, const vo
 int moe_lora_read_stages(const moe_lora_desc *d, const void *workspace, size_t ws_bytes,
                          int32_t *topk_ids, float *topk_w, float *s1, uint16_t *h,
                          float *s2, float *dn, void *stream);
+
+/* Copy the alignment of the last moe_lora_forward on `workspace` out (same
+ * arrays and layout as moe_lora_align produces); any output may be NULL. */
+int moe_lora_read_alignment(const moe_lora_desc *d, const void *workspace, size_t ws_bytes,
+                            int32_t *sorted_b, int32_t *blk_e_b, int32_t *n_b,
+                            int32_t *sorted_l, int32_t *blk_e_l, int32_t *blk_a_l, int32_t *n_l,
+                            void *stream);
 
 /* Per-kernel timing of moe_lora_forward, for profiling only (process-global,
  * not thread-safe). moe_lora_timing_enable(n) makes the next n forward calls

@@ -22,7 +22,7 @@ struct Plan {
     int T, H, I, E, k, L, r, P;
     int bm_b, bm_l, C_b, C_l, nblk_b, nblk_l;
     size_t off_ids, off_w, off_sorted_b, off_blk_e_b, off_counts, off_sorted_l, off_blk_e_l,
-        off_blk_a_l, off_slot, off_lslot, off_sad, off_s1, off_s2, off_h, off_d, total;
+        off_blk_a_l, off_slot, off_lslot, off_sad, off_defer, off_s1, off_s2, off_h, off_d, total;
 };
 
 int roundup_i(long v, long m) { return static_cast<int>((v + m - 1) / m * m); }
@@ -53,7 +53,7 @@ int check_desc(const moe_lora_desc* d) {
     if (d->block_m_lora != 0 && !pow2_in(d->block_m_lora, 16, 256)) return MOE_LORA_EINVAL;
     const long P = static_cast<long>(d->T) * d->top_k;
     if (P > (1L << 24)) return MOE_LORA_EINVAL;
-    if (static_cast<long>(d->E) * (d->L + 1) > 16384) return MOE_LORA_EINVAL;
+    if (static_cast<long>(d->E) * (d->L + 1) > 9712) return MOE_LORA_EINVAL;
     if (align_hist_waves(d->E, d->L) <= 0) return MOE_LORA_EINVAL;
     return MOE_LORA_OK;
 }
@@ -86,6 +86,7 @@ int make_plan(const moe_lora_desc* d, Plan* p) {
     p->off_slot = take(4 * P);
     p->off_lslot = take(4 * P);
     p->off_sad = take(4ul * p->C_b);
+    p->off_defer = take(4ul * align_defer_ints(p->E, p->L));
     const size_t sbytes = p->L > 0 ? 4ul * p->C_b * p->r : 0;
     p->off_s1 = take(sbytes);
     p->off_s2 = take(sbytes);
@@ -199,7 +200,7 @@ int moe_lora_align(const moe_lora_desc* d, const int32_t* topk_ids, const int32_
         return MOE_LORA_EINVAL;
     return launch_align(topk_ids, adapter_ids, p.T, p.k, p.E, p.L, p.bm_b, p.bm_l, p.C_b, p.C_l,
                         sorted_b, blk_e_b, n_b, sorted_l, blk_e_l, blk_a_l, n_l, nullptr,
-                        nullptr, nullptr, nullptr, 0, static_cast<hipStream_t>(stream)) == hipSuccess
+                        nullptr, nullptr, nullptr, 0, nullptr, static_cast<hipStream_t>(stream)) == hipSuccess
                ? MOE_LORA_OK
                : MOE_LORA_EHIP;
 }
@@ -244,7 +245,7 @@ int moe_lora_forward(const moe_lora_desc* d, const moe_lora_weights* w, const vo
     timing_mark(call, 1, s);
     ok(launch_align(ids, adapter_ids, p.T, p.k, p.E, p.L, p.bm_b, p.bm_l, p.C_b, p.C_l, sorted_b,
                     blk_e_b, counts, sorted_l, blk_e_l, blk_a_l, counts + 1, slot, lslot, sad,
-                    nullptr, 0, s));
+                    nullptr, 0, at<int32_t>(workspace, p.off_defer), s));
     timing_mark(call, 2, s);
 
     ShrinkArgs sa{};
@@ -309,6 +310,32 @@ int moe_lora_read_stages(const moe_lora_desc* d, const void* workspace, size_t w
     if (s2) ok(launch_gather_rows_f32(at<float>(ws, p.off_s2), 1, p.C_b, p.r, slot, lslot, p.P, s2, s));
     if (h) ok(launch_gather_rows_bf16(at<uint16_t>(ws, p.off_h), p.I, slot, p.P, h, s));
     if (dn) ok(launch_gather_rows_f32(at<float>(ws, p.off_d), 1, p.C_b, p.H, slot, nullptr, p.P, dn, s));
+    return e == hipSuccess ? MOE_LORA_OK : MOE_LORA_EHIP;
+}
+
+int moe_lora_read_alignment(const moe_lora_desc* d, const void* workspace, size_t ws_bytes,
+                            int32_t* sorted_b, int32_t* blk_e_b, int32_t* n_b, int32_t* sorted_l,
+                            int32_t* blk_e_l, int32_t* blk_a_l, int32_t* n_l, void* stream) {
+    Plan p;
+    const int rc = make_plan(d, &p);
+    if (rc) return rc;
+    if (p.T == 0) return MOE_LORA_OK;
+    if (!workspace) return MOE_LORA_EINVAL;
+    if (ws_bytes < p.total) return MOE_LORA_EWORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    void* ws = const_cast<void*>(workspace);
+    hipError_t e = hipSuccess;
+    auto cp = [&](int32_t* dst, size_t off, size_t n) {
+        if (dst && e == hipSuccess)
+            e = hipMemcpyAsync(dst, at<int32_t>(ws, off), 4 * n, hipMemcpyDeviceToDevice, s);
+    };
+    cp(sorted_b, p.off_sorted_b, p.C_b);
+    cp(blk_e_b, p.off_blk_e_b, p.nblk_b);
+    cp(n_b, p.off_counts, 1);
+    cp(sorted_l, p.off_sorted_l, p.C_l);
+    cp(blk_e_l, p.off_blk_e_l, p.nblk_l);
+    cp(blk_a_l, p.off_blk_a_l, p.nblk_l);
+    cp(n_l, p.off_counts + 4, 1);
     return e == hipSuccess ? MOE_LORA_OK : MOE_LORA_EHIP;
 }
 

@@ -18,11 +18,24 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ D,
     const int n = (blockIdx.y * 256 + threadIdx.x) * 4;
     if (n >= H) return;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < k; ++j) {
-        const int slot = slot_of_pair[t * k + j];
-        const float wj = w[t * k + j];
-        const f32x4 d = *reinterpret_cast<const f32x4*>(D + static_cast<size_t>(slot) * H + n);
-        acc += wj * d;
+    // up to 8 choices per round: all slot/weight loads, then all row loads,
+    // then the sums in j order (no load waits on the previous choice's add)
+    for (int j0 = 0; j0 < k; j0 += 8) {
+        int slot[8];
+        float wj[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int j = min(j0 + u, k - 1);
+            slot[u] = slot_of_pair[t * k + j];
+            wj[u] = w[t * k + j];
+        }
+        f32x4 d[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            d[u] = *reinterpret_cast<const f32x4*>(D + static_cast<size_t>(slot[u]) * H + n);
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (j0 + u < k) acc += wj[u] * d[u];
     }
     *reinterpret_cast<f32x4*>(out + static_cast<size_t>(t) * H + n) = acc;
 }

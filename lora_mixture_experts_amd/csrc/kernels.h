@@ -19,7 +19,9 @@ hipError_t launch_align(const int32_t* topk_ids, const int32_t* adapter_ids, int
                         int32_t* sorted_b, int32_t* blk_e_b, int32_t* n_b,
                         int32_t* sorted_l, int32_t* blk_e_l, int32_t* blk_a_l, int32_t* n_l,
                         int32_t* slot_of_pair, int32_t* lslot_of_pair, int32_t* slot_adapter,
-                        int32_t* zero_buf, int zero_n, hipStream_t s);
+                        int32_t* zero_buf, int zero_n, int32_t* defer, hipStream_t s);
+// ints of scratch the alignment may use to split its scatter off (0 = none)
+int align_defer_ints(int E, int L);
 
 // ---- LoRA shrink ----------------------------------------------------------
 // S[slot][j] = X[row] . A[a][e][j] for the real rows of each LoRA-view block.

@@ -29,17 +29,20 @@ __global__ __launch_bounds__(kShrinkThreads) void k_shrink(ShrinkArgs a) {
     const int nfm = a.bm_l / 16;               // 16-row fragments in the block (1..16)
     const int nkp = kShrinkWaves / nfm;        // K parts per fragment
     const int fm = wave / nkp, kp = wave % nkp;
-    const int nsteps = a.K / 32;
-    const int s0 = kp * nsteps / nkp, s1 = (kp + 1) * nsteps / nkp;
+    // K in chunks of 64; this wave owns chunks [q0, q1)
+    const int nq = a.K / 64;
+    const int q0 = kp * nq / nkp, q1 = (kp + 1) * nq / nkp;
 
     // A operand row (block row fm*16 + lrow); padding rows re-read the
     // block's first (real) row, merging into the same memory requests, and
-    // their outputs are never stored
+    // their outputs are never stored. Lane (lrow, kc) reads 32 contiguous
+    // bytes (elements 16 kc .. 16 kc + 15) of each 64-wide chunk, so a pair of
+    // wave-wide loads consumes whole 128-byte lines.
     int p = a.sorted_l[b * a.bm_l + fm * 16 + lrow];
     if (p >= a.P) p = a.sorted_l[b * a.bm_l];
     const size_t row = a.gather_token ? static_cast<size_t>(p / a.top_k)
                                       : static_cast<size_t>(a.slot_of_pair[p]);
-    const uint16_t* xrow = a.X + row * a.K + kc * 8;
+    const uint16_t* xrow = a.X + row * a.K + kc * 16;
     // B operand rows (LoRA A rows j = fn*16 + lrow); columns j >= r (r = 8)
     // re-read row j - 8 and are never stored, so loads stay unconditional
     const uint16_t* Abase = a.A + (static_cast<size_t>(ad) * a.E + e) * a.r * a.K;
@@ -47,36 +50,46 @@ __global__ __launch_bounds__(kShrinkThreads) void k_shrink(ShrinkArgs a) {
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn) {
         const int j = fn * 16 + lrow;
-        brow[fn] = Abase + static_cast<size_t>(j < a.r ? j : j - 8) * a.K + kc * 8;
+        brow[fn] = Abase + static_cast<size_t>(j < a.r ? j : j - 8) * a.K + kc * 16;
     }
 
     f32x4 acc[FN];
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn) acc[fn] = f32x4{0.f, 0.f, 0.f, 0.f};
+    u32x4 xb[2][2], wb[2][FN][2];
+    auto load = [&](int buf, int q) {
+        const int k0 = q * 64;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) xb[buf][h] = ld16(xrow + k0 + 8 * h);
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) wb[buf][fn][h] = ld16(brow[fn] + k0 + 8 * h);
+    };
+    auto compute = [&](int buf) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) acc[fn] = mfma16x16x32(xb[buf][h], wb[buf][fn][h], acc[fn]);
+    };
     // skip fragments made only of padding (the decision is uniform per wave)
     const bool live = a.sorted_l[b * a.bm_l + fm * 16] < a.P;
-    if (live) {
-        int s = s0;
-        for (; s + 3 < s1; s += 4) {  // four steps per round, loads first
-            u32x4 xa[4], wb[4][FN];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int k0 = (s + u) * 32;
-                xa[u] = ld16(xrow + k0);
-#pragma unroll
-                for (int fn = 0; fn < FN; ++fn) wb[u][fn] = ld16(brow[fn] + k0);
-            }
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-#pragma unroll
-                for (int fn = 0; fn < FN; ++fn) acc[fn] = mfma16x16x32(xa[u], wb[u][fn], acc[fn]);
+    const int n = q1 - q0;
+    if (live && n > 0) {
+        // two-stage register pipeline (as in the skinny projection kernel)
+        load(0, q0);
+        int q = q0;
+        for (int i = 0; i + 1 < n; i += 2, q += 2) {
+            load(1, q + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(0);
+            __builtin_amdgcn_sched_barrier(0);
+            load(0, min(q + 2, q1 - 1));
+            __builtin_amdgcn_sched_barrier(0);
+            compute(1);
+            __builtin_amdgcn_sched_barrier(0);
         }
-        for (; s < s1; ++s) {
-            const int k0 = s * 32;
-            const u32x4 xa = ld16(xrow + k0);
-#pragma unroll
-            for (int fn = 0; fn < FN; ++fn) acc[fn] = mfma16x16x32(xa, ld16(brow[fn] + k0), acc[fn]);
-        }
+        if (n & 1) compute(0);
     }
 
     // add the K parts of each fragment in order 0..nkp-1 and store

@@ -8,6 +8,7 @@
 // "additional grid dimension corresponding to the LoRA index" and the compound
 // sparsity of several adapters on top of expert routing (same post, section
 // "Tuning kernel configurations for Amazon SageMaker AI and Amazon Bedrock").
+#include <algorithm>
 #include <climits>
 
 #include "common.h"
@@ -86,28 +87,48 @@ hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* ids, 
 }
 
 // ---------------------------------------------------------------------------
-// Align: one 1024-thread workgroup.
-//   key(p) = e * (L+1) + a',  a' = adapter if in [0,L) else L.
-// Wave w < nw owns the contiguous pair range [w*R, (w+1)*R). Lanes with equal
-// keys inside a 64-pair step are found with one ballot per key bit, so ranks
-// inside a step come from popcounts; per-wave, per-key histograms in LDS give
-// each wave its exclusive offset. The result is a stable counting sort whose
-// output does not depend on scheduling.
+// Align. key(p) = e * (L+1) + a',  a' = adapter if in [0,L) else L.
+// The P pairs are cut into nr contiguous ranges of R pairs (R a multiple of
+// 64). One 1024-thread workgroup counts every range's keys into its own LDS
+// histogram row (order-free LDS atomics), turns the rows into exclusive
+// per-range offsets and the key totals into segment starts, and writes the
+// padding, the tails and the block maps. The stable scatter then walks each
+// range in 64-pair steps: lanes with equal keys in a step are found with one
+// ballot per key bit, so ranks inside a step come from popcounts, and the
+// range's running per-key offsets come from its LDS row. Small batches scatter
+// in the same workgroup (wave w takes ranges w, w+16, ...); large ones hand
+// the offsets to k_align_scatter, one workgroup per range, so the scattered
+// stores are spread over many CUs. Nothing depends on scheduling order.
 constexpr int kAlignThreads = 1024;
 constexpr int kAlignLdsInts = 38912;  // 152 KiB of the 160 KiB LDS
+constexpr int kAlignStepsPerRange = 4;
 
 static int align_fixed_ints(int E, int L) {
     const int nkeys = E * (L + 1);
     return 2 * nkeys + E * L + E + 64;
 }
 
-int align_hist_waves(int E, int L) {
+// most ranges whose histograms fit the align kernel's LDS (0 = none fits)
+static int align_max_ranges(int E, int L) {
     const long nkeys = static_cast<long>(E) * (L + 1);
     const long avail = kAlignLdsInts - static_cast<long>(align_fixed_ints(E, L));
     if (nkeys <= 0 || avail < nkeys) return 0;
-    const long nw = avail / nkeys;
-    return static_cast<int>(nw > 16 ? 16 : nw);
+    return static_cast<int>(std::min<long>(avail / nkeys, 4096));
 }
+
+// range count and range length for P pairs
+static void align_ranges(int P, int E, int L, int* nr, int* R) {
+    const int maxr = align_max_ranges(E, L);
+    const int per = 64 * kAlignStepsPerRange;
+    int n = std::max(1, (P + per - 1) / per);
+    n = std::min(n, std::max(maxr, 1));
+    int r = (P + n - 1) / n;
+    r = std::max(64, (r + 63) / 64 * 64);
+    *nr = std::max(1, (P + r - 1) / r);
+    *R = r;
+}
+
+int align_hist_waves(int E, int L) { return align_max_ranges(E, L) > 0 ? 1 : 0; }
 
 __device__ __forceinline__ uint64_t match_key(int key, bool valid, int nbits) {
     uint64_t m = ballot64(valid);
@@ -155,21 +176,85 @@ __device__ int block_excl_scan(int* a, int n, int* red) {
     return total;
 }
 
-__device__ __forceinline__ int roundup_i(int v, int m) { return (v + m - 1) / m * m; }
+struct AlignKeys {
+    const int32_t* topk_ids;
+    const int32_t* adapter_ids;
+    int k, E, L;
+    __device__ __forceinline__ int operator()(int p) const {
+        const int e = min(max(topk_ids[p], 0), E - 1);  // memory safety for foreign ids
+        int a = adapter_ids[p / k];
+        if (a < 0 || a >= L) a = L;
+        return e * (L + 1) + a;
+    }
+};
+
+struct AlignOut {
+    int32_t* sorted_b;
+    int32_t* sorted_l;
+    int32_t* slot_of_pair;   // may be null
+    int32_t* lslot_of_pair;  // may be null
+    int32_t* slot_adapter;   // may be null
+};
+
+// Stable scatter of pairs [lo, hi) by one wave; h = the range's running
+// per-key offsets (LDS), bpos / lpos = segment starts.
+__device__ __forceinline__ void scatter_range(const AlignKeys& keyf, const AlignOut& o, int lo, int hi,
+                                              int* h, const int* bpos, const int* lpos, int L,
+                                              int nbits) {
+    const int lane = lane_id();
+    const int L1 = L + 1;
+    const uint64_t below = lanemask_lt();
+    int keys[kAlignStepsPerRange];
+#pragma unroll
+    for (int c = 0; c < kAlignStepsPerRange; ++c) {
+        // clamped, unconditional loads, all in flight together
+        const int p = lo + 64 * c + lane;
+        const int key = keyf(min(p, hi - 1));
+        keys[c] = p < hi ? key : -1;
+    }
+    for (int base = lo, c = 0; base < hi; base += 64, ++c) {
+        const int p = base + lane;
+        int key = -1;
+        if (c < kAlignStepsPerRange) {
+#pragma unroll
+            for (int u = 0; u < kAlignStepsPerRange; ++u)
+                if (u == c) key = keys[u];
+        } else {
+            key = p < hi ? keyf(p) : -1;  // ranges longer than the prefetch
+        }
+        const bool valid = key >= 0;
+        if (!valid) key = 0;
+        const uint64_t m = match_key(key, valid, nbits);
+        const int off = valid ? h[key] : 0;
+        if (valid && lane == __ffsll(static_cast<long long>(m)) - 1) h[key] = off + popc64(m);
+        if (valid) {
+            const int pos = off + popc64(m & below);
+            const int slot = bpos[key] + pos;
+            o.sorted_b[slot] = p;
+            if (o.slot_of_pair) o.slot_of_pair[p] = slot;
+            const int ap = key % L1;
+            int lslot = -1;
+            if (ap < L) {
+                lslot = lpos[(key / L1) * L + ap] + pos;
+                o.sorted_l[lslot] = p;
+            }
+            if (o.lslot_of_pair) o.lslot_of_pair[p] = lslot;
+            if (o.slot_adapter) o.slot_adapter[slot] = ap < L ? ap : -1;
+        }
+    }
+}
 
 __global__ __launch_bounds__(kAlignThreads) void k_align(
-    const int32_t* __restrict__ topk_ids, const int32_t* __restrict__ adapter_ids, int T, int k,
-    int E, int L, int bm_b, int bm_l, int C_b, int C_l, int nw, int R,
-    int32_t* __restrict__ sorted_b, int32_t* __restrict__ blk_e_b, int32_t* __restrict__ n_b_out,
-    int32_t* __restrict__ sorted_l, int32_t* __restrict__ blk_e_l, int32_t* __restrict__ blk_a_l,
-    int32_t* __restrict__ n_l_out, int32_t* __restrict__ slot_of_pair,
-    int32_t* __restrict__ lslot_of_pair, int32_t* __restrict__ slot_adapter,
-    int32_t* __restrict__ zero_buf, int zero_n) {
+    AlignKeys keyf, AlignOut o, int T, int bm_b_log2, int bm_l_log2, int C_b, int C_l, int nr,
+    int R, int32_t* __restrict__ blk_e_b, int32_t* __restrict__ n_b_out,
+    int32_t* __restrict__ blk_e_l, int32_t* __restrict__ blk_a_l, int32_t* __restrict__ n_l_out,
+    int32_t* __restrict__ zero_buf, int zero_n, int32_t* __restrict__ defer) {
     __shared__ int lds[kAlignLdsInts];
-    const int L1 = L + 1;
-    const int nkeys = E * L1, nseg = E * L, P = T * k;
-    int* hist = lds;                 // [nw][nkeys]
-    int* cnt = hist + nw * nkeys;    // [nkeys]
+    const int E = keyf.E, L = keyf.L, L1 = L + 1;
+    const int nkeys = E * L1, nseg = E * L, P = T * keyf.k;
+    const int bm_b = 1 << bm_b_log2, bm_l = 1 << bm_l_log2;
+    int* hist = lds;                 // [nr][nkeys]
+    int* cnt = hist + nr * nkeys;    // [nkeys]
     int* bpos = cnt + nkeys;         // [nkeys]  base-view start of each key
     int* lpos = bpos + nkeys;        // [nseg]   LoRA-view start of each segment
     int* ne = lpos + nseg;           // [E]      pairs per expert
@@ -177,38 +262,24 @@ __global__ __launch_bounds__(kAlignThreads) void k_align(
     const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
     const int nbits = nkeys > 1 ? 32 - __clz(nkeys - 1) : 0;
 
-    auto pair_key = [&](int p) {
-        const int e = min(max(topk_ids[p], 0), E - 1);  // memory safety for foreign ids
-        int a = adapter_ids[p / k];
-        if (a < 0 || a >= L) a = L;
-        return e * L1 + a;
-    };
-
-    for (int i = tid; i < nw * nkeys; i += kAlignThreads) hist[i] = 0;
+    for (int i = tid; i < nr * nkeys; i += kAlignThreads) hist[i] = 0;
     for (int i = tid; i < E; i += kAlignThreads) ne[i] = 0;
     for (int i = tid; i < zero_n; i += kAlignThreads) zero_buf[i] = 0;
     __syncthreads();
 
-    // 1. per-wave key histograms
-    if (wave < nw) {
-        const int lo = wave * R, hi = min(P, lo + R);
-        int* h = hist + wave * nkeys;
-        for (int base = lo; base < hi; base += 64) {
-            const int p = base + lane;
-            const bool valid = p < hi;
-            const int key = valid ? pair_key(p) : 0;
-            const uint64_t m = match_key(key, valid, nbits);
-            if (valid && lane == __ffsll(static_cast<long long>(m)) - 1) h[key] += popc64(m);
-        }
+    // 1. per-range key counts (the order of the LDS atomics does not matter)
+    for (int base = tid; base < P; base += kAlignThreads) {
+        const int r = base / R;
+        atomicAdd(&hist[r * nkeys + keyf(base)], 1);
     }
     __syncthreads();
 
-    // 2. column scan over waves -> exclusive per-wave offsets, totals per key
+    // 2. column scan over ranges -> exclusive per-range offsets, totals per key
     for (int key = tid; key < nkeys; key += kAlignThreads) {
         int run = 0;
-        for (int w = 0; w < nw; ++w) {
-            const int c = hist[w * nkeys + key];
-            hist[w * nkeys + key] = run;
+        for (int r = 0; r < nr; ++r) {
+            const int c = hist[r * nkeys + key];
+            hist[r * nkeys + key] = run;
             run += c;
         }
         cnt[key] = run;
@@ -218,36 +289,37 @@ __global__ __launch_bounds__(kAlignThreads) void k_align(
     for (int key = tid; key < nkeys; key += kAlignThreads) {
         const int e = key / L1;
         int v = cnt[key];
-        if (key % L1 == L) v += roundup_i(ne[e], bm_b) - ne[e];  // expert's padding
+        if (key % L1 == L) v += ((ne[e] + bm_b - 1) & ~(bm_b - 1)) - ne[e];  // expert's padding
         bpos[key] = v;
     }
     for (int s = tid; s < nseg; s += kAlignThreads)
-        lpos[s] = roundup_i(cnt[(s / L) * L1 + s % L], bm_l);
+        lpos[s] = (cnt[(s / L) * L1 + s % L] + bm_l - 1) & ~(bm_l - 1);
     __syncthreads();
     const int n_b = block_excl_scan(bpos, nkeys, red);
     const int n_l = block_excl_scan(lpos, nseg, red);
 
     // 3. sentinels, tails and block maps
-    for (int idx = tid; idx < E * bm_b; idx += kAlignThreads) {
-        const int e = idx / bm_b, i = idx % bm_b;
+    for (int idx = tid; idx < (E << bm_b_log2); idx += kAlignThreads) {
+        const int e = idx >> bm_b_log2, i = idx & (bm_b - 1);
         const int last = e * L1 + L;
-        if (i < roundup_i(ne[e], bm_b) - ne[e]) {
-            sorted_b[bpos[last] + cnt[last] + i] = P;
-            if (slot_adapter) slot_adapter[bpos[last] + cnt[last] + i] = -1;
+        if (i < ((ne[e] + bm_b - 1) & ~(bm_b - 1)) - ne[e]) {
+            const int slot = bpos[last] + cnt[last] + i;
+            o.sorted_b[slot] = P;
+            if (o.slot_adapter) o.slot_adapter[slot] = -1;
         }
     }
     for (int i = n_b + tid; i < C_b; i += kAlignThreads) {
-        sorted_b[i] = P;
-        if (slot_adapter) slot_adapter[i] = -1;
+        o.sorted_b[i] = P;
+        if (o.slot_adapter) o.slot_adapter[i] = -1;
     }
-    for (int idx = tid; idx < nseg * bm_l; idx += kAlignThreads) {
-        const int s = idx / bm_l, i = idx % bm_l;
+    for (int idx = tid; idx < (nseg << bm_l_log2); idx += kAlignThreads) {
+        const int s = idx >> bm_l_log2, i = idx & (bm_l - 1);
         const int c = cnt[(s / L) * L1 + s % L];
-        if (i < roundup_i(c, bm_l) - c) sorted_l[lpos[s] + c + i] = P;
+        if (i < ((c + bm_l - 1) & ~(bm_l - 1)) - c) o.sorted_l[lpos[s] + c + i] = P;
     }
-    for (int i = n_l + tid; i < C_l; i += kAlignThreads) sorted_l[i] = P;
-    for (int b = tid; b < C_b / bm_b; b += kAlignThreads) {
-        const int pos = b * bm_b;
+    for (int i = n_l + tid; i < C_l; i += kAlignThreads) o.sorted_l[i] = P;
+    for (int b = tid; b < (C_b >> bm_b_log2); b += kAlignThreads) {
+        const int pos = b << bm_b_log2;
         int e = -1;
         if (pos < n_b) {
             int lo = 0, hi = E - 1;  // largest e with start(e) <= pos
@@ -259,8 +331,8 @@ __global__ __launch_bounds__(kAlignThreads) void k_align(
         }
         blk_e_b[b] = e;
     }
-    for (int b = tid; b < C_l / bm_l; b += kAlignThreads) {
-        const int pos = b * bm_l;
+    for (int b = tid; b < (C_l >> bm_l_log2); b += kAlignThreads) {
+        const int pos = b << bm_l_log2;
         int e = -1, a = -1;
         if (pos < n_l) {
             int lo = 0, hi = nseg - 1;  // largest segment with start <= pos
@@ -279,34 +351,37 @@ __global__ __launch_bounds__(kAlignThreads) void k_align(
         *n_l_out = n_l;
     }
 
-    // 4. stable scatter
-    if (wave < nw) {
-        const int lo = wave * R, hi = min(P, lo + R);
-        int* h = hist + wave * nkeys;
-        const uint64_t below = lanemask_lt();
-        for (int base = lo; base < hi; base += 64) {
-            const int p = base + lane;
-            const bool valid = p < hi;
-            const int key = valid ? pair_key(p) : 0;
-            const uint64_t m = match_key(key, valid, nbits);
-            const int off = valid ? h[key] : 0;
-            if (valid && lane == __ffsll(static_cast<long long>(m)) - 1) h[key] = off + popc64(m);
-            if (valid) {
-                const int pos = off + popc64(m & below);
-                const int slot = bpos[key] + pos;
-                sorted_b[slot] = p;
-                if (slot_of_pair) slot_of_pair[p] = slot;
-                const int ap = key % L1;
-                int lslot = -1;
-                if (ap < L) {
-                    lslot = lpos[(key / L1) * L + ap] + pos;
-                    sorted_l[lslot] = p;
-                }
-                if (lslot_of_pair) lslot_of_pair[p] = lslot;
-                if (slot_adapter) slot_adapter[slot] = ap < L ? ap : -1;
-            }
-        }
+    // 4. stable scatter, here or in k_align_scatter
+    if (defer) {
+        for (int i = tid; i < nr * nkeys; i += kAlignThreads) defer[i] = hist[i];
+        for (int i = tid; i < nkeys; i += kAlignThreads) defer[nr * nkeys + i] = bpos[i];
+        for (int i = tid; i < nseg; i += kAlignThreads) defer[(nr + 1) * nkeys + i] = lpos[i];
+        return;
     }
+    for (int r = wave; r < nr; r += kAlignThreads / 64)
+        scatter_range(keyf, o, r * R, min(P, (r + 1) * R), hist + r * nkeys, bpos, lpos, L, nbits);
+}
+
+// Step 4 for large batches: workgroup r (one wave) scatters range r with the
+// offsets computed by k_align, kept in LDS.
+__global__ __launch_bounds__(64) void k_align_scatter(AlignKeys keyf, AlignOut o, int T, int nr,
+                                                      int R, const int32_t* __restrict__ defer) {
+    extern __shared__ int h[];  // [nkeys] running offsets, [nkeys] bpos, [E*L] lpos
+    const int E = keyf.E, L = keyf.L, L1 = L + 1, nkeys = E * L1, P = T * keyf.k;
+    const int r = blockIdx.x, lane = threadIdx.x;
+    int* bpos = h + nkeys;
+    int* lpos = bpos + nkeys;
+    for (int i = lane; i < nkeys; i += 64) h[i] = defer[r * nkeys + i];
+    for (int i = lane; i < nkeys + E * L; i += 64) bpos[i] = defer[nr * nkeys + i];
+    __syncthreads();
+    const int nbits = nkeys > 1 ? 32 - __clz(nkeys - 1) : 0;
+    scatter_range(keyf, o, r * R, min(P, (r + 1) * R), h, bpos, lpos, L, nbits);
+}
+
+int align_defer_ints(int E, int L) {
+    const int maxr = align_max_ranges(E, L);
+    const int nkeys = E * (L + 1);
+    return maxr > 0 ? (maxr + 1) * nkeys + E * L : 0;
 }
 
 hipError_t launch_align(const int32_t* topk_ids, const int32_t* adapter_ids, int T, int k,
@@ -314,16 +389,25 @@ hipError_t launch_align(const int32_t* topk_ids, const int32_t* adapter_ids, int
                         int32_t* sorted_b, int32_t* blk_e_b, int32_t* n_b,
                         int32_t* sorted_l, int32_t* blk_e_l, int32_t* blk_a_l, int32_t* n_l,
                         int32_t* slot_of_pair, int32_t* lslot_of_pair, int32_t* slot_adapter,
-                        int32_t* zero_buf, int zero_n, hipStream_t s) {
-    const int nw = align_hist_waves(E, L);
-    if (nw <= 0) return hipErrorInvalidValue;
+                        int32_t* zero_buf, int zero_n, int32_t* defer, hipStream_t s) {
+    if (align_max_ranges(E, L) <= 0) return hipErrorInvalidValue;
+    if ((bm_b & (bm_b - 1)) || (bm_l & (bm_l - 1))) return hipErrorInvalidValue;
     const int P = T * k;
-    const int per = (P + nw - 1) / nw;
-    const int R = ((per + 63) / 64) * 64;
-    hipLaunchKernelGGL(k_align, dim3(1), dim3(kAlignThreads), 0, s, topk_ids, adapter_ids, T, k,
-                       E, L, bm_b, bm_l, C_b, C_l, nw, R > 0 ? R : 64, sorted_b, blk_e_b, n_b,
-                       sorted_l, blk_e_l, blk_a_l, n_l, slot_of_pair, lslot_of_pair, slot_adapter,
-                       zero_buf, zero_n);
+    if (P == 0) return hipSuccess;
+    int nr, R;
+    align_ranges(P, E, L, &nr, &R);
+    const AlignKeys keyf{topk_ids, adapter_ids, k, E, L};
+    const AlignOut o{sorted_b, sorted_l, slot_of_pair, lslot_of_pair, slot_adapter};
+    // one workgroup does everything for small batches; large ones hand the
+    // scattered stores to one workgroup per range
+    const size_t scatter_lds = sizeof(int) * (2 * E * (L + 1) + E * L);
+    if (nr <= kAlignThreads / 64 || scatter_lds > 64 * 1024) defer = nullptr;
+    hipLaunchKernelGGL(k_align, dim3(1), dim3(kAlignThreads), 0, s, keyf, o, T, __builtin_ctz(bm_b),
+                       __builtin_ctz(bm_l), C_b, C_l, nr, R, blk_e_b, n_b, blk_e_l, blk_a_l, n_l,
+                       zero_buf, zero_n, defer);
+    if (defer)
+        hipLaunchKernelGGL(k_align_scatter, dim3(nr), dim3(64), scatter_lds, s, keyf, o, T, nr, R,
+                           defer);
     return hipGetLastError();
 }
 

@@ -56,6 +56,7 @@ def lib():
             "moe_lora_align": ([pD, P, P, P, P, P, P, P, P, P, P], ctypes.c_int),
             "moe_lora_forward": ([pD, pW, P, P, P, P, P, SZ, P], ctypes.c_int),
             "moe_lora_read_stages": ([pD, P, SZ, P, P, P, P, P, P, P], ctypes.c_int),
+            "moe_lora_read_alignment": ([pD, P, SZ, P, P, P, P, P, P, P, P], ctypes.c_int),
             "moe_lora_timing_enable": ([I32], ctypes.c_int),
             "moe_lora_timing_read": ([ctypes.POINTER(ctypes.c_float), pI32], ctypes.c_int),
             "moe_lora_kernel_name": ([I32], ctypes.c_char_p),
@@ -70,7 +71,7 @@ def lib():
 
 EXPORTED = ("moe_lora_strerror", "moe_lora_validate", "moe_lora_block_sizes",
             "moe_lora_workspace_bytes", "moe_lora_align_capacity", "moe_lora_route",
-            "moe_lora_align", "moe_lora_forward", "moe_lora_read_stages",
+            "moe_lora_align", "moe_lora_forward", "moe_lora_read_stages", "moe_lora_read_alignment",
             "moe_lora_timing_enable", "moe_lora_timing_read", "moe_lora_kernel_name")
 
 
@@ -158,6 +159,15 @@ def read_stages(desc, workspace, topk_ids=None, topk_w=None, s1=None, h=None, s2
                                       _ptr(dn), _stream(stream)), "read_stages")
 
 
+def read_alignment(desc, workspace, sorted_b=None, blk_e_b=None, n_b=None, sorted_l=None,
+                   blk_e_l=None, blk_a_l=None, n_l=None, stream=None):
+    _check(lib().moe_lora_read_alignment(ctypes.byref(desc), _ptr(workspace),
+                                         ctypes.c_size_t(workspace.numel() * workspace.element_size()),
+                                         _ptr(sorted_b), _ptr(blk_e_b), _ptr(n_b), _ptr(sorted_l),
+                                         _ptr(blk_e_l), _ptr(blk_a_l), _ptr(n_l), _stream(stream)),
+           "read_alignment")
+
+
 def timing_enable(max_calls: int):
     _check(lib().moe_lora_timing_enable(max_calls), "timing_enable")
 
@@ -208,3 +218,14 @@ class Layer:
                   dn=torch.empty((P, d.H), dtype=torch.float32, device=dev))
         read_stages(d, self.workspace, stream=stream, **st)
         return st
+
+    def alignment(self, stream=None):
+        import torch
+        d, dev = self.desc, self.device
+        C_b, C_l = align_capacity(d)
+        bm_b, bm_l = block_sizes(d)
+        z = lambda n: torch.empty(n, dtype=torch.int32, device=dev)
+        out = dict(sorted_b=z(C_b), blk_e_b=z(C_b // bm_b), n_b=z(1), sorted_l=z(C_l),
+                   blk_e_l=z(C_l // bm_l), blk_a_l=z(C_l // bm_l), n_l=z(1))
+        read_alignment(d, self.workspace, stream=stream, **out)
+        return out

@@ -131,7 +131,10 @@ ALIGN_CASES = [("tiny", {}, (16, 16)), ("decode", {}, (16, 16)), ("decode", {}, 
                ("many", {}, (128, 16)), ("many", {}, (16, 64)),
                ("odd", dict(T=37, H=64, I=64, E=70, top_k=7, L=3, r=8), (16, 16)),
                ("noL", dict(T=300, H=64, I=64, E=5, top_k=2, L=0, r=8), (32, 16)),
-               ("big", dict(T=20000, H=64, I=64, E=64, top_k=8, L=16, r=8), (256, 128))]
+               ("big", dict(T=20000, H=64, I=64, E=64, top_k=8, L=16, r=8), (256, 128)),
+               # key counts near the limit: one histogram range, one wave scatters
+               ("keys", dict(T=300, H=64, I=64, E=256, top_k=8, L=32, r=8), (16, 16)),
+               ("maxkeys", dict(T=4000, H=64, I=64, E=607, top_k=8, L=15, r=8), (32, 16))]
 
 
 @pytest.mark.parametrize("name,dims,bm", ALIGN_CASES)
@@ -166,6 +169,13 @@ def check_layer(case, dev, ntok=64, bm=(0, 0), stages=False):
     log(f"  {case.name} bm={ml.block_sizes(layer.desc)} tokens={len(toks)}: max {mx:.2e} mean {mean:.2e}")
     assert np.all(np.isfinite(got))
     assert mx <= MAX_TOL and mean <= MEAN_TOL, (mx, mean)
+    # the alignment the forward pass used is the oracle's, bit for bit
+    bb, bl = ml.block_sizes(layer.desc)
+    ref_al = oracle.align(ids, case.adapter_ids, case.E, case.L, bb, bl)
+    got_al = {k: v.cpu().numpy() for k, v in layer.alignment().items()}
+    for key in ("sorted_b", "blk_e_b", "sorted_l", "blk_e_l", "blk_a_l"):
+        np.testing.assert_array_equal(got_al[key], ref_al[key], err_msg=key)
+    assert int(got_al["n_b"][0]) == ref_al["n_b"] and int(got_al["n_l"][0]) == ref_al["n_l"]
     if stages:
         gs = {k: v.cpu() for k, v in layer.stages().items()}
         rows = (toks[:, None] * case.top_k + np.arange(case.top_k)[None, :]).reshape(-1)

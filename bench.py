@@ -19,11 +19,14 @@ import os
 import sys
 import time
 
-import numpy as np
-
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
+
+import numpy as np
+
+from lora_mixture_experts_amd.profsum import read_traffic
+
 
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
@@ -152,7 +155,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode", choices=list(WORKLOAD_NAMES))
-    ap.add_argument("--also", default="prefill", help="second workload reported in the same line ('' = none)")
+    ap.add_argument("--also", default="prefill",
+                    help="second workload reported in the same line ('none' = none)")
     ap.add_argument("--rotate", type=int, default=3)
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MiB",
@@ -167,27 +171,33 @@ def main():
     import torch
     dev = torch.device("cuda:0")
     if args.calibrate_copy > 0:
+        # reference dispatches of known size for the HBM byte counters: the
+        # runtime's device-to-device copy, then an elementwise kernel that
+        # streams the same bytes in and out with ordinary vector loads/stores
         n = args.calibrate_copy << 20
-        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
         dst.copy_(src)
+        torch.cuda.synchronize()
+        torch.neg(src, out=dst)
         torch.cuda.synchronize()
         del src, dst
     case, ids, st, ms, kus, b, f, lbytes, lflops = run_workload(args.workload, args.steps, args.warmup,
                                                                args.rotate, dev)
     dom = max(("gemm_gate_up", "gemm_down"), key=lambda n: kus[n])
+    traffic = read_traffic(os.path.join(ROOT, "profiles", f"hbm_traffic_{args.workload}.md"), dom)
     hbm_bound = case.T * case.top_k / max(st["n_experts"], 1) < 312
     if hbm_bound:
         achieved = b[dom] / (kus[dom] * 1e-6) / 1e9
         roof = dict(kernel=dom, bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None,
+                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic,
                     bytes_per_launch=b[dom], us_per_launch=round(kus[dom], 2))
     else:
         achieved = f[dom] / (kus[dom] * 1e-6) / 1e12
         roof = dict(kernel=dom, bound="mfma", achieved=round(achieved, 1), peak=BF16_PEAK_TFLOPS,
-                    unit="TFLOP/s", frac=round(achieved / BF16_PEAK_TFLOPS, 4), traffic=None,
-                    flops_per_launch=f[dom], us_per_launch=round(kus[dom], 2))
+                    unit="TFLOP/s", frac=round(achieved / BF16_PEAK_TFLOPS, 4), traffic=traffic,
+                    flops_per_launch=f[dom], bytes_per_launch=b[dom], us_per_launch=round(kus[dom], 2))
     layer_roof_us = max(lbytes / (HBM_PEAK_GBS * 1e9), lflops / (BF16_PEAK_TFLOPS * 1e12)) * 1e6
     lora_us = kus["shrink_gate_up"] + kus["shrink_down"]
     lora_bytes = b["shrink_gate_up"] + b["shrink_down"]
@@ -208,7 +218,7 @@ def main():
         "routing": st,
         "roofline": roof,
     }
-    if args.also:
+    if args.also and args.also != "none":
         c2, ids2, st2, ms2, kus2, b2, f2, lb2, lf2 = run_workload(args.also, max(5, args.steps // 5),
                                                                    max(2, args.warmup // 2),
                                                                    args.rotate, dev)
@@ -227,7 +237,10 @@ def main():
                              achieved=round(f2[dom2] / (kus2[dom2] * 1e-6) / 1e12, 1),
                              peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
                              frac=round(f2[dom2] / (kus2[dom2] * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4),
-                             traffic=None),
+                             traffic=read_traffic(os.path.join(ROOT, "profiles",
+                                                               f"hbm_traffic_{args.also}.md"), dom2),
+                             flops_per_launch=f2[dom2], bytes_per_launch=b2[dom2],
+                             us_per_launch=round(kus2[dom2], 2)),
         }
     if args.cpu_budget > 0:
         line["cpu_baseline"] = cpu_baseline(case, ids, args.cpu_budget)

@@ -48,7 +48,9 @@ extern "C" {
  *   H and I must be multiples of 64.
  *   block_m_base / block_m_lora: rows per block of the two alignment views;
  *   0 = library default; else a power of two in [16, 256].
- *   flags: reserved, must be 0. */
+ *   flags: 0, or MOE_LORA_FLAG_OUT_BF16 (out is bf16, rounded to nearest even
+ *   from the fp32 sum); any other bit is an error. */
+#define MOE_LORA_FLAG_OUT_BF16 1
 typedef struct moe_lora_desc {
     int32_t T, H, I, E, top_k, L, r;
     int32_t block_m_base, block_m_lora;
@@ -120,7 +122,8 @@ int moe_lora_align(const moe_lora_desc *d, const int32_t *topk_ids, const int32_
  *   x           bf16 [T][H]
  *   logits      f32  [T][E]
  *   adapter_ids i32  [T]   (-1 or any id outside [0, L) = no adapter)
- *   out         f32  [T][H] (overwritten)
+ *   out         f32  [T][H] (overwritten); bf16 bits [T][H] with
+ *               MOE_LORA_FLAG_OUT_BF16
  *   workspace   device buffer of >= moe_lora_workspace_bytes() bytes, 256-byte
  *               aligned; it holds the routing, alignment and intermediates of
  *               this call until the next call that uses it.
@@ -128,7 +131,7 @@ int moe_lora_align(const moe_lora_desc *d, const int32_t *topk_ids, const int32_
  * inside the projection kernels (AWS post, section "Kernel optimizations":
  * the LoRA add is fused into the expand). */
 int moe_lora_forward(const moe_lora_desc *d, const moe_lora_weights *w, const void *x,
-                     const float *logits, const int32_t *adapter_ids, float *out,
+                     const float *logits, const int32_t *adapter_ids, void *out,
                      void *workspace, size_t ws_bytes, void *stream);
 
 /* Copy intermediates of the last moe_lora_forward on `workspace` out in pair

@@ -48,7 +48,7 @@ int check_desc(const moe_lora_desc* d) {
     if (d->E > 1024 || d->top_k < 1 || d->top_k > d->E || d->top_k > 32) return MOE_LORA_EINVAL;
     if (d->L > 0 && !(d->r == 8 || d->r == 16 || d->r == 32 || d->r == 64 || d->r == 128))
         return MOE_LORA_EINVAL;
-    if (d->flags != 0) return MOE_LORA_EINVAL;
+    if (d->flags & ~MOE_LORA_FLAG_OUT_BF16) return MOE_LORA_EINVAL;
     if (d->block_m_base != 0 && !pow2_in(d->block_m_base, 16, 256)) return MOE_LORA_EINVAL;
     if (d->block_m_lora != 0 && !pow2_in(d->block_m_lora, 16, 256)) return MOE_LORA_EINVAL;
     const long P = static_cast<long>(d->T) * d->top_k;
@@ -206,7 +206,7 @@ int moe_lora_align(const moe_lora_desc* d, const int32_t* topk_ids, const int32_
 }
 
 int moe_lora_forward(const moe_lora_desc* d, const moe_lora_weights* w, const void* x,
-                     const float* logits, const int32_t* adapter_ids, float* out,
+                     const float* logits, const int32_t* adapter_ids, void* out,
                      void* workspace, size_t ws_bytes, void* stream) {
     Plan p;
     int rc = make_plan(d, &p);
@@ -281,7 +281,7 @@ int moe_lora_forward(const moe_lora_desc* d, const moe_lora_weights* w, const vo
     ok(launch_gemm(ga, s));
     timing_mark(call, 6, s);
 
-    ok(launch_combine(dn, slot, tw, p.T, p.k, p.H, out, s));
+    ok(launch_combine(dn, slot, tw, p.T, p.k, p.H, out, (d->flags & MOE_LORA_FLAG_OUT_BF16) != 0, s));
     timing_mark(call, 7, s);
     return e == hipSuccess ? MOE_LORA_OK : MOE_LORA_EHIP;
 }

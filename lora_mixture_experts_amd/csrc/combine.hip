@@ -5,15 +5,18 @@
 // on Amazon SageMaker AI and Amazon Bedrock", section "Implementing multi-LoRA
 // inference for MoE models in vLLM": the chosen experts' outputs are
 // aggregated). Each thread owns four consecutive hidden columns of one token.
+// The sum is formed in fp32; the bf16 output form rounds it once, to nearest
+// even, at the store.
 #include "common.h"
 #include "kernels.h"
 
 namespace moelora {
 
+template <bool BF16OUT>
 __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ D,
                                                  const int32_t* __restrict__ slot_of_pair,
                                                  const float* __restrict__ w, int k, int H,
-                                                 float* __restrict__ out) {
+                                                 void* __restrict__ out) {
     const int t = blockIdx.x;
     const int n = (blockIdx.y * 256 + threadIdx.x) * 4;
     if (n >= H) return;
@@ -37,14 +40,24 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ D,
         for (int u = 0; u < 8; ++u)
             if (j0 + u < k) acc += wj[u] * d[u];
     }
-    *reinterpret_cast<f32x4*>(out + static_cast<size_t>(t) * H + n) = acc;
+    const size_t at = static_cast<size_t>(t) * H + n;
+    if (BF16OUT) {
+        const uint32_t lo = f32_to_bf16_rne(acc[0]) | (static_cast<uint32_t>(f32_to_bf16_rne(acc[1])) << 16);
+        const uint32_t hi = f32_to_bf16_rne(acc[2]) | (static_cast<uint32_t>(f32_to_bf16_rne(acc[3])) << 16);
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + at) = make_uint2(lo, hi);
+    } else {
+        *reinterpret_cast<f32x4*>(static_cast<float*>(out) + at) = acc;
+    }
 }
 
 hipError_t launch_combine(const float* D, const int32_t* slot_of_pair, const float* topk_w,
-                          int T, int k, int H, float* out, hipStream_t s) {
+                          int T, int k, int H, void* out, bool out_bf16, hipStream_t s) {
     if (T == 0) return hipSuccess;
     const dim3 grid(T, (H / 4 + 255) / 256), block(256);
-    hipLaunchKernelGGL(k_combine, grid, block, 0, s, D, slot_of_pair, topk_w, k, H, out);
+    if (out_bf16)
+        hipLaunchKernelGGL(k_combine<true>, grid, block, 0, s, D, slot_of_pair, topk_w, k, H, out);
+    else
+        hipLaunchKernelGGL(k_combine<false>, grid, block, 0, s, D, slot_of_pair, topk_w, k, H, out);
     return hipGetLastError();
 }
 

@@ -65,8 +65,9 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
 bool gemm_supported(int N_out, int K, int gate_up, int bm_b);
 
 // ---- combine + stage readers --------------------------------------------
+// out: fp32 [T][H], or bf16 bits [T][H] when out_bf16
 hipError_t launch_combine(const float* D, const int32_t* slot_of_pair, const float* topk_w,
-                          int T, int k, int H, float* out, hipStream_t s);
+                          int T, int k, int H, void* out, bool out_bf16, hipStream_t s);
 
 // dst[p][c] = sum_s src_part[s][slot(p)][c]; rows with mask[p] < 0 are 0
 // (mask may be null).

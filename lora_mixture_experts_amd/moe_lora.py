@@ -13,6 +13,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmoelora.so")
 
 OK, EINVAL, EWORKSPACE, EHIP = 0, -1, -2, -3
+FLAG_OUT_BF16 = 1
 NKERNELS = 7
 
 
@@ -189,9 +190,11 @@ class Layer:
     """Device-resident weights + descriptor + workspace for repeated calls."""
 
     def __init__(self, T, H, I, E, top_k, L, r, w_gate_up, w_down, a_gate_up=None, b_gate_up=None,
-                 a_down=None, b_down=None, block_m_base=0, block_m_lora=0):
+                 a_down=None, b_down=None, block_m_base=0, block_m_lora=0, out_bf16=False):
         import torch
-        self.desc = make_desc(T, H, I, E, top_k, L, r, block_m_base, block_m_lora)
+        self.desc = make_desc(T, H, I, E, top_k, L, r, block_m_base, block_m_lora,
+                              FLAG_OUT_BF16 if out_bf16 else 0)
+        self.out_dtype = torch.bfloat16 if out_bf16 else torch.float32
         self.tensors = (w_gate_up, w_down, a_gate_up, b_gate_up, a_down, b_down)
         self.weights = weights_struct(*self.tensors)
         _check(validate(self.desc, self.weights), "validate")
@@ -201,7 +204,7 @@ class Layer:
     def __call__(self, x, logits, adapter_ids, out=None, stream=None):
         import torch
         if out is None:
-            out = torch.empty((self.desc.T, self.desc.H), dtype=torch.float32, device=self.device)
+            out = torch.empty((self.desc.T, self.desc.H), dtype=self.out_dtype, device=self.device)
         forward(self.desc, self.weights, x, logits, adapter_ids, out, self.workspace, stream)
         return out
 

@@ -36,13 +36,14 @@ def desc(**over):
     d = dict(wl.CONFIGS["decode"])
     d.update(over)
     return ml.make_desc(d["T"], d["H"], d["I"], d["E"], d["top_k"], d["L"], d["r"],
-                        d.get("bm_b", 0), d.get("bm_l", 0))
+                        d.get("bm_b", 0), d.get("bm_l", 0), d.get("flags", 0))
 
 
 @pytest.mark.parametrize("over", [dict(H=2881), dict(I=100), dict(top_k=0), dict(top_k=33, E=40),
                                   dict(top_k=5, E=4), dict(r=24), dict(E=0), dict(T=-1), dict(L=-1),
                                   dict(bm_b=48), dict(bm_b=8), dict(bm_l=512), dict(E=1025),
-                                  dict(E=128, L=200), dict(E=1024, L=9, top_k=8)])
+                                  dict(E=128, L=200), dict(E=1024, L=9, top_k=8), dict(flags=2),
+                                  dict(flags=-1), dict(flags=3)])
 def test_validate_rejects(over):
     assert ml.validate(desc(**over)) == ml.EINVAL
 
@@ -55,6 +56,10 @@ def test_validate_accepts_configs_and_checks_workspace():
         assert n > 0 and n % 256 == 0
         assert ml.validate(ds, None, n) == ml.OK
         assert ml.validate(ds, None, n - 1) == ml.EWORKSPACE
+
+
+def test_validate_accepts_bf16_output_flag():
+    assert ml.validate(desc(flags=ml.FLAG_OUT_BF16)) == ml.OK
 
 
 def test_validate_key_limit_edge():

@@ -282,6 +282,55 @@ def test_repeat_calls_reuse_workspace(dev):
     assert torch.equal(out1, out2)
 
 
+def test_bf16_output_is_rounded_fp32_output(dev):
+    log("bf16 output")
+    case = build_case("decode")
+    layer, t, out32 = run_gpu(case, dev)
+    lb = ml.Layer(case.T, case.H, case.I, case.E, case.top_k, case.L, case.r, t["w_gate_up"], t["w_down"],
+                  t["a_gate_up"], t["b_gate_up"], t["a_down"], t["b_down"], out_bf16=True)
+    outb = lb(t["x"], t["logits"], t["adapter_ids"])
+    torch.cuda.synchronize()
+    assert outb.dtype == torch.bfloat16
+    # the combine sums in fp32 in a fixed order, so the bf16 form is exactly the
+    # round-to-nearest-even of the fp32 output
+    np.testing.assert_array_equal(outb.view(torch.int16).cpu().numpy(),
+                                  out32.to(torch.bfloat16).view(torch.int16).cpu().numpy())
+
+
+def test_graph_replay_matches_eager(dev):
+    # the whole layer captured into one HIP graph (no host sync, no allocation,
+    # no memset inside the call) replays to the eager result, also after the
+    # inputs change in place, with eager calls on the same workspace between
+    # replays
+    log("graph replay")
+    case = build_case("decode")
+    layer, t, out_eager = run_gpu(case, dev)
+    ref = out_eager.clone()
+    out = torch.empty_like(ref)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        layer(t["x"], t["logits"], t["adapter_ids"], out=out)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        layer(t["x"], t["logits"], t["adapter_ids"], out=out)
+    x0 = t["x"].clone()
+    x1 = torch.flip(x0, dims=[0]).contiguous()  # the tokens in reverse order
+    for i in range(4):
+        xi = x0 if i % 2 == 0 else x1
+        t["x"].copy_(xi)
+        want = layer(t["x"], t["logits"], t["adapter_ids"]).clone()  # eager, same workspace
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, want), i
+        if i % 2 == 0:
+            assert torch.equal(out, ref)
+    t["x"].copy_(x0)
+
+
 def test_zero_tokens_is_noop(dev):
     d = ml.make_desc(0, 64, 64, 2, 1, 0, 8)
     w = torch.zeros(2 * 2 * 64 * 64, dtype=torch.bfloat16, device=dev)

@@ -8,7 +8,8 @@ inputs are already resident in HBM.
 Default workload: the decode-shaped layer (16 tokens, hidden = intermediate =
 2880, 32 experts top-4, 8 adapters of rank 32). The prefill-shaped layer
 (4 x 1600 tokens, same dims) is measured in the same run and reported in the
-"prefill" object of the same JSON line.
+"prefill" object of the same JSON line; the wide-expert, many-adapter, tiny
+and dense (one expert) layers follow in "other_workloads".
 
 Weight copies are rotated between calls so that the working set of
 consecutive calls exceeds the 256 MB Infinity Cache.
@@ -33,7 +34,10 @@ BF16_PEAK_TFLOPS = 2500.0
 WORKLOAD_NAMES = {"decode": "decode-shaped MoE-LoRA layer (T=16, H=I=2880, E=32 top-4, L=8, r=32)",
                   "prefill": "prefill-shaped MoE-LoRA layer (T=6400=4x1600, H=I=2880, E=32 top-4, L=8, r=32)",
                   "wide": "wide-expert layer (T=64, H=4096, I=11008, E=8 top-2, L=8, r=32)",
-                  "many": "many-adapter layer (T=512, H=I=2880, E=32 top-4, L=128, r=64)"}
+                  "many": "many-adapter layer (T=512, H=I=2880, E=32 top-4, L=128, r=64)",
+                  "tiny": "tiny MoE-LoRA layer (T=16, H=256, I=512, E=8 top-2, L=2, r=8)",
+                  "dense": "dense multi-LoRA MLP (T=16, H=5120, I=25600, one expert, L=8, r=32)"}
+RIDGE_FLOP_PER_BYTE = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
 
 
 def log(msg):
@@ -113,6 +117,15 @@ def run_workload(name, steps, warmup, rotate, dev):
     ev1.record()
     torch.cuda.synchronize()
     ms = ev0.elapsed_time(ev1) / steps
+    # four more repeats of the same steps, for a median beside the timed value
+    repeats = [ms]
+    for _ in range(4):
+        ev0.record()
+        for i in range(steps):
+            step(i)
+        ev1.record()
+        torch.cuda.synchronize()
+        repeats.append(ev0.elapsed_time(ev1) / steps)
 
     # per-kernel durations: HIP events recorded by the library around each
     # kernel on the launch stream, over a second pass of the same steps
@@ -126,27 +139,70 @@ def run_workload(name, steps, warmup, rotate, dev):
     b, f, layer_bytes, layer_flops = algorithmic(case, st)
     del layers, base
     torch.cuda.empty_cache()
-    return case, ids, st, ms, kernel_us, b, f, layer_bytes, layer_flops
+    return case, ids, st, ms, kernel_us, b, f, layer_bytes, layer_flops, repeats
 
 
-def cpu_baseline(case, ids, budget_s):
+def workload_summary(name, c, st, ms, kus, b, f, lb, lf, repeats_ms):
+    """One workload's object: throughput, per-kernel times, layer roofline and
+    the dominant projection kernel against its bound."""
+    dom = max(("gemm_gate_up", "gemm_down"), key=lambda n: kus[n])
+    mfma = lf / lb > RIDGE_FLOP_PER_BYTE
+    roof_us = max(lb / (HBM_PEAK_GBS * 1e9), lf / (BF16_PEAK_TFLOPS * 1e12)) * 1e6
+    traffic = read_traffic(os.path.join(ROOT, "profiles", f"hbm_traffic_{name}.md"), dom)
+    if mfma:
+        achieved = f[dom] / (kus[dom] * 1e-6) / 1e12
+        roof = dict(kernel=dom, bound="mfma", achieved=round(achieved, 1), peak=BF16_PEAK_TFLOPS,
+                    unit="TFLOP/s", frac=round(achieved / BF16_PEAK_TFLOPS, 4), traffic=traffic,
+                    flops_per_launch=f[dom], bytes_per_launch=b[dom], us_per_launch=round(kus[dom], 2))
+    else:
+        achieved = b[dom] / (kus[dom] * 1e-6) / 1e9
+        roof = dict(kernel=dom, bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic,
+                    bytes_per_launch=b[dom], us_per_launch=round(kus[dom], 2))
+    gemm_us = kus["gemm_gate_up"] + kus["gemm_down"]
+    out = {"workload": WORKLOAD_NAMES[name], "value": round(c.T / (ms * 1e-3), 1), "unit": "tokens/s",
+           "us_per_call": round(ms * 1e3, 2),
+           "us_per_call_median_of_repeats": round(float(np.median(repeats_ms)) * 1e3, 2),
+           "layer_bound": "mfma" if mfma else "hbm",
+           "layer_roofline_frac": round(roof_us / (ms * 1e3), 4),
+           "kernel_us": {k: round(v, 2) for k, v in kus.items()}, "routing": st, "roofline": roof}
+    if mfma:
+        tf = (f["gemm_gate_up"] + f["gemm_down"]) / (gemm_us * 1e-6) / 1e12
+        out["base_gemms_tflops"] = round(tf, 1)
+        out["base_gemms_mfma_frac"] = round(tf / BF16_PEAK_TFLOPS, 4)
+    else:
+        gb = (b["gemm_gate_up"] + b["gemm_down"]) / (gemm_us * 1e-6) / 1e9
+        out["projection_kernels_gbs"] = round(gb, 1)
+        out["projection_kernels_hbm_frac"] = round(gb / HBM_PEAK_GBS, 4)
+    return out
+
+
+def cpu_baseline(case, ids, budget_s, single_budget_s):
     import oracle
-    w = None
     ids_, w = oracle.route(case.logits, case.top_k)
     cores = oracle.default_threads()
-    # bounded sample: whole token batches until the time budget is used
     n_tok = case.T
     toks = np.arange(n_tok, dtype=np.int32)
-    done, t0 = 0, time.perf_counter()
-    while True:
-        oracle.forward(case, ids_, w, tokens=toks, threads=cores)
-        done += n_tok
-        if time.perf_counter() - t0 >= budget_s:
-            break
-    dt = time.perf_counter() - t0
-    return dict(value=done / dt, unit="tokens/s", cores=cores, kind="oracle",
-                sample=f"{done} tokens ({done // n_tok} full {case.name} batches of {n_tok}) "
-                       f"through the fp64 C oracle in {dt:.1f}s")
+
+    def timed(threads, budget):
+        # bounded sample: whole token batches until the time budget is used
+        done, t0 = 0, time.perf_counter()
+        while True:
+            oracle.forward(case, ids_, w, tokens=toks, threads=threads)
+            done += n_tok
+            if time.perf_counter() - t0 >= budget:
+                break
+        return done, time.perf_counter() - t0
+
+    done, dt = timed(cores, budget_s)
+    out = dict(value=done / dt, unit="tokens/s", cores=cores, kind="oracle",
+               sample=f"{done} tokens ({done // n_tok} full {case.name} batches of {n_tok}) "
+                      f"through the fp64 C oracle in {dt:.1f}s")
+    if single_budget_s > 0:
+        d1, t1 = timed(1, single_budget_s)
+        out["single_thread"] = dict(value=d1 / t1, unit="tokens/s", cores=1,
+                                    sample=f"{d1} tokens ({d1 // n_tok} full batches) in {t1:.1f}s")
+    return out
 
 
 def main():
@@ -155,8 +211,10 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode", choices=list(WORKLOAD_NAMES))
-    ap.add_argument("--also", default="prefill",
-                    help="second workload reported in the same line ('none' = none)")
+    ap.add_argument("--cpu-single-budget", type=float, default=3.0,
+                    help="seconds of the one-thread oracle run reported beside the all-core one")
+    ap.add_argument("--also", default="prefill,wide,many,tiny,dense",
+                    help="comma list of further workloads reported in the same line ('none' = none)")
     ap.add_argument("--rotate", type=int, default=3)
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MiB",
@@ -183,67 +241,40 @@ def main():
         torch.neg(src, out=dst)
         torch.cuda.synchronize()
         del src, dst
-    case, ids, st, ms, kus, b, f, lbytes, lflops = run_workload(args.workload, args.steps, args.warmup,
-                                                               args.rotate, dev)
-    dom = max(("gemm_gate_up", "gemm_down"), key=lambda n: kus[n])
-    traffic = read_traffic(os.path.join(ROOT, "profiles", f"hbm_traffic_{args.workload}.md"), dom)
-    hbm_bound = case.T * case.top_k / max(st["n_experts"], 1) < 312
-    if hbm_bound:
-        achieved = b[dom] / (kus[dom] * 1e-6) / 1e9
-        roof = dict(kernel=dom, bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic,
-                    bytes_per_launch=b[dom], us_per_launch=round(kus[dom], 2))
-    else:
-        achieved = f[dom] / (kus[dom] * 1e-6) / 1e12
-        roof = dict(kernel=dom, bound="mfma", achieved=round(achieved, 1), peak=BF16_PEAK_TFLOPS,
-                    unit="TFLOP/s", frac=round(achieved / BF16_PEAK_TFLOPS, 4), traffic=traffic,
-                    flops_per_launch=f[dom], bytes_per_launch=b[dom], us_per_launch=round(kus[dom], 2))
-    layer_roof_us = max(lbytes / (HBM_PEAK_GBS * 1e9), lflops / (BF16_PEAK_TFLOPS * 1e12)) * 1e6
+    case, ids, st, ms, kus, b, f, lbytes, lflops, reps = run_workload(args.workload, args.steps, args.warmup,
+                                                                     args.rotate, dev)
+    main_obj = workload_summary(args.workload, case, st, ms, kus, b, f, lbytes, lflops, reps)
     lora_us = kus["shrink_gate_up"] + kus["shrink_down"]
     lora_bytes = b["shrink_gate_up"] + b["shrink_down"]
     line = {
         "metric": "MoE-LoRA layer tokens/s + us/call (decode 16 tok, prefill 6400 tok); % roofline",
-        "value": round(case.T / (ms * 1e-3), 1),
+        "value": main_obj["value"],
         "unit": "tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
-        "us_per_call": round(ms * 1e3, 2),
+        "us_per_call": main_obj["us_per_call"],
+        "us_per_call_median_of_repeats": main_obj["us_per_call_median_of_repeats"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic (seeded, N(0,1) activations/logits, N(0,0.02) weights)",
         "config": {"workload": WORKLOAD_NAMES[args.workload], "global_batch": case.T, "seq_len": 1,
                    "parallelism": "none (1 GPU)", "rotated_weight_copies": args.rotate},
-        "layer_roofline_frac": round(layer_roof_us / (ms * 1e3), 4),
-        "kernel_us": {k: round(v, 2) for k, v in kus.items()},
+        "layer_roofline_frac": main_obj["layer_roofline_frac"],
+        "kernel_us": main_obj["kernel_us"],
         "lora_shrink_hbm_frac": round(lora_bytes / (lora_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4) if lora_us else None,
         "routing": st,
-        "roofline": roof,
+        "roofline": main_obj["roofline"],
     }
-    if args.also and args.also != "none":
-        c2, ids2, st2, ms2, kus2, b2, f2, lb2, lf2 = run_workload(args.also, max(5, args.steps // 5),
-                                                                   max(2, args.warmup // 2),
-                                                                   args.rotate, dev)
-        dom2 = max(("gemm_gate_up", "gemm_down"), key=lambda n: kus2[n])
-        gemm_us = kus2["gemm_gate_up"] + kus2["gemm_down"]
-        gemm_tf = (f2["gemm_gate_up"] + f2["gemm_down"]) / (gemm_us * 1e-6) / 1e12
-        lroof = max(lb2 / (HBM_PEAK_GBS * 1e9), lf2 / (BF16_PEAK_TFLOPS * 1e12)) * 1e6
-        line["prefill" if args.also == "prefill" else args.also] = {
-            "workload": WORKLOAD_NAMES[args.also], "value": round(c2.T / (ms2 * 1e-3), 1),
-            "unit": "tokens/s", "us_per_call": round(ms2 * 1e3, 2),
-            "layer_roofline_frac": round(lroof / (ms2 * 1e3), 4),
-            "kernel_us": {k: round(v, 2) for k, v in kus2.items()},
-            "base_gemms_tflops": round(gemm_tf, 1),
-            "base_gemms_mfma_frac": round(gemm_tf / BF16_PEAK_TFLOPS, 4),
-            "roofline": dict(kernel=dom2, bound="mfma",
-                             achieved=round(f2[dom2] / (kus2[dom2] * 1e-6) / 1e12, 1),
-                             peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
-                             frac=round(f2[dom2] / (kus2[dom2] * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4),
-                             traffic=read_traffic(os.path.join(ROOT, "profiles",
-                                                               f"hbm_traffic_{args.also}.md"), dom2),
-                             flops_per_launch=f2[dom2], bytes_per_launch=b2[dom2],
-                             us_per_launch=round(kus2[dom2], 2)),
-        }
+    others = [w for w in args.also.split(",") if w and w != "none" and w != args.workload]
+    for name in others:
+        steps2 = max(5, args.steps // 5) if name in ("prefill", "many") else max(10, args.steps // 2)
+        res = run_workload(name, steps2, max(2, args.warmup // 2), args.rotate, dev)
+        obj = workload_summary(name, res[0], res[2], *res[3:])
+        if name == "prefill":
+            line["prefill"] = obj
+        else:
+            line.setdefault("other_workloads", {})[name] = obj
     if args.cpu_budget > 0:
-        line["cpu_baseline"] = cpu_baseline(case, ids, args.cpu_budget)
+        line["cpu_baseline"] = cpu_baseline(case, ids, args.cpu_budget, args.cpu_single_budget)
     print(json.dumps(line), flush=True)
 
 

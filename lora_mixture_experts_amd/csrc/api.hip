@@ -21,6 +21,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 struct Plan {
     int T, H, I, E, k, L, r, P;
     int bm_b, bm_l, C_b, C_l, nblk_b, nblk_l;
+    int ksplit;  // K ranges of the down projection (partial sums summed by the combine)
     size_t off_ids, off_w, off_sorted_b, off_blk_e_b, off_counts, off_sorted_l, off_blk_e_l,
         off_blk_a_l, off_slot, off_lslot, off_sad, off_defer, off_s1, off_s2, off_h, off_d, total;
 };
@@ -28,11 +29,16 @@ struct Plan {
 int roundup_i(long v, long m) { return static_cast<int>((v + m - 1) / m * m); }
 
 int default_bm_base(int P, int E) {
+    if (E == 1) {  // no routing: the one expert holds all P rows
+        int bm = 16;
+        while (bm < P && bm < 128) bm *= 2;
+        return bm;
+    }
     const long avg = (P + E - 1) / E;  // mean rows per expert
-    if (2 * avg <= 16) return 16;
-    if (2 * avg <= 32) return 32;
-    if (2 * avg <= 64) return 64;
-    return 128;
+    if (avg <= 8) return 16;    // weight streaming: one 16-row block per expert
+    if (avg <= 16) return 32;
+    if (avg <= 96) return 64;   // still HBM-bound: register-staged 64-row tiles
+    return 128;                 // MFMA-bound: direct-to-LDS 128 x 192 tiles
 }
 
 int default_bm_lora(int P, int E, int L) {
@@ -73,6 +79,7 @@ int make_plan(const moe_lora_desc* d, Plan* p) {
     p->C_l = roundup_i(P + std::min<long>(static_cast<long>(p->E) * p->L, P) * (p->bm_l - 1), p->bm_l);
     p->nblk_b = p->C_b / p->bm_b;
     p->nblk_l = p->C_l / p->bm_l;
+    p->ksplit = gemm_down_ksplit(p->H, p->I, p->bm_b, p->nblk_b);
     size_t o = 0;
     auto take = [&](size_t bytes) { const size_t at = o; o += up(bytes); return at; };
     p->off_ids = take(4 * P);
@@ -91,7 +98,7 @@ int make_plan(const moe_lora_desc* d, Plan* p) {
     p->off_s1 = take(sbytes);
     p->off_s2 = take(sbytes);
     p->off_h = take(2ul * p->C_b * p->I);
-    p->off_d = take(4ul * p->C_b * p->H);
+    p->off_d = take(4ul * p->ksplit * p->C_b * p->H);
     p->total = o;
     return MOE_LORA_OK;
 }
@@ -262,7 +269,7 @@ int moe_lora_forward(const moe_lora_desc* d, const moe_lora_weights* w, const vo
     GemmArgs ga{};
     ga.sorted_b = sorted_b; ga.blk_e_b = blk_e_b; ga.P = p.P; ga.top_k = p.k; ga.bm_b = p.bm_b;
     ga.n_blocks = p.nblk_b; ga.slot_adapter = sad; ga.L = p.L; ga.E = p.E; ga.r = p.r;
-    ga.C_b = p.C_b; ga.h_out = h; ga.d_out = dn;
+    ga.C_b = p.C_b; ga.h_out = h; ga.d_out = dn; ga.ksplit = 1;
     ga.X = static_cast<const uint16_t*>(x); ga.gate_up = 1;
     ga.W = static_cast<const uint16_t*>(w->w_gate_up); ga.N_out = p.I; ga.K = p.H;
     ga.S = s1; ga.Bl = static_cast<const uint16_t*>(w->b_gate_up);
@@ -277,11 +284,12 @@ int moe_lora_forward(const moe_lora_desc* d, const moe_lora_weights* w, const vo
     timing_mark(call, 5, s);
 
     ga.X = h; ga.gate_up = 0; ga.W = static_cast<const uint16_t*>(w->w_down); ga.N_out = p.H;
-    ga.K = p.I; ga.S = s2; ga.Bl = static_cast<const uint16_t*>(w->b_down);
+    ga.K = p.I; ga.S = s2; ga.Bl = static_cast<const uint16_t*>(w->b_down); ga.ksplit = p.ksplit;
     ok(launch_gemm(ga, s));
     timing_mark(call, 6, s);
 
-    ok(launch_combine(dn, slot, tw, p.T, p.k, p.H, out, (d->flags & MOE_LORA_FLAG_OUT_BF16) != 0, s));
+    ok(launch_combine(dn, p.ksplit, p.C_b, slot, tw, p.T, p.k, p.H, out,
+                      (d->flags & MOE_LORA_FLAG_OUT_BF16) != 0, s));
     timing_mark(call, 7, s);
     return e == hipSuccess ? MOE_LORA_OK : MOE_LORA_EHIP;
 }
@@ -309,7 +317,7 @@ int moe_lora_read_stages(const moe_lora_desc* d, const void* workspace, size_t w
     if (s1) ok(launch_gather_rows_f32(at<float>(ws, p.off_s1), 1, p.C_b, p.r, slot, lslot, p.P, s1, s));
     if (s2) ok(launch_gather_rows_f32(at<float>(ws, p.off_s2), 1, p.C_b, p.r, slot, lslot, p.P, s2, s));
     if (h) ok(launch_gather_rows_bf16(at<uint16_t>(ws, p.off_h), p.I, slot, p.P, h, s));
-    if (dn) ok(launch_gather_rows_f32(at<float>(ws, p.off_d), 1, p.C_b, p.H, slot, nullptr, p.P, dn, s));
+    if (dn) ok(launch_gather_rows_f32(at<float>(ws, p.off_d), p.ksplit, p.C_b, p.H, slot, nullptr, p.P, dn, s));
     return e == hipSuccess ? MOE_LORA_OK : MOE_LORA_EHIP;
 }
 

@@ -1,6 +1,7 @@
 // Top-k weighted combine and the stage readers.
 //
-// Combine: out[t] = sum_j w[t][j] * D[slot(t, j)], j ascending, no atomics
+// Combine: out[t] = sum_j w[t][j] * D[slot(t, j)], j ascending, no atomics,
+// where D is the sum of the down projection's K-range partials (in order)
 // (AWS ML Blog post "Efficiently serve dozens of fine-tuned models with vLLM
 // on Amazon SageMaker AI and Amazon Bedrock", section "Implementing multi-LoRA
 // inference for MoE models in vLLM": the chosen experts' outputs are
@@ -13,33 +14,42 @@
 namespace moelora {
 
 template <bool BF16OUT>
-__global__ __launch_bounds__(256) void k_combine(const float* __restrict__ D,
+__global__ __launch_bounds__(256) void k_combine(const float* __restrict__ D, int nsplit, int C_b,
                                                  const int32_t* __restrict__ slot_of_pair,
                                                  const float* __restrict__ w, int k, int H,
                                                  void* __restrict__ out) {
     const int t = blockIdx.x;
     const int n = (blockIdx.y * 256 + threadIdx.x) * 4;
     if (n >= H) return;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    // up to 8 choices per round: all slot/weight loads, then all row loads,
-    // then the sums in j order (no load waits on the previous choice's add)
-    for (int j0 = 0; j0 < k; j0 += 8) {
+    const size_t part = static_cast<size_t>(C_b) * H;  // one K-range partial
+    // items q = j * nsplit + s in ascending order, 8 per round: the slot loads
+    // of a round, then its row loads, then the adds; d holds choice j's sum
+    // over s, folded into acc (times w_j) when the next choice starts
+    const int nq = k * nsplit;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f}, d = {0.f, 0.f, 0.f, 0.f};
+    for (int q0 = 0; q0 < nq; q0 += 8) {
         int slot[8];
-        float wj[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) slot[u] = slot_of_pair[t * k + min(q0 + u, nq - 1) / nsplit];
+        f32x4 v[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-            const int j = min(j0 + u, k - 1);
-            slot[u] = slot_of_pair[t * k + j];
-            wj[u] = w[t * k + j];
+            const int sp = min(q0 + u, nq - 1) % nsplit;
+            v[u] = *reinterpret_cast<const f32x4*>(D + sp * part + static_cast<size_t>(slot[u]) * H + n);
         }
-        f32x4 d[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
-            d[u] = *reinterpret_cast<const f32x4*>(D + static_cast<size_t>(slot[u]) * H + n);
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-            if (j0 + u < k) acc += wj[u] * d[u];
+        for (int u = 0; u < 8; ++u) {
+            const int q = q0 + u;
+            if (q < nq) {
+                if (q > 0 && q % nsplit == 0) {
+                    acc += w[t * k + q / nsplit - 1] * d;
+                    d = f32x4{0.f, 0.f, 0.f, 0.f};
+                }
+                d += v[u];
+            }
+        }
     }
+    acc += w[t * k + k - 1] * d;
     const size_t at = static_cast<size_t>(t) * H + n;
     if (BF16OUT) {
         const uint32_t lo = f32_to_bf16_rne(acc[0]) | (static_cast<uint32_t>(f32_to_bf16_rne(acc[1])) << 16);
@@ -50,14 +60,15 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ D,
     }
 }
 
-hipError_t launch_combine(const float* D, const int32_t* slot_of_pair, const float* topk_w,
-                          int T, int k, int H, void* out, bool out_bf16, hipStream_t s) {
+hipError_t launch_combine(const float* D, int nsplit, int C_b, const int32_t* slot_of_pair,
+                          const float* topk_w, int T, int k, int H, void* out, bool out_bf16,
+                          hipStream_t s) {
     if (T == 0) return hipSuccess;
     const dim3 grid(T, (H / 4 + 255) / 256), block(256);
     if (out_bf16)
-        hipLaunchKernelGGL(k_combine<true>, grid, block, 0, s, D, slot_of_pair, topk_w, k, H, out);
+        hipLaunchKernelGGL(k_combine<true>, grid, block, 0, s, D, nsplit, C_b, slot_of_pair, topk_w, k, H, out);
     else
-        hipLaunchKernelGGL(k_combine<false>, grid, block, 0, s, D, slot_of_pair, topk_w, k, H, out);
+        hipLaunchKernelGGL(k_combine<false>, grid, block, 0, s, D, nsplit, C_b, slot_of_pair, topk_w, k, H, out);
     return hipGetLastError();
 }
 

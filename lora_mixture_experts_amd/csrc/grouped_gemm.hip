@@ -16,6 +16,8 @@
 // activation columns, so every lane holds matching gate and up values and the
 // SwiGLU epilogue h = silu(gate) * up runs in registers; h is stored in bf16.
 // down: the fp32 result is stored per base slot for the weighted combine.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -79,7 +81,7 @@ __device__ __forceinline__ u32x4 load_lora_b(const GemmArgs& a, int Nw, int ad, 
 // flight while chunk q is multiplied.
 template <bool GATEUP, int FN>
 __global__ __launch_bounds__(64) void k_gemm_skinny(GemmArgs a) {
-    const int b = blockIdx.y, tile = blockIdx.x;
+    const int b = blockIdx.y, tile = blockIdx.x, z = blockIdx.z;  // z: K range (down only)
     const int e = a.blk_e_b[b];
     if (e < 0) return;
     const int lane = threadIdx.x & 63;
@@ -89,6 +91,7 @@ __global__ __launch_bounds__(64) void k_gemm_skinny(GemmArgs a) {
     constexpr int kCols = GATEUP ? FN * 8 : FN * 16;  // output columns per wave
     const int c0 = tile * kCols;
     const int K = a.K;
+    const int Kp = K / a.ksplit, kbeg = z * Kp;  // this workgroup's K range
 
     const int slot = b * 16 + lrow;
     // Padding rows (sentinel P) re-read the block's first row, which is always
@@ -100,15 +103,15 @@ __global__ __launch_bounds__(64) void k_gemm_skinny(GemmArgs a) {
     if (GATEUP) {
         int p = a.sorted_b[slot];
         if (p >= a.P) p = a.sorted_b[b * 16];
-        xrow = a.X + static_cast<size_t>(p / a.top_k) * K + g * 16;
+        xrow = a.X + static_cast<size_t>(p / a.top_k) * K + kbeg + g * 16;
     } else {
-        xrow = a.X + static_cast<size_t>(slot) * K + g * 16;
+        xrow = a.X + static_cast<size_t>(slot) * K + kbeg + g * 16;
     }
     const uint16_t* wrow[FN];
 #pragma unroll
     for (int f = 0; f < FN; ++f)
         wrow[f] = a.W + (static_cast<size_t>(e) * Nw + w_row_of_frag<GATEUP>(f, c0, I) + lrow) * K +
-                  g * 16;
+                  kbeg + g * 16;
 
     f32x4 acc[FN];
 #pragma unroll
@@ -130,14 +133,14 @@ __global__ __launch_bounds__(64) void k_gemm_skinny(GemmArgs a) {
             for (int f = 0; f < FN; ++f) acc[f] = mfma16x16x32(xb[buf][h], wb[buf][f][h], acc[f]);
     };
 
-    const int nq = K / 64;
+    const int nq = Kp / 64;
     load(0, 0);
     __builtin_amdgcn_sched_barrier(0);
 
     // LoRA expand first (its inputs are ready before this kernel starts), so
     // its latency overlaps the first weight loads: acc += S . B^T for every
-    // adapter present among the 16 rows.
-    if (a.L > 0) {
+    // adapter present among the 16 rows (added once: by the first K range).
+    if (a.L > 0 && z == 0) {
         const int my_a = row_adapter(a, slot);
         bool pending = my_a >= 0;
         while (true) {
@@ -191,11 +194,12 @@ __global__ __launch_bounds__(64) void k_gemm_skinny(GemmArgs a) {
                     f32_to_bf16_rne(silu(acc[2 * u][i]) * acc[2 * u + 1][i]);
         }
     } else {
+        float* dpart = a.d_out + static_cast<size_t>(z) * a.C_b * a.N_out;
 #pragma unroll
         for (int f = 0; f < FN; ++f) {
             const int col = c0 + 16 * f + lrow;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) a.d_out[static_cast<size_t>(orow0 + i) * a.N_out + col] = acc[f][i];
+            for (int i = 0; i < 4; ++i) dpart[static_cast<size_t>(orow0 + i) * a.N_out + col] = acc[f][i];
         }
     }
 }
@@ -251,10 +255,10 @@ static inline int tiled_grid(int n_blocks, int n_tiles) {
 template <int FM, int FN, bool GATEUP, typename WRowOf>
 __device__ __forceinline__ void tile_epilogue(const GemmArgs& a, f32x4 (&acc)[FM][FN], bool wlive,
                                               int wrow_base, int wn, int c0, int e, int kc,
-                                              int lrow, WRowOf wrow_of) {
+                                              int lrow, WRowOf wrow_of, int z = 0) {
     if (!wlive) return;
     const int Nw = GATEUP ? 2 * a.N_out : a.N_out;
-    if (a.L > 0) {
+    if (a.L > 0 && z == 0) {  // the LoRA term is added once, by the first K range
         int my_a[FM];
         bool pending[FM];
 #pragma unroll
@@ -308,13 +312,14 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& a, f32x4 (&acc)[FM
                         f32_to_bf16_rne(silu(acc[i][j][q]) * acc[i][j + 1][q]);
             }
         } else {
+            float* dpart = a.d_out + static_cast<size_t>(z) * a.C_b * a.N_out;
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
                 const int col = c0 + 16 * (wn * FN + j) + lrow;
                 if (col >= a.N_out) continue;
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
-                    a.d_out[static_cast<size_t>(orow0 + q) * a.N_out + col] = acc[i][j][q];
+                    dpart[static_cast<size_t>(orow0 + q) * a.N_out + col] = acc[i][j][q];
             }
         }
     }
@@ -343,6 +348,7 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_tiled(GemmArgs a) {
     const int Nw = GATEUP ? 2 * a.N_out : a.N_out;
     const int c0 = tile * kCols;
     const int K = a.K;
+    const int z = blockIdx.y, Kp = K / a.ksplit, kbeg = z * Kp;  // K range (down only)
     const int row0 = b * BM;
     // weight row of tile row r (columns past N_out, in a partial last tile,
     // re-read the last valid row; their results are not stored)
@@ -368,16 +374,16 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_tiled(GemmArgs a) {
         const int slot = row0 + r;
         if (GATEUP) {
             const int p = a.sorted_b[slot];
-            asrc[i] = a.X + static_cast<size_t>((p < a.P ? p : p_first) / a.top_k) * K + ld_chunk * 8;
+            asrc[i] = a.X + static_cast<size_t>((p < a.P ? p : p_first) / a.top_k) * K + kbeg + ld_chunk * 8;
         } else {
-            asrc[i] = a.X + static_cast<size_t>(slot) * K + ld_chunk * 8;
+            asrc[i] = a.X + static_cast<size_t>(slot) * K + kbeg + ld_chunk * 8;
         }
     }
     const uint16_t* bsrc[C::B_LD];
 #pragma unroll
     for (int i = 0; i < C::B_LD; ++i) {
         const int r = ld_row + C::ROWS_PER_PASS * i;
-        bsrc[i] = a.W + (static_cast<size_t>(e) * Nw + wrow_of(r)) * K + ld_chunk * 8;
+        bsrc[i] = a.W + (static_cast<size_t>(e) * Nw + wrow_of(r)) * K + kbeg + ld_chunk * 8;
     }
 
     // A wave whose first row is padding holds no real row (rows are real
@@ -387,7 +393,7 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_tiled(GemmArgs a) {
     const int wrow_base = row0 + wm * (BM / WM);
     const bool wlive = a.sorted_b[wrow_base] < a.P;
     u32x4 ra[2][C::A_LD], rb[2][C::B_LD];
-    const int nk = K / 64;
+    const int nk = Kp / 64;
     auto gload = [&](int set, int kt) {
         const int k0 = kt * 64;
 #pragma unroll
@@ -454,7 +460,7 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_tiled(GemmArgs a) {
     }
     if (nk & 1) compute(0);
 
-    tile_epilogue<FM, FN, GATEUP>(a, acc, wlive, wrow_base, wn, c0, e, kc, lrow, wrow_of);
+    tile_epilogue<FM, FN, GATEUP>(a, acc, wlive, wrow_base, wn, c0, e, kc, lrow, wrow_of, z);
 }
 
 // ===========================================================================
@@ -666,7 +672,7 @@ template <int BM, int BNT, int WM, int WN>
 static hipError_t launch_tiled(const GemmArgs& a, hipStream_t s) {
     const int cols = a.gate_up ? BNT / 2 : BNT;
     const int n_tiles = (a.N_out + cols - 1) / cols;
-    const dim3 grid(tiled_grid(a.n_blocks, n_tiles)), block(64 * WM * WN);
+    const dim3 grid(tiled_grid(a.n_blocks, n_tiles), a.ksplit), block(64 * WM * WN);
     if (a.gate_up)
         hipLaunchKernelGGL((k_gemm_tiled<BM, BNT, WM, WN, true>), grid, block, 0, s, a);
     else
@@ -690,14 +696,31 @@ static int skinny_fn(int N_out, int gate_up) {
     return (MOELORA_SKINNY_FN == 8 && N_out % cols8 == 0) ? 8 : 4;
 }
 
+int gemm_down_ksplit(int N_out, int K, int bm_b, int n_blocks) {
+    if (bm_b >= 128 || n_blocks <= 0) return 1;
+    const long cols = bm_b == 16 ? 16 * skinny_fn(N_out, 0) : 128;
+    const long waves = (N_out + cols - 1) / cols * n_blocks * (bm_b == 16 ? 1 : 4);
+    constexpr long kTargetWaves = 4096;  // about 16 per CU
+    constexpr int kMinChunks = 8;        // at least 512 of K per split
+    constexpr int kLongK = 96;           // only long K ranges (>= 6144) are split
+    const int chunks = K / 64;
+    if (chunks < kLongK) return 1;
+    int ks = static_cast<int>(std::min<long>((kTargetWaves + waves - 1) / waves, chunks / kMinChunks));
+    for (; ks > 1; --ks)
+        if (chunks % ks == 0) break;
+    return std::max(ks, 1);
+}
+
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
     if (a.n_blocks == 0) return hipSuccess;
     if (!gemm_supported(a.N_out, a.K, a.gate_up, a.bm_b)) return hipErrorInvalidValue;
+    if (a.ksplit < 1 || (a.K / 64) % a.ksplit || (a.ksplit > 1 && (a.gate_up || a.bm_b >= 128)))
+        return hipErrorInvalidValue;
     if (a.bm_b == 16) {
         const int fn = skinny_fn(a.N_out, a.gate_up);
         const int cols = a.gate_up ? fn * 8 : fn * 16;
         if (a.n_blocks > 65535) return hipErrorInvalidValue;
-        const dim3 grid(a.N_out / cols, a.n_blocks), block(64);
+        const dim3 grid(a.N_out / cols, a.n_blocks, a.ksplit), block(64);
         if (fn == 8) {
             if (a.gate_up) hipLaunchKernelGGL((k_gemm_skinny<true, 8>), grid, block, 0, s, a);
             else hipLaunchKernelGGL((k_gemm_skinny<false, 8>), grid, block, 0, s, a);

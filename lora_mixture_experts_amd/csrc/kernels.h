@@ -58,16 +58,24 @@ struct GemmArgs {
     const uint16_t* Bl;       // gate_up: [L][E][2I][r]; down: [L][E][H][r]
     // outputs
     uint16_t* h_out;          // [C_b][I]
-    float* d_out;             // [C_b][H]
+    float* d_out;             // [ksplit][C_b][H] partial sums over K ranges (down)
+    int ksplit;               // down only: the K range is cut into ksplit equal parts
 };
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
 // Whether a tile configuration exists for these sizes.
 bool gemm_supported(int N_out, int K, int gate_up, int bm_b);
+// K splits for the down projection: enough waves to fill the chip when the
+// grid is small (few blocks, few column tiles, long K); 1 for the large-block
+// kernels. Always divides K / 64.
+int gemm_down_ksplit(int N_out, int K, int bm_b, int n_blocks);
 
 // ---- combine + stage readers --------------------------------------------
+// out[t] = sum_j w[t][j] * (sum_s D[s][slot(t, j)]), s = 0..nsplit-1 (the
+// K-range partial sums of the down projection), all in a fixed order.
 // out: fp32 [T][H], or bf16 bits [T][H] when out_bf16
-hipError_t launch_combine(const float* D, const int32_t* slot_of_pair, const float* topk_w,
-                          int T, int k, int H, void* out, bool out_bf16, hipStream_t s);
+hipError_t launch_combine(const float* D, int nsplit, int C_b, const int32_t* slot_of_pair,
+                          const float* topk_w, int T, int k, int H, void* out, bool out_bf16,
+                          hipStream_t s);
 
 // dst[p][c] = sum_s src_part[s][slot(p)][c]; rows with mask[p] < 0 are 0
 // (mask may be null).

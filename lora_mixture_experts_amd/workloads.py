@@ -42,6 +42,12 @@ CONFIGS = {
     "prefill": dict(T=6400, H=2880, I=2880, E=32, top_k=4, L=8, r=32),
     "wide": dict(T=64, H=4096, I=11008, E=8, top_k=2, L=8, r=32),
     "many": dict(T=512, H=2880, I=2880, E=32, top_k=4, L=128, r=64),
+    # dense multi-LoRA projection pair (one expert, so routing is trivial):
+    # the pages report that the same work also speeds up dense models such as
+    # Qwen3 32B (AWS post, first section; Korean summary, "Performance
+    # benchmarks and availability"); Qwen3-32B-like MLP dims at decode, one
+    # adapter per request as in "decode"
+    "dense": dict(T=16, H=5120, I=25600, E=1, top_k=1, L=8, r=32),
 }
 CONFIG_SEED = {name: i for i, name in enumerate(CONFIGS)}
 
@@ -136,7 +142,7 @@ def routing_inputs(name: str, dims: dict, seed: int):
     meta = {}
     if name == "tiny":
         ad = rng.integers(-1, 2, size=T)
-    elif name == "decode":
+    elif name in ("decode", "dense"):
         # one token per request, concurrency T; adapter uniform over the L slots
         ad = rng.integers(0, L, size=T)
     elif name == "prefill":

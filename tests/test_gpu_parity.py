@@ -218,6 +218,12 @@ def test_layer_parity_many_sampled(dev):
     check_layer(case, dev, ntok=96, stages=True)
 
 
+def test_layer_parity_dense_sampled(dev):
+    # one expert, top-1: the dense multi-LoRA projection pair
+    log("layer dense")
+    check_layer(build_case("dense"), dev, ntok=4, stages=True)
+
+
 @pytest.mark.parametrize("bm", [(16, 16), (32, 16), (64, 64), (128, 32), (256, 256)])
 def test_layer_block_sizes(dev, bm):
     log(f"layer block sizes {bm}")

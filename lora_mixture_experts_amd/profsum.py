@@ -4,6 +4,9 @@ Two modes, each writing one short markdown file:
 
   stats   from a `rocprofv3 --kernel-trace --stats --output-format csv` run:
           calls and average / min / max duration per kernel.
+  counters  per-kernel averages of whatever counters one or more
+          `rocprofv3 --pmc` runs collected (e.g. MFMA busy cycles, LDS bank
+          conflicts, L2 hits and misses).
   traffic from two `rocprofv3 --pmc FETCH_SIZE` / `--pmc WRITE_SIZE` runs of a
           command that first streams a known number of bytes through HBM
           (bench.py --calibrate-copy MiB): the readings of that reference
@@ -14,6 +17,7 @@ The traffic file ends with a fenced json block that bench.py reads; it records
 a hash of the kernel sources, so the figures are dropped once a kernel changes.
 
   python -m lora_mixture_experts_amd.profsum stats KERNEL_STATS.csv --cmd "..." --out FILE
+  python -m lora_mixture_experts_amd.profsum counters COUNTERS.csv [...] --title T --cmd "..." --out FILE
   python -m lora_mixture_experts_amd.profsum traffic FETCH.csv WRITE.csv --copy-mib N \\
          --workload NAME --cmd "..." --out FILE
 """
@@ -93,6 +97,24 @@ def stats_summary(path: str, cmd: str) -> str:
         lines.append(f"| `{_short(r['Name'])}` | {label(r['Name']) or '-'} | {r['Calls']} | "
                      f"{float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
                      f"{float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.2f} |")
+    return "\n".join(lines) + "\n"
+
+
+def counters_summary(paths, title: str, cmd: str) -> str:
+    vals = defaultdict(lambda: defaultdict(list))
+    for path in paths:
+        for r in csv.DictReader(open(path)):
+            if label(r["Kernel_Name"]) is None:
+                continue
+            vals[_short(r["Kernel_Name"])][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    names = sorted({c for per in vals.values() for c in per})
+    lines = [f"# {title}", "", "Commands (from the repository root):", "", "```", cmd, _self_cmd(), "```", "",
+             f"Kernel sources hash: `{kernel_source_hash()}`", "",
+             "Average per dispatch (summed over the chip's counter instances).", "",
+             "| kernel | " + " | ".join(names) + " |", "|---|" + "---|" * len(names)]
+    for k, per in vals.items():
+        cells = [f"{sum(per[n]) / len(per[n]):.4g}" if per.get(n) else "-" for n in names]
+        lines.append(f"| `{k}` | " + " | ".join(cells) + " |")
     return "\n".join(lines) + "\n"
 
 
@@ -177,6 +199,11 @@ def main():
     s.add_argument("csv")
     s.add_argument("--cmd", required=True)
     s.add_argument("--out", required=True)
+    c = sub.add_parser("counters")
+    c.add_argument("csv", nargs="+")
+    c.add_argument("--title", required=True)
+    c.add_argument("--cmd", required=True)
+    c.add_argument("--out", required=True)
     t = sub.add_parser("traffic")
     t.add_argument("fetch_csv")
     t.add_argument("write_csv")
@@ -187,6 +214,8 @@ def main():
     a = ap.parse_args()
     if a.mode == "stats":
         text = stats_summary(a.csv, a.cmd)
+    elif a.mode == "counters":
+        text = counters_summary(a.csv, a.title, a.cmd)
     else:
         text = traffic_summary(a.fetch_csv, a.write_csv, a.copy_mib, a.workload, a.cmd)
     with open(a.out, "w") as f:

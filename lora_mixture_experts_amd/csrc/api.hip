@@ -2,6 +2,7 @@
 // sequence of the multi-LoRA MoE expert layer (see include/moe_lora.h).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 #include <cstring>
 #include <vector>
@@ -22,6 +23,7 @@ struct Plan {
     int T, H, I, E, k, L, r, P;
     int bm_b, bm_l, C_b, C_l, nblk_b, nblk_l;
     int ksplit;  // K ranges of the down projection (partial sums summed by the combine)
+    int ssplit;  // K ranges of the two shrinks (partials summed by the projection kernels)
     size_t off_ids, off_w, off_sorted_b, off_blk_e_b, off_counts, off_sorted_l, off_blk_e_l,
         off_blk_a_l, off_slot, off_lslot, off_sad, off_defer, off_s1, off_s2, off_h, off_d, total;
 };
@@ -80,6 +82,8 @@ int make_plan(const moe_lora_desc* d, Plan* p) {
     p->nblk_b = p->C_b / p->bm_b;
     p->nblk_l = p->C_l / p->bm_l;
     p->ksplit = gemm_down_ksplit(p->H, p->I, p->bm_b, p->nblk_b);
+    p->ssplit = p->L > 0 ? std::min(shrink_ksplit(p->nblk_l, p->H, p->bm_b),
+                                    shrink_ksplit(p->nblk_l, p->I, p->bm_b)) : 1;
     size_t o = 0;
     auto take = [&](size_t bytes) { const size_t at = o; o += up(bytes); return at; };
     p->off_ids = take(4 * P);
@@ -94,7 +98,7 @@ int make_plan(const moe_lora_desc* d, Plan* p) {
     p->off_lslot = take(4 * P);
     p->off_sad = take(4ul * p->C_b);
     p->off_defer = take(4ul * align_defer_ints(p->E, p->L));
-    const size_t sbytes = p->L > 0 ? 4ul * p->C_b * p->r : 0;
+    const size_t sbytes = p->L > 0 ? 4ul * p->ssplit * p->C_b * p->r : 0;
     p->off_s1 = take(sbytes);
     p->off_s2 = take(sbytes);
     p->off_h = take(2ul * p->C_b * p->I);
@@ -258,7 +262,7 @@ int moe_lora_forward(const moe_lora_desc* d, const moe_lora_weights* w, const vo
     ShrinkArgs sa{};
     sa.top_k = p.k; sa.P = p.P; sa.sorted_l = sorted_l; sa.blk_e_l = blk_e_l;
     sa.blk_a_l = blk_a_l; sa.slot_of_pair = slot; sa.E = p.E; sa.r = p.r; sa.bm_l = p.bm_l;
-    sa.n_blocks = p.nblk_l;
+    sa.n_blocks = p.nblk_l; sa.ksplit = p.ssplit; sa.C_b = p.C_b;
     if (p.L > 0) {
         sa.X = static_cast<const uint16_t*>(x); sa.gather_token = 1; sa.K = p.H;
         sa.A = static_cast<const uint16_t*>(w->a_gate_up); sa.S = s1;
@@ -269,7 +273,7 @@ int moe_lora_forward(const moe_lora_desc* d, const moe_lora_weights* w, const vo
     GemmArgs ga{};
     ga.sorted_b = sorted_b; ga.blk_e_b = blk_e_b; ga.P = p.P; ga.top_k = p.k; ga.bm_b = p.bm_b;
     ga.n_blocks = p.nblk_b; ga.slot_adapter = sad; ga.L = p.L; ga.E = p.E; ga.r = p.r;
-    ga.C_b = p.C_b; ga.h_out = h; ga.d_out = dn; ga.ksplit = 1;
+    ga.C_b = p.C_b; ga.h_out = h; ga.d_out = dn; ga.ksplit = 1; ga.s_split = p.ssplit;
     ga.X = static_cast<const uint16_t*>(x); ga.gate_up = 1;
     ga.W = static_cast<const uint16_t*>(w->w_gate_up); ga.N_out = p.I; ga.K = p.H;
     ga.S = s1; ga.Bl = static_cast<const uint16_t*>(w->b_gate_up);
@@ -314,8 +318,8 @@ int moe_lora_read_stages(const moe_lora_desc* d, const void* workspace, size_t w
         ok(hipMemcpyAsync(topk_w, at<float>(ws, p.off_w), 4ul * p.P, hipMemcpyDeviceToDevice, s));
     const int32_t* lslot = at<int32_t>(ws, p.off_lslot);  // -1 = pair without adapter
     // with L == 0 every mask entry is -1 and the (empty) S buffers are never read
-    if (s1) ok(launch_gather_rows_f32(at<float>(ws, p.off_s1), 1, p.C_b, p.r, slot, lslot, p.P, s1, s));
-    if (s2) ok(launch_gather_rows_f32(at<float>(ws, p.off_s2), 1, p.C_b, p.r, slot, lslot, p.P, s2, s));
+    if (s1) ok(launch_gather_rows_f32(at<float>(ws, p.off_s1), p.ssplit, p.C_b, p.r, slot, lslot, p.P, s1, s));
+    if (s2) ok(launch_gather_rows_f32(at<float>(ws, p.off_s2), p.ssplit, p.C_b, p.r, slot, lslot, p.P, s2, s));
     if (h) ok(launch_gather_rows_bf16(at<uint16_t>(ws, p.off_h), p.I, slot, p.P, h, s));
     if (dn) ok(launch_gather_rows_f32(at<float>(ws, p.off_d), p.ksplit, p.C_b, p.H, slot, nullptr, p.P, dn, s));
     return e == hipSuccess ? MOE_LORA_OK : MOE_LORA_EHIP;

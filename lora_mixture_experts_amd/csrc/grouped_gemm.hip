@@ -40,13 +40,16 @@ __device__ __forceinline__ void load_s_hilo(const GemmArgs& a, int slot, bool in
 #pragma unroll
     for (int q = 0; q < 8; ++q) v[q] = 0.f;
     if (in_run && j0 < a.r) {
-        const float* src = a.S + static_cast<size_t>(slot) * a.r + j0;
-        const f32x4 x0 = *reinterpret_cast<const f32x4*>(src);
-        const f32x4 x1 = *reinterpret_cast<const f32x4*>(src + 4);
+        // the shrink's K-range partials, added in order
+        for (int sp = 0; sp < a.s_split; ++sp) {
+            const float* src = a.S + (static_cast<size_t>(sp) * a.C_b + slot) * a.r + j0;
+            const f32x4 x0 = *reinterpret_cast<const f32x4*>(src);
+            const f32x4 x1 = *reinterpret_cast<const f32x4*>(src + 4);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            v[q] = x0[q];
-            v[4 + q] = x1[q];
+            for (int q = 0; q < 4; ++q) {
+                v[q] += x0[q];
+                v[4 + q] += x1[q];
+            }
         }
     }
     hi = pack_bf16x8(v);

@@ -36,9 +36,13 @@ struct ShrinkArgs {
     const int32_t* slot_of_pair;
     const uint16_t* A;   // [L][E][r][K]
     int E, r, bm_l, n_blocks;
-    float* S;            // [C_b][r]
+    float* S;            // [ksplit][C_b][r]: one partial sum per K range
+    int ksplit, C_b;     // K ranges (workgroups per LoRA block), base-view capacity
 };
 hipError_t launch_shrink(const ShrinkArgs& a, hipStream_t s);
+// K ranges for the shrink: several workgroups per LoRA block when there are
+// few blocks (decode-sized batches), so that more CUs stream the LoRA A.
+int shrink_ksplit(int n_blocks_l, int K, int bm_b);
 
 // ---- grouped expert GEMM with fused LoRA expand (+ SwiGLU) ---------------
 struct GemmArgs {
@@ -53,7 +57,8 @@ struct GemmArgs {
     // LoRA expand
     const int32_t* slot_adapter;  // [C_b] adapter of each base slot, -1 = none / padding
     int L, E, r;
-    const float* S;           // [C_b][r] shrink output (unused when L == 0)
+    const float* S;           // [s_split][C_b][r] shrink partials (unused when L == 0)
+    int s_split;              // number of shrink partials, summed in order on load
     int C_b;
     const uint16_t* Bl;       // gate_up: [L][E][2I][r]; down: [L][E][H][r]
     // outputs

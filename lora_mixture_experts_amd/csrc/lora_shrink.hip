@@ -10,6 +10,8 @@
 // parts are added through LDS in a fixed order: no atomics, no cross-workgroup
 // traffic, and the result is deterministic. Each output element is written
 // once, in base-slot order, for the expand fused into the projection kernel.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -29,9 +31,12 @@ __global__ __launch_bounds__(kShrinkThreads) void k_shrink(ShrinkArgs a) {
     const int nfm = a.bm_l / 16;               // 16-row fragments in the block (1..16)
     const int nkp = kShrinkWaves / nfm;        // K parts per fragment
     const int fm = wave / nkp, kp = wave % nkp;
-    // K in chunks of 64; this wave owns chunks [q0, q1)
-    const int nq = a.K / 64;
-    const int q0 = kp * nq / nkp, q1 = (kp + 1) * nq / nkp;
+    // K in chunks of 64; this workgroup owns chunks [z0, z1) (its K range)
+    // and this wave [q0, q1) of them
+    const int nqa = a.K / 64, z = blockIdx.y;
+    const int z0 = z * nqa / a.ksplit, z1 = (z + 1) * nqa / a.ksplit;
+    const int nq = z1 - z0;
+    const int q0 = z0 + kp * nq / nkp, q1 = z0 + (kp + 1) * nq / nkp;
 
     // A operand row (block row fm*16 + lrow); padding rows re-read the
     // block's first (real) row, merging into the same memory requests, and
@@ -112,15 +117,25 @@ __global__ __launch_bounds__(kShrinkThreads) void k_shrink(ShrinkArgs a) {
         if (j < a.r) {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                if (oslot[i] >= 0) a.S[static_cast<size_t>(oslot[i]) * a.r + j] = v[i];
+                if (oslot[i] >= 0) a.S[(static_cast<size_t>(z) * a.C_b + oslot[i]) * a.r + j] = v[i];
         }
     }
+}
+
+int shrink_ksplit(int n_blocks_l, int K, int bm_b) {
+    // only for long K (each LoRA block then streams a large A on one CU),
+    // few LoRA blocks, and small base blocks (the projection kernels add the
+    // partials when they load S; each partial costs every projection wave a
+    // few loads, so the split stays small)
+    if (bm_b > 32 || n_blocks_l <= 0 || n_blocks_l >= 128 || K < 4096) return 1;
+    return std::max(1, std::min({4, (256 + n_blocks_l - 1) / n_blocks_l, K / 64 / 4}));
 }
 
 hipError_t launch_shrink(const ShrinkArgs& a, hipStream_t s) {
     if (a.n_blocks == 0) return hipSuccess;
     if (a.bm_l < 16 || a.bm_l > 256 || (kShrinkWaves % (a.bm_l / 16)) != 0) return hipErrorInvalidValue;
-    const dim3 grid(a.n_blocks), block(kShrinkThreads);
+    if (a.ksplit < 1 || a.ksplit > a.K / 64) return hipErrorInvalidValue;
+    const dim3 grid(a.n_blocks, a.ksplit), block(kShrinkThreads);
     switch ((a.r + 15) / 16) {
         case 1: hipLaunchKernelGGL(k_shrink<1>, grid, block, 0, s, a); break;
         case 2: hipLaunchKernelGGL(k_shrink<2>, grid, block, 0, s, a); break;

@@ -248,6 +248,25 @@ def test_layer_shapes(dev, i):
     check_layer(case, dev, ntok=dims["T"], stages=True)
 
 
+def test_layer_api_maxima(dev):
+    # E = 1024 (16 logits per lane in the router), top_k = 32 (the largest
+    # choice count), rank 128
+    log("layer maxima")
+    dims = dict(T=24, H=64, I=128, E=1024, top_k=32, L=2, r=128)
+    case = build_case("maxima", dims=dims, seed=77)
+    check_layer(case, dev, ntok=dims["T"], stages=True)
+
+
+def test_layer_foreign_adapter_ids(dev):
+    # ids outside [0, L) mean "no adapter" in the whole layer, not only in
+    # the alignment
+    log("layer foreign adapter ids")
+    case = build_case("decode", touched_only=False)
+    case.adapter_ids[::3] = case.L + 5
+    case.adapter_ids[1::4] = -7
+    check_layer(case, dev, ntok=case.T, stages=True)
+
+
 def test_no_adapter_and_zero_b_agree(dev):
     log("layer no-adapter variants")
     case = build_case("decode", touched_only=False)

@@ -267,10 +267,18 @@ __global__ __launch_bounds__(kAlignThreads) void k_align(
     for (int i = tid; i < zero_n; i += kAlignThreads) zero_buf[i] = 0;
     __syncthreads();
 
-    // 1. per-range key counts (the order of the LDS atomics does not matter)
-    for (int base = tid; base < P; base += kAlignThreads) {
-        const int r = base / R;
-        atomicAdd(&hist[r * nkeys + keyf(base)], 1);
+    // 1. per-range key counts (the order of the LDS atomics does not matter);
+    // 8 keys per thread are loaded before their atomics, so the loads of a
+    // round are in flight together (clamped indices, counted only if valid)
+    for (int base = tid; base < P; base += 8 * kAlignThreads) {
+        int key[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) key[u] = keyf(min(base + u * kAlignThreads, P - 1));
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int p = base + u * kAlignThreads;
+            if (p < P) atomicAdd(&hist[(p / R) * nkeys + key[u]], 1);
+        }
     }
     __syncthreads();
 

@@ -62,7 +62,7 @@ int check_desc(const moe_lora_desc* d) {
     const long P = static_cast<long>(d->T) * d->top_k;
     if (P > (1L << 24)) return MOE_LORA_EINVAL;
     if (static_cast<long>(d->E) * (d->L + 1) > 9712) return MOE_LORA_EINVAL;
-    if (align_hist_waves(d->E, d->L) <= 0) return MOE_LORA_EINVAL;
+    if (!align_fits(d->E, d->L)) return MOE_LORA_EINVAL;
     return MOE_LORA_OK;
 }
 
@@ -211,7 +211,7 @@ int moe_lora_align(const moe_lora_desc* d, const int32_t* topk_ids, const int32_
         return MOE_LORA_EINVAL;
     return launch_align(topk_ids, adapter_ids, p.T, p.k, p.E, p.L, p.bm_b, p.bm_l, p.C_b, p.C_l,
                         sorted_b, blk_e_b, n_b, sorted_l, blk_e_l, blk_a_l, n_l, nullptr,
-                        nullptr, nullptr, nullptr, 0, nullptr, static_cast<hipStream_t>(stream)) == hipSuccess
+                        nullptr, nullptr, nullptr, static_cast<hipStream_t>(stream)) == hipSuccess
                ? MOE_LORA_OK
                : MOE_LORA_EHIP;
 }
@@ -256,7 +256,7 @@ int moe_lora_forward(const moe_lora_desc* d, const moe_lora_weights* w, const vo
     timing_mark(call, 1, s);
     ok(launch_align(ids, adapter_ids, p.T, p.k, p.E, p.L, p.bm_b, p.bm_l, p.C_b, p.C_l, sorted_b,
                     blk_e_b, counts, sorted_l, blk_e_l, blk_a_l, counts + 1, slot, lslot, sad,
-                    nullptr, 0, at<int32_t>(workspace, p.off_defer), s));
+                    at<int32_t>(workspace, p.off_defer), s));
     timing_mark(call, 2, s);
 
     ShrinkArgs sa{};

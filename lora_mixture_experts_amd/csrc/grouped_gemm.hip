@@ -646,18 +646,14 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_dma(GemmArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Tile shapes of the LDS kernel, by block height. Large blocks (many rows per
-// expert) take 256-wide tiles: per unit of work they move the least data from
-// L2 and LDS. The column count may leave a partial last tile.
-#ifndef MOELORA_DMA_CFG
-#define MOELORA_DMA_CFG 3
-#endif
-#ifndef MOELORA_BIG_WM
-#define MOELORA_BIG_WM 2
-#endif
-#ifndef MOELORA_BIG_BNT
-#define MOELORA_BIG_BNT 256
-#endif
+// Launch shapes by block height (rows per block of the base view):
+//   16        skinny: one wave per 16 x 64 tile (gate_up: 32 h columns)
+//   32, 64    tiled:  32 x 128 (1 x 4 waves) and 64 x 128 (2 x 2 waves)
+//   128, 256  direct-load: 128 x 192 and 256 x 192 (2 x 2 waves, 2 stages)
+// These shapes were the fastest of those measured on MI355X for the
+// decode-, many-adapter- and prefill-shaped layers. The column count may
+// leave a partial last tile.
+constexpr int kSkinnyFN = 4;  // 16-column fragments per skinny wave
 
 template <int BM, int BNT, int WM, int WN, int NS>
 static hipError_t launch_dma(const GemmArgs& a, hipStream_t s) {
@@ -689,19 +685,9 @@ bool gemm_supported(int N_out, int K, int gate_up, int bm_b) {
     return bm_b == 32 || bm_b == 64 || bm_b == 128 || bm_b == 256;
 }
 
-#ifndef MOELORA_SKINNY_FN
-#define MOELORA_SKINNY_FN 4
-#endif
-
-// fragments per skinny workgroup: 8 when the column count allows, else 4
-static int skinny_fn(int N_out, int gate_up) {
-    const int cols8 = gate_up ? 64 : 128;
-    return (MOELORA_SKINNY_FN == 8 && N_out % cols8 == 0) ? 8 : 4;
-}
-
 int gemm_down_ksplit(int N_out, int K, int bm_b, int n_blocks) {
     if (bm_b >= 128 || n_blocks <= 0) return 1;
-    const long cols = bm_b == 16 ? 16 * skinny_fn(N_out, 0) : 128;
+    const long cols = bm_b == 16 ? 16 * kSkinnyFN : 128;
     const long waves = (N_out + cols - 1) / cols * n_blocks * (bm_b == 16 ? 1 : 4);
     constexpr long kTargetWaves = 4096;  // about 16 per CU
     constexpr int kMinChunks = 8;        // at least 512 of K per split
@@ -720,35 +706,18 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
     if (a.ksplit < 1 || (a.K / 64) % a.ksplit || (a.ksplit > 1 && (a.gate_up || a.bm_b >= 128)))
         return hipErrorInvalidValue;
     if (a.bm_b == 16) {
-        const int fn = skinny_fn(a.N_out, a.gate_up);
-        const int cols = a.gate_up ? fn * 8 : fn * 16;
+        const int cols = a.gate_up ? kSkinnyFN * 8 : kSkinnyFN * 16;
         if (a.n_blocks > 65535) return hipErrorInvalidValue;
         const dim3 grid(a.N_out / cols, a.n_blocks, a.ksplit), block(64);
-        if (fn == 8) {
-            if (a.gate_up) hipLaunchKernelGGL((k_gemm_skinny<true, 8>), grid, block, 0, s, a);
-            else hipLaunchKernelGGL((k_gemm_skinny<false, 8>), grid, block, 0, s, a);
-        } else {
-            if (a.gate_up) hipLaunchKernelGGL((k_gemm_skinny<true, 4>), grid, block, 0, s, a);
-            else hipLaunchKernelGGL((k_gemm_skinny<false, 4>), grid, block, 0, s, a);
-        }
+        if (a.gate_up) hipLaunchKernelGGL((k_gemm_skinny<true, kSkinnyFN>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((k_gemm_skinny<false, kSkinnyFN>), grid, block, 0, s, a);
         return hipGetLastError();
     }
     switch (a.bm_b) {
         case 32: return launch_tiled<32, 128, 1, 4>(a, s);
         case 64: return launch_tiled<64, 128, 2, 2>(a, s);
-#if MOELORA_DMA_CFG == 1
-        case 128: return launch_dma<128, 192, 2, 2, 3>(a, s);
-        case 256: return launch_dma<256, 256, 2, 2, 2>(a, s);
-#elif MOELORA_DMA_CFG == 2
-        case 128: return launch_dma<128, 256, 2, 2, 3>(a, s);
-        case 256: return launch_dma<256, 128, 4, 2, 3>(a, s);
-#elif MOELORA_DMA_CFG == 3
         case 128: return launch_dma<128, 192, 2, 2, 2>(a, s);
         case 256: return launch_dma<256, 192, 2, 2, 2>(a, s);
-#else
-        case 128: return launch_tiled<128, 192, 2, 2>(a, s);
-        case 256: return launch_tiled<256, MOELORA_BIG_BNT, MOELORA_BIG_WM, 2>(a, s);
-#endif
         default: return hipErrorInvalidValue;
     }
 }

@@ -10,16 +10,16 @@ namespace moelora {
 hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* w,
                         hipStream_t s);
 
-// Largest number of waves whose per-wave key histograms fit the align kernel's
-// LDS for this key count (0 = does not fit).
-int align_hist_waves(int E, int L);
+// Whether the alignment kernel's LDS holds the key counts of E experts x
+// (L adapters + none) together with at least one histogram row.
+bool align_fits(int E, int L);
 
 hipError_t launch_align(const int32_t* topk_ids, const int32_t* adapter_ids, int T, int k,
                         int E, int L, int bm_b, int bm_l, int C_b, int C_l,
                         int32_t* sorted_b, int32_t* blk_e_b, int32_t* n_b,
                         int32_t* sorted_l, int32_t* blk_e_l, int32_t* blk_a_l, int32_t* n_l,
                         int32_t* slot_of_pair, int32_t* lslot_of_pair, int32_t* slot_adapter,
-                        int32_t* zero_buf, int zero_n, int32_t* defer, hipStream_t s);
+                        int32_t* defer, hipStream_t s);
 // ints of scratch the alignment may use to split its scatter off (0 = none)
 int align_defer_ints(int E, int L);
 

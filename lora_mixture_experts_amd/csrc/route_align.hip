@@ -128,7 +128,7 @@ static void align_ranges(int P, int E, int L, int* nr, int* R) {
     *R = r;
 }
 
-int align_hist_waves(int E, int L) { return align_max_ranges(E, L) > 0 ? 1 : 0; }
+bool align_fits(int E, int L) { return align_max_ranges(E, L) > 0; }
 
 __device__ __forceinline__ uint64_t match_key(int key, bool valid, int nbits) {
     uint64_t m = ballot64(valid);
@@ -248,7 +248,7 @@ __global__ __launch_bounds__(kAlignThreads) void k_align(
     AlignKeys keyf, AlignOut o, int T, int bm_b_log2, int bm_l_log2, int C_b, int C_l, int nr,
     int R, int32_t* __restrict__ blk_e_b, int32_t* __restrict__ n_b_out,
     int32_t* __restrict__ blk_e_l, int32_t* __restrict__ blk_a_l, int32_t* __restrict__ n_l_out,
-    int32_t* __restrict__ zero_buf, int zero_n, int32_t* __restrict__ defer) {
+    int32_t* __restrict__ defer) {
     __shared__ int lds[kAlignLdsInts];
     const int E = keyf.E, L = keyf.L, L1 = L + 1;
     const int nkeys = E * L1, nseg = E * L, P = T * keyf.k;
@@ -264,7 +264,6 @@ __global__ __launch_bounds__(kAlignThreads) void k_align(
 
     for (int i = tid; i < nr * nkeys; i += kAlignThreads) hist[i] = 0;
     for (int i = tid; i < E; i += kAlignThreads) ne[i] = 0;
-    for (int i = tid; i < zero_n; i += kAlignThreads) zero_buf[i] = 0;
     __syncthreads();
 
     // 1. per-range key counts (the order of the LDS atomics does not matter);
@@ -397,7 +396,7 @@ hipError_t launch_align(const int32_t* topk_ids, const int32_t* adapter_ids, int
                         int32_t* sorted_b, int32_t* blk_e_b, int32_t* n_b,
                         int32_t* sorted_l, int32_t* blk_e_l, int32_t* blk_a_l, int32_t* n_l,
                         int32_t* slot_of_pair, int32_t* lslot_of_pair, int32_t* slot_adapter,
-                        int32_t* zero_buf, int zero_n, int32_t* defer, hipStream_t s) {
+                        int32_t* defer, hipStream_t s) {
     if (align_max_ranges(E, L) <= 0) return hipErrorInvalidValue;
     if ((bm_b & (bm_b - 1)) || (bm_l & (bm_l - 1))) return hipErrorInvalidValue;
     const int P = T * k;
@@ -412,7 +411,7 @@ hipError_t launch_align(const int32_t* topk_ids, const int32_t* adapter_ids, int
     if (nr <= kAlignThreads / 64 || scatter_lds > 64 * 1024) defer = nullptr;
     hipLaunchKernelGGL(k_align, dim3(1), dim3(kAlignThreads), 0, s, keyf, o, T, __builtin_ctz(bm_b),
                        __builtin_ctz(bm_l), C_b, C_l, nr, R, blk_e_b, n_b, blk_e_l, blk_a_l, n_l,
-                       zero_buf, zero_n, defer);
+                       defer);
     if (defer)
         hipLaunchKernelGGL(k_align_scatter, dim3(nr), dim3(64), scatter_lds, s, keyf, o, T, nr, R,
                            defer);

@@ -1,0 +1,64 @@
+"""Host-side checks of bench.py: the algorithmic byte/flop model, the bound
+selection, and the one-GPU contract (no GPU needed)."""
+import os
+import subprocess
+import sys
+from types import SimpleNamespace
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+
+def small_case():
+    # 4 tokens, top-2 of 3 experts; adapters: 1, none, 0, 1 (L = 2)
+    return SimpleNamespace(name="t", T=4, H=64, I=128, E=3, top_k=2, L=2, r=8,
+                           adapter_ids=np.array([1, -1, 0, 1], np.int32))
+
+
+def test_routing_stats_counts_touched_experts_and_segments():
+    c = small_case()
+    ids = np.array([[0, 1], [2, 0], [1, 2], [0, 1]], np.int32)
+    st = bench.routing_stats(c, ids)
+    # segments (adapter, expert): (1,0), (1,1), (0,1), (0,2); token 1 has none
+    assert st == dict(n_experts=3, n_segments=4, P=8, P_lora=6)
+
+
+def test_algorithmic_model_matches_the_layer_definition():
+    c = small_case()
+    st = dict(n_experts=3, n_segments=4, P=8, P_lora=6)
+    b, f, lb, lf = bench.algorithmic(c, st)
+    H, I, r = c.H, c.I, c.r
+    # projections: 2 flops per multiply-add, base rows for every pair, LoRA
+    # expand for pairs with an adapter
+    assert f["gemm_gate_up"] == 2 * 8 * 2 * I * H + 2 * 6 * 2 * I * r
+    assert f["gemm_down"] == 2 * 8 * H * I + 2 * 6 * H * r
+    # layer: touched base weights (6HI bytes per expert), touched LoRA
+    # (2r(2H+3I) per segment), x, logits, fp32 out
+    assert lb == 3 * 6 * H * I + 4 * 2 * r * (2 * H + 3 * I) + 4 * H * 2 + 4 * 3 * 4 + 4 * H * 4
+    assert lf == 6 * H * I * 8 + 2 * r * (2 * H + 3 * I) * 6
+    # the gate_up kernel streams the touched experts' W_gu once
+    assert b["gemm_gate_up"] >= 3 * 2 * I * H * 2
+
+
+def test_bound_selection_uses_the_ridge_point():
+    assert abs(bench.RIDGE_FLOP_PER_BYTE - 312.5) < 1e-9
+    c = small_case()
+    st = dict(n_experts=3, n_segments=4, P=8, P_lora=6)
+    b, f, lb, lf = bench.algorithmic(c, st)
+    kus = {k: 10.0 for k in ("route", "align", "shrink_gate_up", "gemm_gate_up", "shrink_down",
+                             "gemm_down", "combine")}
+    obj = bench.workload_summary("decode", c, st, 0.05, kus, b, f, lb, lf, [0.05] * 5)
+    assert obj["layer_bound"] == "hbm" and obj["roofline"]["bound"] == "hbm"
+    assert obj["roofline"]["unit"] == "GB/s" and obj["roofline"]["peak"] == 8000.0
+    assert abs(obj["roofline"]["frac"] - obj["roofline"]["achieved"] / 8000.0) < 1e-3
+    assert obj["value"] == round(4 / 0.05e-3, 1)
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr

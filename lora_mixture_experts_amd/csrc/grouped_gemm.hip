@@ -40,15 +40,26 @@ __device__ __forceinline__ void load_s_hilo(const GemmArgs& a, int slot, bool in
 #pragma unroll
     for (int q = 0; q < 8; ++q) v[q] = 0.f;
     if (in_run && j0 < a.r) {
-        // the shrink's K-range partials, added in order
-        for (int sp = 0; sp < a.s_split; ++sp) {
-            const float* src = a.S + (static_cast<size_t>(sp) * a.C_b + slot) * a.r + j0;
-            const f32x4 x0 = *reinterpret_cast<const f32x4*>(src);
-            const f32x4 x1 = *reinterpret_cast<const f32x4*>(src + 4);
+        // the shrink's K-range partials: all loads are issued before the
+        // first add (one memory latency, not one per partial), then they are
+        // added in order 0, 1, ...
+        f32x4 x[kMaxShrinkSplit][2];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                v[q] += x0[q];
-                v[4 + q] += x1[q];
+        for (int sp = 0; sp < kMaxShrinkSplit; ++sp) {
+            if (sp < a.s_split) {
+                const float* src = a.S + (static_cast<size_t>(sp) * a.C_b + slot) * a.r + j0;
+                x[sp][0] = *reinterpret_cast<const f32x4*>(src);
+                x[sp][1] = *reinterpret_cast<const f32x4*>(src + 4);
+            }
+        }
+#pragma unroll
+        for (int sp = 0; sp < kMaxShrinkSplit; ++sp) {
+            if (sp < a.s_split) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    v[q] += x[sp][0][q];
+                    v[4 + q] += x[sp][1][q];
+                }
             }
         }
     }
@@ -705,6 +716,7 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
     if (!gemm_supported(a.N_out, a.K, a.gate_up, a.bm_b)) return hipErrorInvalidValue;
     if (a.ksplit < 1 || (a.K / 64) % a.ksplit || (a.ksplit > 1 && (a.gate_up || a.bm_b >= 128)))
         return hipErrorInvalidValue;
+    if (a.L > 0 && (a.s_split < 1 || a.s_split > kMaxShrinkSplit)) return hipErrorInvalidValue;
     if (a.bm_b == 16) {
         const int cols = a.gate_up ? kSkinnyFN * 8 : kSkinnyFN * 16;
         if (a.n_blocks > 65535) return hipErrorInvalidValue;

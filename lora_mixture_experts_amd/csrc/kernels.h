@@ -42,6 +42,8 @@ struct ShrinkArgs {
 hipError_t launch_shrink(const ShrinkArgs& a, hipStream_t s);
 // K ranges for the shrink: several workgroups per LoRA block when there are
 // few blocks (decode-sized batches), so that more CUs stream the LoRA A.
+// At most kMaxShrinkSplit; the projection kernels add the partials.
+constexpr int kMaxShrinkSplit = 4;
 int shrink_ksplit(int n_blocks_l, int K, int bm_b);
 
 // ---- grouped expert GEMM with fused LoRA expand (+ SwiGLU) ---------------

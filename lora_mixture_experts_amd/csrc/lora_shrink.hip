@@ -138,12 +138,13 @@ __global__ __launch_bounds__(kShrinkThreads) void k_shrink(ShrinkArgs a) {
 }
 
 int shrink_ksplit(int n_blocks_l, int K, int bm_b) {
-    // only for long K (each LoRA block then streams a large A on one CU),
-    // few LoRA blocks, and small base blocks (the projection kernels add the
-    // partials when they load S; each partial costs every projection wave a
-    // few loads, so the split stays small)
+    // Only for long K, few LoRA blocks and small base blocks. A CU streams a
+    // LoRA A at a rate bounded by the loads it can keep in flight, so each
+    // such block's K is cut into ranges on separate CUs (at least 4 chunks
+    // of 64 each). The projection kernels add the partials when they load S;
+    // at K below 4096 that extra load cost as much as the split saved.
     if (bm_b > 32 || n_blocks_l <= 0 || n_blocks_l >= 128 || K < 4096) return 1;
-    return std::max(1, std::min({4, (256 + n_blocks_l - 1) / n_blocks_l, K / 64 / 4}));
+    return std::max(1, std::min({kMaxShrinkSplit, (256 + n_blocks_l - 1) / n_blocks_l, K / 64 / 4}));
 }
 
 hipError_t launch_shrink(const ShrinkArgs& a, hipStream_t s) {

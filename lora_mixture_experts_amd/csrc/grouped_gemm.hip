@@ -40,26 +40,17 @@ __device__ __forceinline__ void load_s_hilo(const GemmArgs& a, int slot, bool in
 #pragma unroll
     for (int q = 0; q < 8; ++q) v[q] = 0.f;
     if (in_run && j0 < a.r) {
-        // the shrink's K-range partials: all loads are issued before the
-        // first add (one memory latency, not one per partial), then they are
-        // added in order 0, 1, ...
-        f32x4 x[kMaxShrinkSplit][2];
+        // the shrink's K-range partials, added in order (a loop, not an
+        // unrolled batch of loads: holding every partial at once costs the
+        // direct-load kernel enough registers to halve its occupancy)
+        for (int sp = 0; sp < a.s_split; ++sp) {
+            const float* src = a.S + (static_cast<size_t>(sp) * a.C_b + slot) * a.r + j0;
+            const f32x4 x0 = *reinterpret_cast<const f32x4*>(src);
+            const f32x4 x1 = *reinterpret_cast<const f32x4*>(src + 4);
 #pragma unroll
-        for (int sp = 0; sp < kMaxShrinkSplit; ++sp) {
-            if (sp < a.s_split) {
-                const float* src = a.S + (static_cast<size_t>(sp) * a.C_b + slot) * a.r + j0;
-                x[sp][0] = *reinterpret_cast<const f32x4*>(src);
-                x[sp][1] = *reinterpret_cast<const f32x4*>(src + 4);
-            }
-        }
-#pragma unroll
-        for (int sp = 0; sp < kMaxShrinkSplit; ++sp) {
-            if (sp < a.s_split) {
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    v[q] += x[sp][0][q];
-                    v[4 + q] += x[sp][1][q];
-                }
+            for (int q = 0; q < 4; ++q) {
+                v[q] += x0[q];
+                v[4 + q] += x1[q];
             }
         }
     }

@@ -42,7 +42,7 @@ def lib():
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is missing: build it first "
-                               "(python -c 'import __graft_entry__ as g; g.build()')")
+                               "(python -m lora_mixture_experts_amd.build)")
         L = ctypes.CDLL(LIB_PATH)
         P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
         pD, pW = ctypes.POINTER(Desc), ctypes.POINTER(Weights)

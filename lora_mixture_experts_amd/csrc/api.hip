@@ -25,7 +25,9 @@ struct Plan {
     int ksplit;  // K ranges of the down projection (partial sums summed by the combine)
     int ssplit;  // K ranges of the two shrinks (partials summed by the projection kernels)
     size_t off_ids, off_w, off_sorted_b, off_blk_e_b, off_counts, off_sorted_l, off_blk_e_l,
-        off_blk_a_l, off_slot, off_lslot, off_sad, off_defer, off_s1, off_s2, off_h, off_d, total;
+        off_blk_a_l, off_slot, off_lslot, off_sad, off_defer, off_s1, off_s2, off_s1hl, off_s2hl,
+        off_h, off_d, total;
+    bool s_hl;  // the direct-load projection kernels take S as bf16 hi/lo rows
 };
 
 int roundup_i(long v, long m) { return static_cast<int>((v + m - 1) / m * m); }
@@ -100,6 +102,12 @@ int make_plan(const moe_lora_desc* d, Plan* p) {
     const size_t sbytes = p->L > 0 ? 4ul * p->ssplit * p->C_b * p->r : 0;
     p->off_s1 = take(sbytes);
     p->off_s2 = take(sbytes);
+    // the direct-load kernels (128- and 256-row blocks, never a split shrink)
+    // run the expand in their pipeline from a bf16 hi/lo copy of S
+    p->s_hl = p->L > 0 && p->bm_b >= 128 && p->ssplit == 1;
+    const size_t hlbytes = p->s_hl ? 2ul * p->C_b * s_hl_stride_of(p->r) : 0;
+    p->off_s1hl = take(hlbytes);
+    p->off_s2hl = take(hlbytes);
     p->off_h = take(2ul * p->C_b * p->I);
     p->off_d = take(4ul * p->ksplit * p->C_b * p->H);
     p->total = o;
@@ -262,9 +270,12 @@ int moe_lora_forward(const moe_lora_desc* d, const moe_lora_weights* w, const vo
     sa.top_k = p.k; sa.P = p.P; sa.sorted_l = sorted_l; sa.blk_e_l = blk_e_l;
     sa.blk_a_l = blk_a_l; sa.slot_of_pair = slot; sa.E = p.E; sa.r = p.r; sa.bm_l = p.bm_l;
     sa.n_blocks = p.nblk_l; sa.ksplit = p.ssplit; sa.C_b = p.C_b;
+    sa.s_hl_stride = s_hl_stride_of(p.r);
+    uint16_t* s1hl = p.s_hl ? at<uint16_t>(workspace, p.off_s1hl) : nullptr;
+    uint16_t* s2hl = p.s_hl ? at<uint16_t>(workspace, p.off_s2hl) : nullptr;
     if (p.L > 0) {
         sa.X = static_cast<const uint16_t*>(x); sa.gather_token = 1; sa.K = p.H;
-        sa.A = static_cast<const uint16_t*>(w->a_gate_up); sa.S = s1;
+        sa.A = static_cast<const uint16_t*>(w->a_gate_up); sa.S = s1; sa.S_hl = s1hl;
         ok(launch_shrink(sa, s));
     }
     timing_mark(call, 3, s);
@@ -276,18 +287,20 @@ int moe_lora_forward(const moe_lora_desc* d, const moe_lora_weights* w, const vo
     ga.X = static_cast<const uint16_t*>(x); ga.gate_up = 1;
     ga.W = static_cast<const uint16_t*>(w->w_gate_up); ga.N_out = p.I; ga.K = p.H;
     ga.S = s1; ga.Bl = static_cast<const uint16_t*>(w->b_gate_up);
+    ga.S_hl = s1hl; ga.s_hl_stride = s_hl_stride_of(p.r);
     ok(launch_gemm(ga, s));
     timing_mark(call, 4, s);
 
     if (p.L > 0) {
         sa.X = h; sa.gather_token = 0; sa.K = p.I;
-        sa.A = static_cast<const uint16_t*>(w->a_down); sa.S = s2;
+        sa.A = static_cast<const uint16_t*>(w->a_down); sa.S = s2; sa.S_hl = s2hl;
         ok(launch_shrink(sa, s));
     }
     timing_mark(call, 5, s);
 
     ga.X = h; ga.gate_up = 0; ga.W = static_cast<const uint16_t*>(w->w_down); ga.N_out = p.H;
     ga.K = p.I; ga.S = s2; ga.Bl = static_cast<const uint16_t*>(w->b_down); ga.ksplit = p.ksplit;
+    ga.S_hl = s2hl;
     ok(launch_gemm(ga, s));
     timing_mark(call, 6, s);
 

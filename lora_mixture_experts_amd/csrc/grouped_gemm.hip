@@ -260,10 +260,13 @@ static inline int tiled_grid(int n_blocks, int n_tiles) {
 template <int FM, int FN, bool GATEUP, typename WRowOf>
 __device__ __forceinline__ void tile_epilogue(const GemmArgs& a, f32x4 (&acc)[FM][FN], bool wlive,
                                               int wrow_base, int wn, int c0, int e, int kc,
-                                              int lrow, WRowOf wrow_of, int z = 0) {
+                                              int lrow, WRowOf wrow_of, int z = 0,
+                                              bool expand = true) {
     if (!wlive) return;
     const int Nw = GATEUP ? 2 * a.N_out : a.N_out;
-    if (a.L > 0 && z == 0) {  // the LoRA term is added once, by the first K range
+    // the LoRA term is added once, by the first K range, unless the pipeline
+    // already added it
+    if (a.L > 0 && z == 0 && expand) {
         int my_a[FM];
         bool pending[FM];
 #pragma unroll
@@ -547,6 +550,11 @@ __device__ __forceinline__ void dma_step(const DmaCtx<FM, FN, A_PW, B_PW>& c, f3
     }
 }
 
+// adapter runs per tile that the direct-load kernel expands inside its
+// pipeline, and the zero row its LoRA stages read for rows outside a run
+constexpr int kMaxPipeRuns = 4;
+__device__ __attribute__((aligned(128))) uint16_t g_zero_row[64] = {};
+
 template <int BM, int BNT, int WM, int WN, int NS, bool GATEUP>
 __global__ __launch_bounds__(64 * WM * WN) void k_gemm_dma(GemmArgs a) {
     constexpr int NW = WM * WN;
@@ -620,31 +628,115 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_dma(GemmArgs a) {
         for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int nk = K / 64;
+
+    // LoRA expand as extra pipeline stages. The tile's rows hold one expert
+    // and are ordered by adapter, so the adapters form runs. For each run
+    // (up to kMaxPipeRuns) the pipeline appends s_hl_stride / 64 stages whose
+    // A rows are the run's rows of S as bf16 [hi | lo | zeros] (other rows
+    // read a zero row) and whose B rows are the run's LoRA B rows, each read
+    // twice (once against hi, once against lo): the same MFMAs as the
+    // epilogue expand, now fed through LDS with their loads in flight while
+    // earlier stages multiply. Tiles with more runs use the epilogue.
+    int nruns = 0, run0 = 0, run1 = 0, run2 = 0, run3 = 0;
+    bool pipe_expand = false;
+    int row_ad[A_PW];
+#pragma unroll
+    for (int i = 0; i < A_PW; ++i) row_ad[i] = -1;
+    if (a.L > 0 && a.S_hl != nullptr) {
+        constexpr int RPL = BM / 64;  // tile rows per lane
+        int adq[RPL];
+#pragma unroll
+        for (int q = 0; q < RPL; ++q) adq[q] = a.slot_adapter[row0 + 64 * q + lane];
+        uint64_t starts[RPL];
+        int total = 0;
+#pragma unroll
+        for (int q = 0; q < RPL; ++q) {
+            int prev = __shfl(adq[q], (lane + 63) & 63);
+            const int carry = q > 0 ? __shfl(adq[q > 0 ? q - 1 : 0], 63) : -2;
+            if (lane == 0) prev = carry;
+            starts[q] = ballot64(adq[q] >= 0 && adq[q] != prev);
+            total += __popcll(starts[q]);
+        }
+        if (total <= kMaxPipeRuns) {
+            pipe_expand = true;
+#pragma unroll
+            for (int q = 0; q < RPL; ++q) {
+                uint64_t m = starts[q];
+                while (m) {
+                    const int v = __shfl(adq[q], __ffsll(static_cast<long long>(m)) - 1);
+                    if (nruns == 0) run0 = v;
+                    else if (nruns == 1) run1 = v;
+                    else if (nruns == 2) run2 = v;
+                    else run3 = v;
+                    ++nruns;
+                    m &= m - 1;
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < A_PW; ++i) {
+                const int r = 8 * (wave * A_PW + i) + lr;  // 8 rows of one 64-row group
+                const int qi = (8 * (wave * A_PW + i)) / 64;
+                int v = adq[0];
+#pragma unroll
+                for (int q = 1; q < RPL; ++q)
+                    if (q == qi) v = adq[q];
+                row_ad[i] = __shfl(v, r & 63);
+            }
+        }
+    }
+    const int spr = pipe_expand ? a.s_hl_stride / 64 : 0;  // stages per run
+    const int nk_all = nk + nruns * spr;
+    auto issue = [&](int stage, uint16_t* ab, uint16_t* bb) {
+        if (stage < nk) {
+            dma_issue<A_PW, B_PW>(asrc, bsrc, ab, bb, wave, stage * 64);
+            return;
+        }
+        const int t = stage - nk, q = t / spr, sub = t - q * spr;
+        const int ad = q == 0 ? run0 : q == 1 ? run1 : q == 2 ? run2 : run3;
+#pragma unroll
+        for (int i = 0; i < A_PW; ++i) {
+            const int r = 8 * (wave * A_PW + i) + lr;
+            const int c = pc ^ (r & 7);
+            const uint16_t* src = row_ad[i] == ad
+                                      ? a.S_hl + static_cast<size_t>(row0 + r) * a.s_hl_stride + sub * 64 + c * 8
+                                      : g_zero_row + c * 8;
+            dma16(src, ab + (wave * A_PW + i) * 512);
+        }
+#pragma unroll
+        for (int i = 0; i < B_PW; ++i) {
+            const int r = 8 * (wave * B_PW + i) + lr;
+            const int c = pc ^ (r & 7);
+            const int j0 = (sub * 64 + c * 8) & (a.r - 1);
+            dma16(a.Bl + (static_cast<size_t>(ad * a.E + e) * Nw + wrow_of(r)) * a.r + j0,
+                  bb + (wave * B_PW + i) * 512);
+        }
+    };
+
     DmaCtx<FM, FN, A_PW, B_PW> ctx{asrc, bsrc, wave, wm * (BM / WM), wn * (BNT / WN), kc, lrow, wlive};
     uint16_t* const abufs[3] = {As0, As1, As2};
     uint16_t* const bbufs[3] = {Bs0, Bs1, Bs2};
 #pragma unroll
     for (int s = 0; s < NS - 1; ++s)
-        if (s < nk) dma_issue<A_PW, B_PW>(ctx.asrc, ctx.bsrc, abufs[s], bbufs[s], wave, s * 64);
+        if (s < nk_all) issue(s, abufs[s], bbufs[s]);
     // one pipeline step: stage k (buffer k % NS) is complete for this wave once
     // at most the loads of the stage requested after it are in flight; the
     // barrier then makes every wave's part visible and frees the buffer that
     // the next request overwrites (it was multiplied one step earlier)
-    for (int k = 0; k < nk; k += NS) {
+    for (int k = 0; k < nk_all; k += NS) {
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
-            if (k + s >= nk) break;
-            if (k + s + 1 < nk)
+            if (k + s >= nk_all) break;
+            if (k + s + 1 < nk_all)
                 wait_vmcnt<(NS - 2) * LPS>();
             else
                 wait_vmcnt<0>();
             bare_barrier();
-            dma_step(ctx, acc, abufs[s], bbufs[s], abufs[(s + NS - 1) % NS], bbufs[(s + NS - 1) % NS],
-                     k + s + NS - 1 < nk ? (k + s + NS - 1) * 64 : -1);
+            if (k + s + NS - 1 < nk_all) issue(k + s + NS - 1, abufs[(s + NS - 1) % NS], bbufs[(s + NS - 1) % NS]);
+            dma_step(ctx, acc, abufs[s], bbufs[s], abufs[(s + NS - 1) % NS], bbufs[(s + NS - 1) % NS], -1);
         }
     }
 
-    tile_epilogue<FM, FN, GATEUP>(a, acc, wlive, wrow_base, wn, c0, e, kc, lrow, wrow_of);
+    tile_epilogue<FM, FN, GATEUP>(a, acc, wlive, wrow_base, wn, c0, e, kc, lrow, wrow_of, 0, !pipe_expand);
 }
 
 // ---------------------------------------------------------------------------
@@ -708,6 +800,8 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
     if (a.ksplit < 1 || (a.K / 64) % a.ksplit || (a.ksplit > 1 && (a.gate_up || a.bm_b >= 128)))
         return hipErrorInvalidValue;
     if (a.L > 0 && (a.s_split < 1 || a.s_split > kMaxShrinkSplit)) return hipErrorInvalidValue;
+    if (a.L > 0 && a.S_hl && (a.s_split != 1 || a.s_hl_stride != s_hl_stride_of(a.r)))
+        return hipErrorInvalidValue;
     if (a.bm_b == 16) {
         const int cols = a.gate_up ? kSkinnyFN * 8 : kSkinnyFN * 16;
         if (a.n_blocks > 65535) return hipErrorInvalidValue;

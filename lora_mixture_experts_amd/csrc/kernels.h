@@ -38,7 +38,13 @@ struct ShrinkArgs {
     int E, r, bm_l, n_blocks;
     float* S;            // [ksplit][C_b][r]: one partial sum per K range
     int ksplit, C_b;     // K ranges (workgroups per LoRA block), base-view capacity
+    // optional (ksplit == 1 only): S again as bf16 rows [C_b][s_hl_stride] =
+    // hi parts (r), lo parts (r), zeros; hi + lo carries S to about 2^-16
+    uint16_t* S_hl;
+    int s_hl_stride;
 };
+// Row length (elements) of the bf16 hi/lo copy of S: whole 64-wide K steps.
+inline int s_hl_stride_of(int r) { return 2 * r < 64 ? 64 : 2 * r; }
 hipError_t launch_shrink(const ShrinkArgs& a, hipStream_t s);
 // K ranges for the shrink: several workgroups per LoRA block when there are
 // few blocks (decode-sized batches), so that more CUs stream the LoRA A.
@@ -67,6 +73,10 @@ struct GemmArgs {
     uint16_t* h_out;          // [C_b][I]
     float* d_out;             // [ksplit][C_b][H] partial sums over K ranges (down)
     int ksplit;               // down only: the K range is cut into ksplit equal parts
+    // optional bf16 hi/lo copy of S (see ShrinkArgs); the direct-load kernel
+    // then runs the expand as extra stages of its LDS pipeline
+    const uint16_t* S_hl;
+    int s_hl_stride;
 };
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
 // Whether a tile configuration exists for these sizes.

@@ -134,6 +134,26 @@ __global__ __launch_bounds__(kShrinkThreads) void k_shrink(ShrinkArgs a) {
                     if (oslot[i] >= 0) a.S[(static_cast<size_t>(z) * a.C_b + oslot[i]) * a.r + j] = acc[fn][i];
             }
         }
+        if (a.S_hl) {
+            // the bf16 copy: hi = bf16(s), lo = bf16(s - hi), then zeros to
+            // the row end (only when 2r is below one 64-wide K step)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if (oslot[i] < 0) continue;
+                uint16_t* row = a.S_hl + static_cast<size_t>(oslot[i]) * a.s_hl_stride;
+#pragma unroll
+                for (int fn = 0; fn < FN; ++fn) {
+                    const int j = fn * 16 + lrow;
+                    if (j < a.r) {
+                        const uint16_t hi = f32_to_bf16_rne(acc[fn][i]);
+                        row[j] = hi;
+                        row[a.r + j] = f32_to_bf16_rne(acc[fn][i] - bf16_to_f32(hi));
+                        if constexpr (FN == 1)
+                            for (int q = 2 * a.r + j; q < a.s_hl_stride; q += a.r) row[q] = 0;
+                    }
+                }
+            }
+        }
     }
 }
 
@@ -151,6 +171,7 @@ hipError_t launch_shrink(const ShrinkArgs& a, hipStream_t s) {
     if (a.n_blocks == 0) return hipSuccess;
     if (a.bm_l < 16 || a.bm_l > 256 || (a.bm_l & (a.bm_l - 1))) return hipErrorInvalidValue;
     if (a.ksplit < 1 || a.ksplit > a.K / 64) return hipErrorInvalidValue;
+    if (a.S_hl && (a.ksplit != 1 || a.s_hl_stride != s_hl_stride_of(a.r))) return hipErrorInvalidValue;
     const dim3 grid(a.n_blocks, a.ksplit), block(kShrinkThreads);
     switch ((a.r + 15) / 16) {
         case 1: hipLaunchKernelGGL(k_shrink<1>, grid, block, 0, s, a); break;

@@ -232,6 +232,22 @@ def test_layer_block_sizes(dev, bm):
     check_layer(case, dev, ntok=150, bm=bm, stages=True)
 
 
+@pytest.mark.parametrize("r,L,bm,pure", [(8, 3, 128, False), (64, 3, 128, True), (128, 2, 256, False),
+                                          (32, 6, 128, False), (16, 7, 256, True)])
+def test_pipeline_expand(dev, r, L, bm, pure):
+    # 128- and 256-row blocks run the LoRA expand as extra stages of their
+    # LDS pipeline when a tile holds at most 4 adapter runs (L <= 3 here) and
+    # in the epilogue otherwise (L = 6, 7: tiles with more runs); pure: base
+    # weights zero, so the output is the LoRA path alone
+    log(f"pipeline expand r={r} L={L} bm={bm} pure={pure}")
+    dims = dict(T=300, H=128, I=192, E=2, top_k=1, L=L, r=r)
+    case = build_case(f"pipe{r}_{L}", dims=dims, seed=60 + r + L)
+    if pure:
+        case.w_gate_up[:] = 0
+        case.w_down[:] = 0
+    check_layer(case, dev, ntok=dims["T"], bm=(bm, 16), stages=True)
+
+
 RANDOM_DIMS = [dict(T=1, H=64, I=64, E=1, top_k=1, L=1, r=8),
                dict(T=3, H=128, I=64, E=4, top_k=4, L=2, r=16),
                dict(T=33, H=64, I=192, E=9, top_k=2, L=4, r=64),

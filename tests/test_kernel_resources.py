@@ -31,6 +31,7 @@ MIN_OCCUPANCY = {
     "k_gemm_dma<256, 192, 2, 2, 2, true>": 1,
     "k_gemm_dma<256, 192, 2, 2, 2, false>": 1,
 }
+MIN_OCCUPANCY_SHRINK = {"k_shrink<1>": 8, "k_shrink<2>": 5, "k_shrink<4>": 3, "k_shrink<8>": 1}
 
 
 def _demangle(names):
@@ -82,3 +83,12 @@ def test_projection_kernels_keep_their_occupancy(reports):
         for v in hits:
             got = v.get("Occupancy")  # waves per SIMD
             assert got is not None and got >= want, (name, v)
+
+
+def test_shrink_kernels_keep_their_occupancy(reports):
+    rep = reports["lora_shrink.hip"]
+    for name, want in MIN_OCCUPANCY_SHRINK.items():
+        hits = [v for k, v in rep.items() if k.startswith(name)]
+        assert hits, f"{name} not found among {sorted(rep)}"
+        for v in hits:
+            assert v.get("Occupancy", 0) >= want, (name, v)

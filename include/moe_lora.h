@@ -48,9 +48,16 @@ extern "C" {
  *   H and I must be multiples of 64.
  *   block_m_base / block_m_lora: rows per block of the two alignment views;
  *   0 = library default; else a power of two in [16, 256].
- *   flags: 0, or MOE_LORA_FLAG_OUT_BF16 (out is bf16, rounded to nearest even
- *   from the fp32 sum); any other bit is an error. */
+ *   flags: a combination of
+ *     MOE_LORA_FLAG_OUT_BF16        out is bf16, rounded to nearest even from
+ *                                   the fp32 sum
+ *     MOE_LORA_FLAG_SHRINK_LAUNCH   run the two LoRA shrinks as launches of
+ *                                   their own even where the library would run
+ *                                   them inside the projection launches (for
+ *                                   comparison; the results agree to rounding)
+ *   any other bit is an error. */
 #define MOE_LORA_FLAG_OUT_BF16 1
+#define MOE_LORA_FLAG_SHRINK_LAUNCH 2
 typedef struct moe_lora_desc {
     int32_t T, H, I, E, top_k, L, r;
     int32_t block_m_base, block_m_lora;
@@ -129,7 +136,13 @@ int moe_lora_align(const moe_lora_desc *d, const int32_t *topk_ids, const int32_
  *               this call until the next call that uses it.
  * The gate_up and down LoRA expands add into the base projections' results
  * inside the projection kernels (AWS post, section "Kernel optimizations":
- * the LoRA add is fused into the expand). */
+ * the LoRA add is fused into the expand). With 16-row base blocks (few rows
+ * per expert, the default when T*top_k/E <= 8) the LoRA shrinks run inside
+ * the projection launches too, as producer waves beside the base weight
+ * stream; the projection waves wait for them, by polling a counter in the
+ * workspace, only before their expand. Such a wait is bounded (about a second
+ * of polling): if it ever ran out, the output would be undefined, but every
+ * wave still ends. */
 int moe_lora_forward(const moe_lora_desc *d, const moe_lora_weights *w, const void *x,
                      const float *logits, const int32_t *adapter_ids, void *out,
                      void *workspace, size_t ws_bytes, void *stream);
@@ -157,7 +170,9 @@ int moe_lora_read_alignment(const moe_lora_desc *d, const void *workspace, size_
  * record HIP events around each of their kernels on their stream (n = 0 turns
  * it off). moe_lora_timing_read synchronises those events and returns the
  * summed milliseconds per kernel (ms[i], i < MOE_LORA_NKERNELS, in the order
- * of moe_lora_kernel_name) and the number of calls recorded, then resets. */
+ * of moe_lora_kernel_name) and the number of calls recorded, then resets. A
+ * kernel that the calls did not launch reports 0: the shrinks when they ran
+ * inside the projection launches, or when L == 0. */
 #define MOE_LORA_NKERNELS 7
 int moe_lora_timing_enable(int32_t max_calls);
 int moe_lora_timing_read(float *ms, int32_t *ncalls);

@@ -24,6 +24,7 @@ struct Plan {
     int bm_b, bm_l, C_b, C_l, nblk_b, nblk_l;
     int ksplit;  // K ranges of the down projection (partial sums summed by the combine)
     int ssplit;  // K ranges of the two shrinks (partials summed by the projection kernels)
+    bool fused;  // the shrinks run as producer waves inside the projection launches
     size_t off_ids, off_w, off_sorted_b, off_blk_e_b, off_counts, off_sorted_l, off_blk_e_l,
         off_blk_a_l, off_slot, off_lslot, off_sad, off_defer, off_s1, off_s2, off_s1hl, off_s2hl,
         off_h, off_d, total;
@@ -57,7 +58,7 @@ int check_desc(const moe_lora_desc* d) {
     if (d->E > 1024 || d->top_k < 1 || d->top_k > d->E || d->top_k > 32) return MOE_LORA_EINVAL;
     if (d->L > 0 && !(d->r == 8 || d->r == 16 || d->r == 32 || d->r == 64 || d->r == 128))
         return MOE_LORA_EINVAL;
-    if (d->flags & ~MOE_LORA_FLAG_OUT_BF16) return MOE_LORA_EINVAL;
+    if (d->flags & ~(MOE_LORA_FLAG_OUT_BF16 | MOE_LORA_FLAG_SHRINK_LAUNCH)) return MOE_LORA_EINVAL;
     if (d->block_m_base != 0 && !pow2_in(d->block_m_base, 16, 256)) return MOE_LORA_EINVAL;
     if (d->block_m_lora != 0 && !pow2_in(d->block_m_lora, 16, 256)) return MOE_LORA_EINVAL;
     const long P = static_cast<long>(d->T) * d->top_k;
@@ -83,8 +84,14 @@ int make_plan(const moe_lora_desc* d, Plan* p) {
     p->nblk_b = p->C_b / p->bm_b;
     p->nblk_l = p->C_l / p->bm_l;
     p->ksplit = gemm_down_ksplit(p->H, p->I, p->bm_b, p->nblk_b);
-    p->ssplit = p->L > 0 ? std::min(shrink_ksplit(p->nblk_l, p->H, p->bm_b),
-                                    shrink_ksplit(p->nblk_l, p->I, p->bm_b)) : 1;
+    // 16-row base blocks (few rows per expert: the projections stream their
+    // weights) run the shrinks inside the projection launches
+    p->fused = p->L > 0 && p->bm_b == 16 && !(d->flags & MOE_LORA_FLAG_SHRINK_LAUNCH);
+    if (p->fused)
+        p->ssplit = std::max(producer_ksplit(p->H), producer_ksplit(p->I));
+    else
+        p->ssplit = p->L > 0 ? std::min(shrink_ksplit(p->nblk_l, p->H, p->bm_b),
+                                        shrink_ksplit(p->nblk_l, p->I, p->bm_b)) : 1;
     size_t o = 0;
     auto take = [&](size_t bytes) { const size_t at = o; o += up(bytes); return at; };
     p->off_ids = take(4 * P);
@@ -137,7 +144,8 @@ const char* kKernelNames[MOE_LORA_NKERNELS] = {"route", "align", "shrink_gate_up
 struct Timing {
     int max_calls = 0;
     int ncalls = 0;
-    std::vector<hipEvent_t> ev;  // [max_calls][NKERNELS + 1]
+    std::vector<hipEvent_t> ev;        // [max_calls][NKERNELS + 1]
+    std::vector<uint8_t> launched;     // [max_calls][NKERNELS]: whether the call launched kernel i
 } g_timing;
 
 void timing_mark(int call, int i, hipStream_t s) {
@@ -254,12 +262,19 @@ int moe_lora_forward(const moe_lora_desc* d, const moe_lora_weights* w, const vo
     float* dn = at<float>(workspace, p.off_d);
 
     int call = -1;
-    if (g_timing.max_calls > 0 && g_timing.ncalls < g_timing.max_calls) call = g_timing.ncalls++;
+    if (g_timing.max_calls > 0 && g_timing.ncalls < g_timing.max_calls) {
+        call = g_timing.ncalls++;
+        const bool shrink_launched = p.L > 0 && !p.fused;
+        uint8_t* l = &g_timing.launched[static_cast<size_t>(call) * MOE_LORA_NKERNELS];
+        l[2] = l[4] = shrink_launched ? 1 : 0;  // shrink_gate_up, shrink_down
+    }
 
     hipError_t e = hipSuccess;
     auto ok = [&](hipError_t v) { if (e == hipSuccess) e = v; };
     timing_mark(call, 0, s);
-    ok(launch_route(logits, p.T, p.E, p.k, ids, tw, s));
+    // counts[0..1]: n_b, n_l (alignment); counts[2..3]: producer counts of
+    // the two projections, zeroed by the routing launch
+    ok(launch_route(logits, p.T, p.E, p.k, ids, tw, s, counts + 2, 2));
     timing_mark(call, 1, s);
     ok(launch_align(ids, adapter_ids, p.T, p.k, p.E, p.L, p.bm_b, p.bm_l, p.C_b, p.C_l, sorted_b,
                     blk_e_b, counts, sorted_l, blk_e_l, blk_a_l, counts + 1, slot, lslot, sad,
@@ -273,7 +288,7 @@ int moe_lora_forward(const moe_lora_desc* d, const moe_lora_weights* w, const vo
     sa.s_hl_stride = s_hl_stride_of(p.r);
     uint16_t* s1hl = p.s_hl ? at<uint16_t>(workspace, p.off_s1hl) : nullptr;
     uint16_t* s2hl = p.s_hl ? at<uint16_t>(workspace, p.off_s2hl) : nullptr;
-    if (p.L > 0) {
+    if (p.L > 0 && !p.fused) {
         sa.X = static_cast<const uint16_t*>(x); sa.gather_token = 1; sa.K = p.H;
         sa.A = static_cast<const uint16_t*>(w->a_gate_up); sa.S = s1; sa.S_hl = s1hl;
         ok(launch_shrink(sa, s));
@@ -288,10 +303,17 @@ int moe_lora_forward(const moe_lora_desc* d, const moe_lora_weights* w, const vo
     ga.W = static_cast<const uint16_t*>(w->w_gate_up); ga.N_out = p.I; ga.K = p.H;
     ga.S = s1; ga.Bl = static_cast<const uint16_t*>(w->b_gate_up);
     ga.S_hl = s1hl; ga.s_hl_stride = s_hl_stride_of(p.r);
+    if (p.fused) {
+        ga.prod_ncf = (p.r + 15) / 16;
+        ga.prod_units = p.nblk_l * ga.prod_ncf * p.ssplit;
+        ga.gather_token = 1; ga.sorted_l = sorted_l; ga.blk_e_l = blk_e_l; ga.blk_a_l = blk_a_l;
+        ga.slot_of_pair = slot; ga.Al = static_cast<const uint16_t*>(w->a_gate_up);
+        ga.bm_l = p.bm_l; ga.S_out = s1; ga.done = counts + 2; ga.n_l = counts + 1;
+    }
     ok(launch_gemm(ga, s));
     timing_mark(call, 4, s);
 
-    if (p.L > 0) {
+    if (p.L > 0 && !p.fused) {
         sa.X = h; sa.gather_token = 0; sa.K = p.I;
         sa.A = static_cast<const uint16_t*>(w->a_down); sa.S = s2; sa.S_hl = s2hl;
         ok(launch_shrink(sa, s));
@@ -301,6 +323,10 @@ int moe_lora_forward(const moe_lora_desc* d, const moe_lora_weights* w, const vo
     ga.X = h; ga.gate_up = 0; ga.W = static_cast<const uint16_t*>(w->w_down); ga.N_out = p.H;
     ga.K = p.I; ga.S = s2; ga.Bl = static_cast<const uint16_t*>(w->b_down); ga.ksplit = p.ksplit;
     ga.S_hl = s2hl;
+    if (p.fused) {
+        ga.gather_token = 0; ga.Al = static_cast<const uint16_t*>(w->a_down);
+        ga.S_out = s2; ga.done = counts + 3;
+    }
     ok(launch_gemm(ga, s));
     timing_mark(call, 6, s);
 
@@ -370,6 +396,7 @@ int moe_lora_timing_enable(int32_t max_calls) {
     g_timing.max_calls = 0;
     if (max_calls <= 0) return MOE_LORA_OK;
     g_timing.ev.resize(static_cast<size_t>(max_calls) * (MOE_LORA_NKERNELS + 1));
+    g_timing.launched.assign(static_cast<size_t>(max_calls) * MOE_LORA_NKERNELS, 1);
     for (auto& ev : g_timing.ev)
         if (hipEventCreate(&ev) != hipSuccess) return MOE_LORA_EHIP;
     g_timing.max_calls = max_calls;
@@ -384,6 +411,9 @@ int moe_lora_timing_read(float* ms, int32_t* ncalls) {
         hipEvent_t* ev = &g_timing.ev[static_cast<size_t>(c) * (MOE_LORA_NKERNELS + 1)];
         if (hipEventSynchronize(ev[MOE_LORA_NKERNELS]) != hipSuccess) return MOE_LORA_EHIP;
         for (int i = 0; i < MOE_LORA_NKERNELS; ++i) {
+            // a kernel the call did not launch reports 0 (its marks enclose
+            // only the events' own overhead)
+            if (!g_timing.launched[static_cast<size_t>(c) * MOE_LORA_NKERNELS + i]) continue;
             float t = 0.f;
             if (hipEventElapsedTime(&t, ev[i], ev[i + 1]) != hipSuccess) return MOE_LORA_EHIP;
             ms[i] += t;

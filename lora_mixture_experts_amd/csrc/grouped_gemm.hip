@@ -17,6 +17,7 @@
 // SwiGLU epilogue h = silu(gate) * up runs in registers; h is stored in bf16.
 // down: the fp32 result is stored per base slot for the weighted combine.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 #include "kernels.h"
@@ -33,13 +34,24 @@ __device__ __forceinline__ int w_row_of_frag(int f, int c0, int I) {
 __device__ __forceinline__ int row_adapter(const GemmArgs& a, int slot) { return a.slot_adapter[slot]; }
 
 // S row chunk (8 values starting at j0) as hi/lo bf16 operands; zero when the
-// row is not in the current adapter run or j is past r.
+// row is not in the current adapter run or j is past r. COHERENT: S was
+// written during this launch by producer waves (possibly on another XCD, whose
+// L2 this one does not see), so it is read with agent-coherent loads, which
+// fetch from the coherence point instead of a possibly stale local L2 line.
+template <bool COHERENT = false>
 __device__ __forceinline__ void load_s_hilo(const GemmArgs& a, int slot, bool in_run, int j0,
                                             u32x4& hi, u32x4& lo) {
     float v[8], rest[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q) v[q] = 0.f;
-    if (in_run && j0 < a.r) {
+    if (COHERENT && in_run && j0 < a.r) {
+        for (int sp = 0; sp < a.s_split; ++sp) {
+            const float* src = a.S + (static_cast<size_t>(sp) * a.C_b + slot) * a.r + j0;
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+                v[q] += __hip_atomic_load(src + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    } else if (in_run && j0 < a.r) {
         // the shrink's K-range partials, added in order (a loop, not an
         // unrolled batch of loads: holding every partial at once costs the
         // direct-load kernel enough registers to halve its occupancy)
@@ -84,16 +96,143 @@ __device__ __forceinline__ u32x4 load_lora_b(const GemmArgs& a, int Nw, int ad, 
 // 128-byte lines of 16 rows; the two 16-byte halves feed two MFMA K steps and
 // the activation operand uses the same K assignment. Loads of chunk q+1 are in
 // flight while chunk q is multiplied.
+//
+// LoRA shrink inside the launch. When a.prod_units > 0 the first prod_units
+// workgroups are producer waves that compute S = X . A^T (the shrink of the
+// same post's section "Kernel optimizations") while the other waves stream the
+// base weights, so the LoRA A bytes share the projection's HBM stream instead
+// of a launch of their own. A projection wave multiplies its base K range
+// first and waits for the producers only before its expand.
+
+// Upper bound on the polls of a projection wave waiting for the producers. The
+// hardware dispatches the workgroups of a grid in index order, so every
+// producer (the lowest indices) is resident before any projection wave that
+// could wait for it, and producers never wait; the bound only guarantees that
+// every wave ends (about a second at most).
+constexpr int kMaxProducerPolls = 1 << 20;
+
+// One producer unit: the 16 S columns cf of LoRA-view block bl over K range ks,
+// for every real row of the block; then the unit counts itself in a.done with
+// release semantics, after all of its stores.
+__device__ __forceinline__ void shrink_producer(const GemmArgs& a, int unit) {
+    const int lane = threadIdx.x & 63;
+    const int kc = lane >> 4, lrow = lane & 15;
+    const int cf = unit % a.prod_ncf, rest = unit / a.prod_ncf;
+    const int ks = rest % a.s_split, bl = rest / a.s_split;
+    const int e = a.blk_e_l[bl];
+    if (e < 0) return;  // block past the live LoRA view: not counted
+    const int ad = a.blk_a_l[bl];
+    const int K = a.K;
+    // LoRA A row j of this lane's column; with r = 8 the upper 8 columns
+    // re-read rows j - 8 and are never stored
+    const int j = cf * 16 + lrow;
+    const uint16_t* arow =
+        a.Al + ((static_cast<size_t>(ad) * a.E + e) * a.r + (j < a.r ? j : j - 8)) * K + kc * 16;
+    const int nqa = K / 64;
+    const int q0 = ks * nqa / a.s_split, q1 = (ks + 1) * nqa / a.s_split, n = q1 - q0;
+    const int base = bl * a.bm_l;
+    const int p_first = a.sorted_l[base];
+    for (int fm = 0; fm < a.bm_l / 16; ++fm) {
+        if (a.sorted_l[base + fm * 16] >= a.P) break;  // the rest of the block is padding
+        // X row of block row fm*16 + lrow (padding rows re-read the first row)
+        int p = a.sorted_l[base + fm * 16 + lrow];
+        if (p >= a.P) p = p_first;
+        const size_t xr = a.gather_token ? static_cast<size_t>(p / a.top_k)
+                                         : static_cast<size_t>(a.slot_of_pair[p]);
+        const uint16_t* xrow = a.X + xr * K + kc * 16;
+        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+        u32x4 xb[2][2], wb[2][2];
+        auto load = [&](int buf, int q) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                xb[buf][h] = ld16(xrow + q * 64 + 8 * h);
+                wb[buf][h] = ld16(arow + q * 64 + 8 * h);
+            }
+        };
+        auto compute = [&](int buf) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) acc = mfma16x16x32(xb[buf][h], wb[buf][h], acc);
+        };
+        if (n > 0) {
+            load(0, q0);
+            int q = q0;
+            for (int i = 0; i + 1 < n; i += 2, q += 2) {
+                load(1, q + 1);
+                __builtin_amdgcn_sched_barrier(0);
+                compute(0);
+                __builtin_amdgcn_sched_barrier(0);
+                load(0, min(q + 2, q1 - 1));
+                __builtin_amdgcn_sched_barrier(0);
+                compute(1);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            if (n & 1) compute(0);
+        }
+        if (j < a.r) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int q = a.sorted_l[base + fm * 16 + 4 * kc + i];
+                if (q < a.P)
+                    __hip_atomic_store(&a.S_out[(static_cast<size_t>(ks) * a.C_b + a.slot_of_pair[q]) * a.r + j],
+                                       acc[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+    }
+    // The S stores above are agent-coherent (they write through to the
+    // coherence point that every XCD reads from), so waiting for this wave's
+    // stores to complete orders them before the count. An agent-scope release
+    // fence would add a write-back of this XCD's whole L2, which measured
+    // about 1 us of the projection's time per producer wave per XCD.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (lane == 0) __hip_atomic_fetch_add(a.done, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Whether every live producer unit has counted itself (live LoRA blocks x
+// column fragments x K ranges); one poll, wave-uniform result. S is read only
+// after a true result, with agent-coherent loads (load_s_hilo<true>), so no
+// agent-scope acquire is needed: that acquire would invalidate this XCD's
+// whole L2 once per projection wave, thousands of times per launch.
+__device__ __forceinline__ bool producers_done(const GemmArgs& a, int target) {
+    const int v = __hip_atomic_load(a.done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const bool ok = __builtin_amdgcn_readfirstlane(v) >= target;
+    // keeps the compiler from moving the S loads above the poll (no cache
+    // maintenance; the hardware issues them after the poll has returned)
+    asm volatile("" ::: "memory");
+    return ok;
+}
+
+__device__ __forceinline__ int producer_target(const GemmArgs& a) {
+    return (*a.n_l / a.bm_l) * a.prod_ncf * a.s_split;
+}
+
+// Poll until producers_done (bounded by kMaxProducerPolls).
+__device__ __forceinline__ void wait_producers(const GemmArgs& a, int target) {
+    for (int polls = 0; polls < kMaxProducerPolls; ++polls) {
+        if (producers_done(a, target)) break;
+        __builtin_amdgcn_s_sleep(2);
+    }
+}
+
 template <bool GATEUP, int FN>
 __global__ __launch_bounds__(64) void k_gemm_skinny(GemmArgs a) {
-    const int b = blockIdx.y, tile = blockIdx.x, z = blockIdx.z;  // z: K range (down only)
+    // 1-D grid: producer units first, then (column tile, block, K range) with
+    // the tile fastest
+    int wg = blockIdx.x;
+    if (wg < a.prod_units) {
+        shrink_producer(a, wg);
+        return;
+    }
+    wg -= a.prod_units;
+    constexpr int kCols = GATEUP ? FN * 8 : FN * 16;  // output columns per wave
+    const int n_tiles = a.N_out / kCols;
+    const int tile = wg % n_tiles, b = (wg / n_tiles) % a.n_blocks;
+    const int z = wg / n_tiles / a.n_blocks;  // K range (down only)
     const int e = a.blk_e_b[b];
     if (e < 0) return;
     const int lane = threadIdx.x & 63;
     const int g = lane >> 4, lrow = lane & 15;
     const int I = GATEUP ? a.N_out : 0;
     const int Nw = GATEUP ? 2 * a.N_out : a.N_out;
-    constexpr int kCols = GATEUP ? FN * 8 : FN * 16;  // output columns per wave
     const int c0 = tile * kCols;
     const int K = a.K;
     const int Kp = K / a.ksplit, kbeg = z * Kp;  // this workgroup's K range
@@ -142,11 +281,21 @@ __global__ __launch_bounds__(64) void k_gemm_skinny(GemmArgs a) {
     load(0, 0);
     __builtin_amdgcn_sched_barrier(0);
 
-    // LoRA expand first (its inputs are ready before this kernel starts), so
-    // its latency overlaps the first weight loads: acc += S . B^T for every
-    // adapter present among the 16 rows (added once: by the first K range).
-    if (a.L > 0 && z == 0) {
-        const int my_a = row_adapter(a, slot);
+    // LoRA expand: acc += S . B^T for every adapter present among the 16 rows
+    // (added once: by the first K range). With S from a separate launch it
+    // runs first, so its latency overlaps the first weight loads; with the
+    // producers in this launch it runs after the base K loop.
+    const bool lora = a.L > 0 && z == 0;
+    const int my_a = lora ? row_adapter(a, slot) : -1;
+    // With the producers in this launch the expand runs part-way through or
+    // after the base K loop, depending on when the producers finish; it then
+    // accumulates into its own registers, added to the base result after the
+    // loop, so the result does not depend on that timing.
+    const bool late = lora && a.prod_units > 0;
+    f32x4 acc_l[FN];
+#pragma unroll
+    for (int f = 0; f < FN; ++f) acc_l[f] = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto expand = [&](auto coherent, f32x4 (&dst)[FN]) {
         bool pending = my_a >= 0;
         while (true) {
             const uint64_t m = ballot64(pending);
@@ -161,15 +310,28 @@ __global__ __launch_bounds__(64) void k_gemm_skinny(GemmArgs a) {
 #pragma unroll
                 for (int f = 0; f < FN; ++f)
                     bb[f] = load_lora_b(a, Nw, acur, e, w_row_of_frag<GATEUP>(f, c0, I) + lrow, j0);
-                load_s_hilo(a, slot, in_run, j0, hi, lo);
+                load_s_hilo<decltype(coherent)::value>(a, slot, in_run, j0, hi, lo);
 #pragma unroll
                 for (int f = 0; f < FN; ++f) {
-                    acc[f] = mfma16x16x32(hi, bb[f], acc[f]);
-                    acc[f] = mfma16x16x32(lo, bb[f], acc[f]);
+                    dst[f] = mfma16x16x32(hi, bb[f], dst[f]);
+                    dst[f] = mfma16x16x32(lo, bb[f], dst[f]);
                 }
             }
         }
-    }
+    };
+    if (lora && !late) expand(std::false_type{}, acc);
+
+    // With the producers in this launch, the gate_up expand runs half-way
+    // through the K loop if they are done by then (one poll), so that its
+    // load latency is hidden while the other waves keep HBM busy; otherwise
+    // after the loop. On the decode-shaped layer the producers finish within
+    // the first 45 % of the gate_up launch, so the waves that finish last,
+    // which set the launch's length, expand mid-stream (gate_up 191 -> 187 us).
+    // The down projection expands after its loop: a poll half-way or three
+    // quarters through measured 2-5 us slower there.
+    const int target = late ? producer_target(a) : 0;
+    const int q_mid = GATEUP ? (nq / 2) & ~1 : nq;
+    bool expanded = !late;
 
     // Two-stage register pipeline with one back edge and no early exit, so
     // the prefetch stays in flight across iterations; scheduling barriers stop
@@ -177,6 +339,12 @@ __global__ __launch_bounds__(64) void k_gemm_skinny(GemmArgs a) {
     // end re-reads the last chunk (in bounds) and is discarded.
     int q = 0;
     for (int i = 0; i + 1 < nq; i += 2, q += 2) {
+        if (!expanded && q == q_mid) {
+            if (producers_done(a, target)) {
+                expand(std::true_type{}, acc_l);
+                expanded = true;
+            }
+        }
         load(1, q + 1);
         __builtin_amdgcn_sched_barrier(0);
         compute(0);
@@ -187,6 +355,15 @@ __global__ __launch_bounds__(64) void k_gemm_skinny(GemmArgs a) {
         __builtin_amdgcn_sched_barrier(0);
     }
     if (nq & 1) compute(0);
+
+    if (!expanded) {
+        wait_producers(a, target);
+        expand(std::true_type{}, acc_l);
+    }
+    if (late) {
+#pragma unroll
+        for (int f = 0; f < FN; ++f) acc[f] += acc_l[f];
+    }
 
     const int orow0 = b * 16 + 4 * g;
     if (GATEUP) {
@@ -799,13 +976,20 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
     if (!gemm_supported(a.N_out, a.K, a.gate_up, a.bm_b)) return hipErrorInvalidValue;
     if (a.ksplit < 1 || (a.K / 64) % a.ksplit || (a.ksplit > 1 && (a.gate_up || a.bm_b >= 128)))
         return hipErrorInvalidValue;
-    if (a.L > 0 && (a.s_split < 1 || a.s_split > kMaxShrinkSplit)) return hipErrorInvalidValue;
+    if (a.L > 0 && (a.s_split < 1 || a.s_split > (a.prod_units > 0 ? kMaxProducerSplit : kMaxShrinkSplit)))
+        return hipErrorInvalidValue;
+    if (a.prod_units < 0 || (a.prod_units > 0 && (a.L <= 0 || a.bm_b != 16 || a.S_hl || !a.done ||
+                                                  !a.n_l || !a.S_out || a.S_out != a.S ||
+                                                  a.prod_ncf != (a.r + 15) / 16 || a.bm_l < 16 ||
+                                                  a.bm_l > 256 || (a.bm_l & (a.bm_l - 1)))))
+        return hipErrorInvalidValue;
     if (a.L > 0 && a.S_hl && (a.s_split != 1 || a.s_hl_stride != s_hl_stride_of(a.r)))
         return hipErrorInvalidValue;
     if (a.bm_b == 16) {
         const int cols = a.gate_up ? kSkinnyFN * 8 : kSkinnyFN * 16;
-        if (a.n_blocks > 65535) return hipErrorInvalidValue;
-        const dim3 grid(a.N_out / cols, a.n_blocks, a.ksplit), block(64);
+        const long total = static_cast<long>(a.N_out / cols) * a.n_blocks * a.ksplit + a.prod_units;
+        if (total > 0x7fffffffL) return hipErrorInvalidValue;
+        const dim3 grid(static_cast<unsigned>(total)), block(64);
         if (a.gate_up) hipLaunchKernelGGL((k_gemm_skinny<true, kSkinnyFN>), grid, block, 0, s, a);
         else hipLaunchKernelGGL((k_gemm_skinny<false, kSkinnyFN>), grid, block, 0, s, a);
         return hipGetLastError();

@@ -7,8 +7,9 @@
 namespace moelora {
 
 // ---- route + align --------------------------------------------------------
+// zero_words[0 .. n_zero) are set to 0 by the same launch (n_zero <= 256).
 hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* w,
-                        hipStream_t s);
+                        hipStream_t s, int32_t* zero_words = nullptr, int n_zero = 0);
 
 // Whether the alignment kernel's LDS holds the key counts of E experts x
 // (L adapters + none) together with at least one histogram row.
@@ -51,6 +52,15 @@ hipError_t launch_shrink(const ShrinkArgs& a, hipStream_t s);
 // At most kMaxShrinkSplit; the projection kernels add the partials.
 constexpr int kMaxShrinkSplit = 4;
 int shrink_ksplit(int n_blocks_l, int K, int bm_b);
+// K ranges of a shrink run inside a projection kernel: each producer wave
+// streams at most kProducerMaxK of K, so the producers finish well before the
+// projection's own K loop ends (up to kMaxProducerSplit ranges).
+constexpr int kProducerMaxK = 4096;
+constexpr int kMaxProducerSplit = 16;
+inline int producer_ksplit(int K) {
+    const int s = (K + kProducerMaxK - 1) / kProducerMaxK;
+    return s < 1 ? 1 : (s > kMaxProducerSplit ? kMaxProducerSplit : s);
+}
 
 // ---- grouped expert GEMM with fused LoRA expand (+ SwiGLU) ---------------
 struct GemmArgs {
@@ -77,6 +87,25 @@ struct GemmArgs {
     // then runs the expand as extra stages of its LDS pipeline
     const uint16_t* S_hl;
     int s_hl_stride;
+    // LoRA shrink run inside this launch (16-row blocks only; prod_units == 0:
+    // S comes from a separate shrink launch). The first prod_units
+    // workgroups of the grid are producer waves: unit u computes the 16
+    // columns (u % prod_ncf) of S, over K range (u / prod_ncf) % s_split, for
+    // the rows of LoRA-view block u / (prod_ncf * s_split), writes them to
+    // S_out and then counts itself in *done. The projection waves run their
+    // base K loop first and wait for every live unit before the expand.
+    int prod_units;
+    int prod_ncf;
+    int gather_token;             // producer X row of pair p: x[p / top_k] (1) or h[slot_of_pair[p]] (0)
+    const int32_t* sorted_l;
+    const int32_t* blk_e_l;
+    const int32_t* blk_a_l;
+    const int32_t* slot_of_pair;
+    const uint16_t* Al;           // gate_up: [L][E][r][H]; down: [L][E][r][I]
+    int bm_l;
+    float* S_out;                 // the buffer S points at
+    int32_t* done;                // producer completion count, zero at launch
+    const int32_t* n_l;           // padded LoRA-view length (live LoRA blocks x bm_l)
 };
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
 // Whether a tile configuration exists for these sizes.

@@ -24,9 +24,12 @@ constexpr int kRouteMaxPerLane = 16;  // E <= 1024
 
 __global__ __launch_bounds__(256) void k_route(const float* __restrict__ logits, int T, int E,
                                                int k, int32_t* __restrict__ ids,
-                                               float* __restrict__ w) {
+                                               float* __restrict__ w,
+                                               int32_t* __restrict__ zero_words, int n_zero) {
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    // counters that later kernels of the same call count up from zero
+    if (blockIdx.x == 0 && threadIdx.x < n_zero) zero_words[threadIdx.x] = 0;
     if (t >= T) return;
     const float* row = logits + static_cast<size_t>(t) * E;
     const int nper = (E + 63) >> 6;
@@ -80,9 +83,11 @@ __global__ __launch_bounds__(256) void k_route(const float* __restrict__ logits,
 }
 
 hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* w,
-                        hipStream_t s) {
+                        hipStream_t s, int32_t* zero_words, int n_zero) {
     if (T == 0) return hipSuccess;
-    hipLaunchKernelGGL(k_route, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, k, ids, w);
+    if (n_zero < 0 || n_zero > 256 || (n_zero > 0 && !zero_words)) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_route, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, k, ids, w,
+                       zero_words, n_zero);
     return hipGetLastError();
 }
 

@@ -14,6 +14,7 @@ LIB_PATH = os.path.join(_PKG, "libmoelora.so")
 
 OK, EINVAL, EWORKSPACE, EHIP = 0, -1, -2, -3
 FLAG_OUT_BF16 = 1
+FLAG_SHRINK_LAUNCH = 2
 NKERNELS = 7
 
 
@@ -190,10 +191,12 @@ class Layer:
     """Device-resident weights + descriptor + workspace for repeated calls."""
 
     def __init__(self, T, H, I, E, top_k, L, r, w_gate_up, w_down, a_gate_up=None, b_gate_up=None,
-                 a_down=None, b_down=None, block_m_base=0, block_m_lora=0, out_bf16=False):
+                 a_down=None, b_down=None, block_m_base=0, block_m_lora=0, out_bf16=False,
+                 shrink_launch=False):
         import torch
         self.desc = make_desc(T, H, I, E, top_k, L, r, block_m_base, block_m_lora,
-                              FLAG_OUT_BF16 if out_bf16 else 0)
+                              (FLAG_OUT_BF16 if out_bf16 else 0) |
+                              (FLAG_SHRINK_LAUNCH if shrink_launch else 0))
         self.out_dtype = torch.bfloat16 if out_bf16 else torch.float32
         self.tensors = (w_gate_up, w_down, a_gate_up, b_gate_up, a_down, b_down)
         self.weights = weights_struct(*self.tensors)

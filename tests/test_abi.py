@@ -42,8 +42,8 @@ def desc(**over):
 @pytest.mark.parametrize("over", [dict(H=2881), dict(I=100), dict(top_k=0), dict(top_k=33, E=40),
                                   dict(top_k=5, E=4), dict(r=24), dict(E=0), dict(T=-1), dict(L=-1),
                                   dict(bm_b=48), dict(bm_b=8), dict(bm_l=512), dict(E=1025),
-                                  dict(E=128, L=200), dict(E=1024, L=9, top_k=8), dict(flags=2),
-                                  dict(flags=-1), dict(flags=3)])
+                                  dict(E=128, L=200), dict(E=1024, L=9, top_k=8), dict(flags=4),
+                                  dict(flags=-1), dict(flags=7)])
 def test_validate_rejects(over):
     assert ml.validate(desc(**over)) == ml.EINVAL
 
@@ -58,8 +58,21 @@ def test_validate_accepts_configs_and_checks_workspace():
         assert ml.validate(ds, None, n - 1) == ml.EWORKSPACE
 
 
-def test_validate_accepts_bf16_output_flag():
+def test_validate_accepts_output_and_shrink_flags():
     assert ml.validate(desc(flags=ml.FLAG_OUT_BF16)) == ml.OK
+    assert ml.validate(desc(flags=ml.FLAG_SHRINK_LAUNCH)) == ml.OK
+    assert ml.validate(desc(flags=ml.FLAG_OUT_BF16 | ml.FLAG_SHRINK_LAUNCH)) == ml.OK
+
+
+def test_shrink_launch_flag_keeps_the_decode_workspace_size():
+    # decode shape: 16-row base blocks, so the shrinks run inside the
+    # projection launches; their S buffers hold one partial per K range of
+    # at most 4096, while the separate launch of this shape uses one range
+    d = wl.CONFIGS["decode"]
+    fused = ml.make_desc(d["T"], d["H"], d["I"], d["E"], d["top_k"], d["L"], d["r"])
+    sep = ml.make_desc(d["T"], d["H"], d["I"], d["E"], d["top_k"], d["L"], d["r"],
+                       flags=ml.FLAG_SHRINK_LAUNCH)
+    assert ml.workspace_bytes(fused) == ml.workspace_bytes(sep)
 
 
 def test_validate_key_limit_edge():

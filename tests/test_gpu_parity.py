@@ -56,11 +56,11 @@ def build_case(name, dims=None, seed=None, touched_only=True):
     return wl.make_case(name, seed=seed, dims=dims, experts=experts, lora_blocks=blocks)
 
 
-def run_gpu(case, dev, bm_b=0, bm_l=0):
+def run_gpu(case, dev, bm_b=0, bm_l=0, shrink_launch=False):
     t = wl.device_tensors(case, dev)
     layer = ml.Layer(case.T, case.H, case.I, case.E, case.top_k, case.L, case.r,
                      t["w_gate_up"], t["w_down"], t["a_gate_up"], t["b_gate_up"], t["a_down"],
-                     t["b_down"], block_m_base=bm_b, block_m_lora=bm_l)
+                     t["b_down"], block_m_base=bm_b, block_m_lora=bm_l, shrink_launch=shrink_launch)
     out = layer(t["x"], t["logits"], t["adapter_ids"])
     torch.cuda.synchronize()
     return layer, t, out
@@ -159,10 +159,10 @@ def test_align_parity(dev, name, dims, bm):
 
 # ----------------------------------------------------------------------------- the layer
 
-def check_layer(case, dev, ntok=64, bm=(0, 0), stages=False):
+def check_layer(case, dev, ntok=64, bm=(0, 0), stages=False, shrink_launch=False):
     ids, w = oracle.route(case.logits, case.top_k)
     toks = sample_tokens(case, ntok)
-    layer, t, out = run_gpu(case, dev, *bm)
+    layer, t, out = run_gpu(case, dev, *bm, shrink_launch=shrink_launch)
     ref, st = oracle.forward(case, ids, w, tokens=toks, stages=True)
     got = out.cpu().numpy()[toks]
     mx, mean = metrics(got, ref)
@@ -248,6 +248,45 @@ def test_pipeline_expand(dev, r, L, bm, pure):
         case.w_gate_up[:] = 0
         case.w_down[:] = 0
     check_layer(case, dev, ntok=dims["T"], bm=(bm, 16), stages=True)
+
+
+# 16-row base blocks run the two shrinks as producer waves inside the
+# projection launches; the projection waves wait for them before the expand.
+# Each case also runs with the shrinks in launches of their own.
+FUSED_CASES = [
+    ("decode", None, (0, 0), True),
+    # gate_up K = 8256: three producer K ranges; down K = 128 (two 64-wide
+    # chunks) is then cut into three ranges too, one of them empty
+    ("fusedK3", dict(T=12, H=8256, I=128, E=2, top_k=1, L=3, r=16), (16, 16), False),
+    ("fusedK2", dict(T=20, H=4160, I=256, E=3, top_k=2, L=2, r=32), (16, 16), True),
+    # 64-row LoRA blocks: each producer loops over four row fragments
+    ("fusedBL", dict(T=120, H=128, I=192, E=2, top_k=1, L=1, r=32), (16, 64), True),
+    # rank 8: the producer's upper 8 columns re-read rows and are never stored
+    ("fusedR8", dict(T=20, H=64, I=128, E=4, top_k=2, L=3, r=8), (16, 16), False),
+    # rank 128: eight column fragments per LoRA block
+    ("fusedR128", dict(T=16, H=128, I=128, E=8, top_k=2, L=2, r=128), (16, 16), False),
+]
+
+
+@pytest.mark.parametrize("name,dims,bm,pure", FUSED_CASES)
+def test_shrinks_inside_projections(dev, name, dims, bm, pure):
+    log(f"shrinks inside projections {name} bm={bm} pure={pure}")
+    case = build_case(name, dims=dims, seed=None if dims is None else 90 + len(name))
+    if pure:
+        case.w_gate_up[:] = 0
+        case.w_down[:] = 0
+    out_f = check_layer(case, dev, ntok=case.T, bm=bm, stages=True)
+    out_s = check_layer(case, dev, ntok=case.T, bm=bm, stages=True, shrink_launch=True)
+    # the two agree far inside the oracle bars: they differ only in the
+    # shrinks' fp32 summation order, which can move an h value across a bf16
+    # rounding boundary (one bf16 step is 2^-8 of that value)
+    mx, mean = metrics(out_f.cpu().numpy(), out_s.cpu().numpy())
+    assert mx < MAX_TOL / 10 and mean < MEAN_TOL / 10, (mx, mean)
+    # and the fused form is repeatable bit for bit
+    layer, t, out1 = run_gpu(case, dev, *bm)
+    out2 = layer(t["x"], t["logits"], t["adapter_ids"])
+    torch.cuda.synchronize()
+    assert torch.equal(out1, out2)
 
 
 RANDOM_DIMS = [dict(T=1, H=64, I=64, E=1, top_k=1, L=1, r=8),

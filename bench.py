@@ -118,7 +118,7 @@ def lora_kernels_summary(kus, b):
             "hbm_frac": round(gbs / HBM_PEAK_GBS, 4) if gbs else None}
 
 
-def run_workload(name, steps, warmup, rotate, dev):
+def run_workload(name, steps, warmup, rotate, dev, table=None):
     import torch
 
     import oracle
@@ -136,7 +136,12 @@ def run_workload(name, steps, warmup, rotate, dev):
         tens = base if i == 0 else {k: v.clone() for k, v in base.items()}
         layers.append((ml.Layer(case.T, case.H, case.I, case.E, case.top_k, case.L, case.r,
                                 tens["w_gate_up"], tens["w_down"], tens["a_gate_up"],
-                                tens["b_gate_up"], tens["a_down"], tens["b_down"]), tens))
+                                tens["b_gate_up"], tens["a_down"], tens["b_down"], tuning=table), tens))
+    layer0 = layers[0][0]
+    bm_b, bm_l = ml.block_sizes(layer0.desc)
+    launch = {"block_m_base": bm_b, "block_m_lora": bm_l,
+              "shrink_launch": bool(layer0.desc.flags & ml.FLAG_SHRINK_LAUNCH),
+              "from_tuning_table": layer0.tuned is not None}
     out = torch.empty((case.T, case.H), dtype=torch.float32, device=dev)
 
     def step(i):
@@ -175,10 +180,10 @@ def run_workload(name, steps, warmup, rotate, dev):
     b, f, layer_bytes, layer_flops = algorithmic(case, st)
     del layers, base
     torch.cuda.empty_cache()
-    return case, ids, st, ms, kernel_us, b, f, layer_bytes, layer_flops, repeats
+    return case, ids, st, ms, kernel_us, b, f, layer_bytes, layer_flops, repeats, launch
 
 
-def workload_summary(name, c, st, ms, kus, b, f, lb, lf, repeats_ms):
+def workload_summary(name, c, st, ms, kus, b, f, lb, lf, repeats_ms, launch=None):
     """One workload's object: throughput, per-kernel times, layer roofline and
     the dominant projection kernel against its bound."""
     b, f = fold_fused(kus, b, f)
@@ -204,6 +209,8 @@ def workload_summary(name, c, st, ms, kus, b, f, lb, lf, repeats_ms):
            "layer_roofline_frac": round(roof_us / (ms * 1e3), 4),
            "kernel_us": {k: round(v, 2) for k, v in kus.items()}, "routing": st, "roofline": roof,
            "lora_shrink_expand_kernels": lora_kernels_summary(kus, b)}
+    if launch is not None:
+        out["launch"] = launch
     if mfma:
         tf = (f["gemm_gate_up"] + f["gemm_down"]) / (gemm_us * 1e-6) / 1e12
         out["base_gemms_tflops"] = round(tf, 1)
@@ -255,6 +262,10 @@ def main():
                     help="comma list of further workloads reported in the same line ('none' = none)")
     ap.add_argument("--rotate", type=int, default=3)
     ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--tuning", default=None, metavar="DIR",
+                    help="tuning folder (per-shape block sizes and shrink placement); default: the "
+                         "package's configs folder when it exists")
+    ap.add_argument("--no-tuning", action="store_true", help="use the library's default choices")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MiB",
                     help="first run one plain device-to-device copy of this size, as the "
                          "reference dispatch for scaling HBM byte counters")
@@ -279,9 +290,17 @@ def main():
         torch.neg(src, out=dst)
         torch.cuda.synchronize()
         del src, dst
-    case, ids, st, ms, kus, b, f, lbytes, lflops, reps = run_workload(args.workload, args.steps, args.warmup,
-                                                                     args.rotate, dev)
-    main_obj = workload_summary(args.workload, case, st, ms, kus, b, f, lbytes, lflops, reps)
+    from lora_mixture_experts_amd import tuning
+    table, table_dir = None, None
+    if not args.no_tuning:
+        table_dir = args.tuning or tuning.DEFAULT_FOLDER
+        if args.tuning or os.path.isdir(table_dir):
+            table = tuning.load(table_dir)
+        else:
+            table_dir = None
+    case, ids, st, ms, kus, b, f, lbytes, lflops, reps, launch = run_workload(
+        args.workload, args.steps, args.warmup, args.rotate, dev, table)
+    main_obj = workload_summary(args.workload, case, st, ms, kus, b, f, lbytes, lflops, reps, launch)
     line = {
         "metric": "MoE-LoRA layer tokens/s + us/call (decode 16 tok, prefill 6400 tok); % roofline",
         "value": main_obj["value"],
@@ -293,7 +312,9 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic (seeded, N(0,1) activations/logits, N(0,0.02) weights)",
         "config": {"workload": WORKLOAD_NAMES[args.workload], "global_batch": case.T, "seq_len": 1,
-                   "parallelism": "none (1 GPU)", "rotated_weight_copies": args.rotate},
+                   "parallelism": "none (1 GPU)", "rotated_weight_copies": args.rotate,
+                   "tuning_table": os.path.relpath(table_dir, ROOT) if table_dir else None,
+                   "launch": launch},
         "layer_roofline_frac": main_obj["layer_roofline_frac"],
         "kernel_us": main_obj["kernel_us"],
         "lora_shrink_expand_kernels": main_obj["lora_shrink_expand_kernels"],
@@ -303,7 +324,7 @@ def main():
     others = [w for w in args.also.split(",") if w and w != "none" and w != args.workload]
     for name in others:
         steps2 = max(5, args.steps // 5) if name in ("prefill", "many") else max(10, args.steps // 2)
-        res = run_workload(name, steps2, max(2, args.warmup // 2), args.rotate, dev)
+        res = run_workload(name, steps2, max(2, args.warmup // 2), args.rotate, dev, table)
         obj = workload_summary(name, res[0], res[2], *res[3:])
         if name == "prefill":
             line["prefill"] = obj

@@ -137,9 +137,10 @@ int moe_lora_align(const moe_lora_desc *d, const int32_t *topk_ids, const int32_
  * The gate_up and down LoRA expands add into the base projections' results
  * inside the projection kernels (AWS post, section "Kernel optimizations":
  * the LoRA add is fused into the expand). With 16-row base blocks (few rows
- * per expert, the default when T*top_k/E <= 8) the LoRA shrinks run inside
- * the projection launches too, as producer waves beside the base weight
- * stream; the projection waves wait for them, by polling a counter in the
+ * per expert, the default when T*top_k/E <= 8) and at most 1024 producer
+ * waves (LoRA-view block capacity x ceil(r/16) x K ranges of up to 4096),
+ * the LoRA shrinks run inside the projection launches too, as producer waves
+ * beside the base weight stream; the projection waves wait for them, by polling a counter in the
  * workspace, only before their expand. Such a wait is bounded (about a second
  * of polling): if it ever ran out, the output would be undefined, but every
  * wave still ends. */

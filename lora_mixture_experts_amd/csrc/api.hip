@@ -85,8 +85,16 @@ int make_plan(const moe_lora_desc* d, Plan* p) {
     p->nblk_l = p->C_l / p->bm_l;
     p->ksplit = gemm_down_ksplit(p->H, p->I, p->bm_b, p->nblk_b);
     // 16-row base blocks (few rows per expert: the projections stream their
-    // weights) run the shrinks inside the projection launches
-    p->fused = p->L > 0 && p->bm_b == 16 && !(d->flags & MOE_LORA_FLAG_SHRINK_LAUNCH);
+    // weights) run the shrinks inside the projection launches, as long as
+    // the producer waves stay a small share of the machine (at most about
+    // one per SIMD); more of them take the wave slots ahead of the projection
+    // and measured slower than separate launches
+    p->fused = false;
+    if (p->L > 0 && p->bm_b == 16 && !(d->flags & MOE_LORA_FLAG_SHRINK_LAUNCH)) {
+        const int ss = std::max(producer_ksplit(p->H), producer_ksplit(p->I));
+        const long units = static_cast<long>(p->nblk_l) * ((p->r + 15) / 16) * ss;
+        p->fused = units <= kMaxProducerUnits;
+    }
     if (p->fused)
         p->ssplit = std::max(producer_ksplit(p->H), producer_ksplit(p->I));
     else

@@ -57,6 +57,10 @@ int shrink_ksplit(int n_blocks_l, int K, int bm_b);
 // projection's own K loop ends (up to kMaxProducerSplit ranges).
 constexpr int kProducerMaxK = 4096;
 constexpr int kMaxProducerSplit = 16;
+// at most this many producer waves per projection launch (LoRA-view block
+// capacity x column fragments x K ranges); beyond it the shrinks get launches
+// of their own
+constexpr long kMaxProducerUnits = 1024;
 inline int producer_ksplit(int K) {
     const int s = (K + kProducerMaxK - 1) / kProducerMaxK;
     return s < 1 ? 1 : (s > kMaxProducerSplit ? kMaxProducerSplit : s);

@@ -192,8 +192,18 @@ class Layer:
 
     def __init__(self, T, H, I, E, top_k, L, r, w_gate_up, w_down, a_gate_up=None, b_gate_up=None,
                  a_down=None, b_down=None, block_m_base=0, block_m_lora=0, out_bf16=False,
-                 shrink_launch=False):
+                 shrink_launch=False, tuning=None):
+        """tuning: a tuning.Table; when it holds a choice for this shape and
+        token count it sets the block sizes and the shrink placement (only if
+        none of them is given explicitly)."""
         import torch
+        self.tuned = None
+        if tuning is not None and block_m_base == 0 and block_m_lora == 0 and not shrink_launch:
+            self.tuned = tuning.lookup(T, H, I, E, top_k, L, r)
+            if self.tuned is not None:
+                block_m_base = self.tuned.block_m_base
+                block_m_lora = self.tuned.block_m_lora
+                shrink_launch = self.tuned.shrink_launch
         self.desc = make_desc(T, H, I, E, top_k, L, r, block_m_base, block_m_lora,
                               (FLAG_OUT_BF16 if out_bf16 else 0) |
                               (FLAG_SHRINK_LAUNCH if shrink_launch else 0))

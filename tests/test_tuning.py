@@ -1,0 +1,93 @@
+"""Host-side checks of the per-shape tuning table and the tuner's search space
+(no GPU needed)."""
+import json
+import os
+
+import pytest
+
+from lora_mixture_experts_amd import moe_lora as ml
+from lora_mixture_experts_amd import tune
+from lora_mixture_experts_amd import tuning
+from lora_mixture_experts_amd import workloads as wl
+
+SHAPE = dict(H=2880, I=2880, E=32, top_k=4, L=8, r=32)
+
+
+def entry(T_max, bm_b, bm_l=16, sep=False, us=1.0):
+    return {"T_max": T_max, "block_m_base": bm_b, "block_m_lora": bm_l, "shrink_launch": sep, "us": us}
+
+
+def test_round_trip_and_bucket_lookup(tmp_path):
+    d = str(tmp_path)
+    tuning.save_entry(d, SHAPE, entry(16, 16, sep=True))
+    tuning.save_entry(d, SHAPE, entry(6400, 128, 32))
+    tuning.save_entry(d, SHAPE, entry(512, 64))
+    t = tuning.load(d)
+    assert len(t) == 3
+    args = [SHAPE[k] for k in tuning.SHAPE_KEYS]
+    # the smallest T_max >= T applies
+    assert t.lookup(1, *args) == tuning.Choice(16, 16, True)
+    assert t.lookup(16, *args) == tuning.Choice(16, 16, True)
+    assert t.lookup(17, *args) == tuning.Choice(64, 16, False)
+    assert t.lookup(6400, *args) == tuning.Choice(128, 32, False)
+    # beyond the largest bucket, or another shape: no advice
+    assert t.lookup(6401, *args) is None
+    assert t.lookup(16, 2880, 2880, 32, 4, 8, 64) is None
+    # entries are kept sorted and replaced by T_max
+    tuning.save_entry(d, SHAPE, entry(512, 32))
+    t = tuning.load(d)
+    assert [e["T_max"] for e in t.entries(*args)] == [16, 512, 6400]
+    assert t.lookup(100, *args) == tuning.Choice(32, 16, False)
+
+
+def test_files_are_named_by_shape(tmp_path):
+    path = tuning.save_entry(str(tmp_path), SHAPE, entry(16, 16))
+    assert os.path.basename(path) == "H2880_I2880_E32_k4_L8_r32.json"
+    doc = json.load(open(path))
+    assert doc["shape"] == SHAPE and doc["device"] == "gfx950"
+
+
+@pytest.mark.parametrize("bad", [dict(block_m_base=48), dict(block_m_lora=8), dict(T_max=0),
+                                 dict(shrink_launch="yes"), dict(block_m_base=None)])
+def test_invalid_entries_are_rejected(tmp_path, bad):
+    e = entry(16, 16)
+    e.update(bad)
+    with pytest.raises(ValueError):
+        tuning.save_entry(str(tmp_path), SHAPE, e)
+    path = tmp_path / "x.json"
+    path.write_text(json.dumps({"shape": SHAPE, "entries": [e]}))
+    with pytest.raises(ValueError):
+        tuning.load(str(tmp_path))
+
+
+def test_missing_folder_is_an_error_and_other_files_are_ignored(tmp_path):
+    with pytest.raises(FileNotFoundError):
+        tuning.load(str(tmp_path / "nope"))
+    (tmp_path / "README.txt").write_text("not a table")
+    assert len(tuning.load(str(tmp_path))) == 0
+
+
+def test_committed_table_loads_and_names_valid_choices():
+    if not os.path.isdir(tuning.DEFAULT_FOLDER):
+        pytest.skip("no committed tuning folder")
+    t = tuning.load(tuning.DEFAULT_FOLDER)
+    for key in t.shapes():
+        for e in t.entries(*key):
+            H, I, E, k, L, r = key
+            d = ml.make_desc(e["T_max"], H, I, E, k, L, r, e["block_m_base"], e["block_m_lora"],
+                             ml.FLAG_SHRINK_LAUNCH if e["shrink_launch"] else 0)
+            assert ml.validate(d) == ml.OK, (key, e)
+
+
+@pytest.mark.parametrize("name", list(wl.CONFIGS))
+def test_search_space_holds_the_library_default(name):
+    c = wl.CONFIGS[name]
+    cands = list(tune.candidates(c["L"]))
+    assert len(set(cands)) == len(cands)
+    d0 = ml.make_desc(c["T"], c["H"], c["I"], c["E"], c["top_k"], c["L"], c["r"])
+    bm_b, bm_l = ml.block_sizes(d0)
+    assert (bm_b, bm_l, False) in cands
+    valid = [x for x in cands
+             if ml.validate(ml.make_desc(c["T"], c["H"], c["I"], c["E"], c["top_k"], c["L"], c["r"], x[0], x[1],
+                                         ml.FLAG_SHRINK_LAUNCH if x[2] else 0)) == ml.OK]
+    assert len(valid) >= 10

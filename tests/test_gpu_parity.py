@@ -289,6 +289,38 @@ def test_shrinks_inside_projections(dev, name, dims, bm, pure):
     assert torch.equal(out1, out2)
 
 
+def _shrink_launch_times(case, dev, bm):
+    layer, t, _ = run_gpu(case, dev, *bm)
+    ml.timing_enable(2)
+    layer(t["x"], t["logits"], t["adapter_ids"])
+    layer(t["x"], t["logits"], t["adapter_ids"])
+    torch.cuda.synchronize()
+    ms, n = ml.timing_read()
+    ml.timing_enable(0)
+    names = ml.kernel_names()
+    assert n == 2
+    return ms[names.index("shrink_gate_up")], ms[names.index("shrink_down")]
+
+
+def test_shrink_placement_rule(dev):
+    # the shrinks run inside the projection launches (their timing slots read
+    # exactly 0) for 16-row base blocks with at most 1024 producer waves, and
+    # in launches of their own otherwise
+    log("shrink placement")
+    dec = build_case("decode")
+    assert _shrink_launch_times(dec, dev, (0, 0)) == (0.0, 0.0)
+    # 16-row base blocks on a larger batch: LoRA-view capacity
+    # (2048 + 256 * 15) / 16 = 368 blocks x 4 column fragments (r = 64)
+    # = 1472 > 1024 producer waves
+    dims = dict(T=512, H=128, I=128, E=32, top_k=4, L=8, r=64)
+    big = build_case("placement", dims=dims, seed=21)
+    g, d = _shrink_launch_times(big, dev, (16, 16))
+    assert g > 0.0 and d > 0.0
+    # 64-row base blocks: always separate launches
+    g, d = _shrink_launch_times(build_case("many"), dev, (0, 0))
+    assert g > 0.0 and d > 0.0
+
+
 RANDOM_DIMS = [dict(T=1, H=64, I=64, E=1, top_k=1, L=1, r=8),
                dict(T=3, H=128, I=64, E=4, top_k=4, L=2, r=16),
                dict(T=33, H=64, I=192, E=9, top_k=2, L=4, r=64),

@@ -213,7 +213,7 @@ __device__ __forceinline__ void wait_producers(const GemmArgs& a, int target) {
     }
 }
 
-template <bool GATEUP, int FN>
+template <bool GATEUP, int FN, int NS>
 __global__ __launch_bounds__(64) void k_gemm_skinny(GemmArgs a) {
     // 1-D grid: producer units first, then (column tile, block, K range) with
     // the tile fastest
@@ -260,7 +260,7 @@ __global__ __launch_bounds__(64) void k_gemm_skinny(GemmArgs a) {
     f32x4 acc[FN];
 #pragma unroll
     for (int f = 0; f < FN; ++f) acc[f] = f32x4{0.f, 0.f, 0.f, 0.f};
-    u32x4 xb[2][2], wb[2][FN][2];
+    u32x4 xb[NS][2], wb[NS][FN][2];
     auto load = [&](int buf, int q) {
         const int k0 = q * 64;
 #pragma unroll
@@ -278,7 +278,8 @@ __global__ __launch_bounds__(64) void k_gemm_skinny(GemmArgs a) {
     };
 
     const int nq = Kp / 64;
-    load(0, 0);
+#pragma unroll
+    for (int st = 0; st + 1 < NS; ++st) load(st, min(st, nq - 1));
     __builtin_amdgcn_sched_barrier(0);
 
     // LoRA expand: acc += S . B^T for every adapter present among the 16 rows
@@ -330,31 +331,35 @@ __global__ __launch_bounds__(64) void k_gemm_skinny(GemmArgs a) {
     // The down projection expands after its loop: a poll half-way or three
     // quarters through measured 2-5 us slower there.
     const int target = late ? producer_target(a) : 0;
-    const int q_mid = GATEUP ? (nq / 2) & ~1 : nq;
+    const int q_mid = GATEUP ? nq / 2 / NS * NS : nq;
     bool expanded = !late;
 
-    // Two-stage register pipeline with one back edge and no early exit, so
-    // the prefetch stays in flight across iterations; scheduling barriers stop
-    // the compiler from sinking loads next to their use. A prefetch past the
-    // end re-reads the last chunk (in bounds) and is discarded.
+    // NS-stage register pipeline: chunk c sits in buffer c % NS and is
+    // requested NS - 1 chunks ahead of its use. The main loop has one back
+    // edge and no early exit, so the requests stay in flight across
+    // iterations; scheduling barriers stop the compiler from sinking loads
+    // next to their use. A request past the end re-reads the last chunk (in
+    // bounds) and is discarded.
     int q = 0;
-    for (int i = 0; i + 1 < nq; i += 2, q += 2) {
+    for (; q + NS <= nq; q += NS) {
         if (!expanded && q == q_mid) {
             if (producers_done(a, target)) {
                 expand(std::true_type{}, acc_l);
                 expanded = true;
             }
         }
-        load(1, q + 1);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(0);
-        __builtin_amdgcn_sched_barrier(0);
-        load(0, min(q + 2, nq - 1));
-        __builtin_amdgcn_sched_barrier(0);
-        compute(1);
-        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int st = 0; st < NS; ++st) {
+            load((st + NS - 1) % NS, min(q + st + NS - 1, nq - 1));
+            __builtin_amdgcn_sched_barrier(0);
+            compute(st);
+            __builtin_amdgcn_sched_barrier(0);
+        }
     }
-    if (nq & 1) compute(0);
+    // the last nq - q (< NS) chunks are already in buffers 0 .. nq - q - 1
+#pragma unroll
+    for (int st = 0; st + 1 < NS; ++st)
+        if (st < nq - q) compute(st);
 
     if (!expanded) {
         wait_producers(a, target);
@@ -924,7 +929,13 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_dma(GemmArgs a) {
 // These shapes were the fastest of those measured on MI355X for the
 // decode-, many-adapter- and prefill-shaped layers. The column count may
 // leave a partial last tile.
-constexpr int kSkinnyFN = 4;  // 16-column fragments per skinny wave
+// 16-column weight fragments per skinny wave and register pipeline stages,
+// per projection (gate_up: fragments pair gate and up rows, so a wave writes
+// FN * 8 h columns; down: FN * 16 D columns)
+constexpr int kSkinnyFNGateUp = 4;
+constexpr int kSkinnyNSGateUp = 2;
+constexpr int kSkinnyFNDown = 4;
+constexpr int kSkinnyNSDown = 2;
 
 template <int BM, int BNT, int WM, int WN, int NS>
 static hipError_t launch_dma(const GemmArgs& a, hipStream_t s) {
@@ -952,13 +963,13 @@ static hipError_t launch_tiled(const GemmArgs& a, hipStream_t s) {
 
 bool gemm_supported(int N_out, int K, int gate_up, int bm_b) {
     if (K % 64 != 0 || N_out % 32 != 0) return false;
-    if (bm_b == 16) return N_out % (gate_up ? 32 : 64) == 0;
+    if (bm_b == 16) return N_out % (gate_up ? kSkinnyFNGateUp * 8 : kSkinnyFNDown * 16) == 0;
     return bm_b == 32 || bm_b == 64 || bm_b == 128 || bm_b == 256;
 }
 
 int gemm_down_ksplit(int N_out, int K, int bm_b, int n_blocks) {
     if (bm_b >= 128 || n_blocks <= 0) return 1;
-    const long cols = bm_b == 16 ? 16 * kSkinnyFN : 128;
+    const long cols = bm_b == 16 ? 16 * kSkinnyFNDown : 128;
     const long waves = (N_out + cols - 1) / cols * n_blocks * (bm_b == 16 ? 1 : 4);
     constexpr long kTargetWaves = 4096;  // about 16 per CU
     constexpr int kMinChunks = 8;        // at least 512 of K per split
@@ -986,12 +997,14 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
     if (a.L > 0 && a.S_hl && (a.s_split != 1 || a.s_hl_stride != s_hl_stride_of(a.r)))
         return hipErrorInvalidValue;
     if (a.bm_b == 16) {
-        const int cols = a.gate_up ? kSkinnyFN * 8 : kSkinnyFN * 16;
+        const int cols = a.gate_up ? kSkinnyFNGateUp * 8 : kSkinnyFNDown * 16;
         const long total = static_cast<long>(a.N_out / cols) * a.n_blocks * a.ksplit + a.prod_units;
         if (total > 0x7fffffffL) return hipErrorInvalidValue;
         const dim3 grid(static_cast<unsigned>(total)), block(64);
-        if (a.gate_up) hipLaunchKernelGGL((k_gemm_skinny<true, kSkinnyFN>), grid, block, 0, s, a);
-        else hipLaunchKernelGGL((k_gemm_skinny<false, kSkinnyFN>), grid, block, 0, s, a);
+        if (a.gate_up)
+            hipLaunchKernelGGL((k_gemm_skinny<true, kSkinnyFNGateUp, kSkinnyNSGateUp>), grid, block, 0, s, a);
+        else
+            hipLaunchKernelGGL((k_gemm_skinny<false, kSkinnyFNDown, kSkinnyNSDown>), grid, block, 0, s, a);
         return hipGetLastError();
     }
     switch (a.bm_b) {

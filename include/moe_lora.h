@@ -140,10 +140,11 @@ int moe_lora_align(const moe_lora_desc *d, const int32_t *topk_ids, const int32_
  * per expert, the default when T*top_k/E <= 8) and at most 1024 producer
  * waves (LoRA-view block capacity x ceil(r/16) x K ranges of up to 4096),
  * the LoRA shrinks run inside the projection launches too, as producer waves
- * beside the base weight stream; the projection waves wait for them, by polling a counter in the
- * workspace, only before their expand. Such a wait is bounded (about a second
- * of polling): if it ever ran out, the output would be undefined, but every
- * wave still ends. */
+ * beside the base weight stream; the projection waves wait for them, by
+ * polling a counter in the workspace, only before their expand. Such a wait
+ * is bounded (about a second of polling): if it ever ran out, every wave
+ * still ends, the output is not valid, and moe_lora_read_status reports
+ * MOE_LORA_STATUS_WAIT_TIMEOUT. */
 int moe_lora_forward(const moe_lora_desc *d, const moe_lora_weights *w, const void *x,
                      const float *logits, const int32_t *adapter_ids, void *out,
                      void *workspace, size_t ws_bytes, void *stream);
@@ -158,6 +159,16 @@ int moe_lora_forward(const moe_lora_desc *d, const moe_lora_weights *w, const vo
 int moe_lora_read_stages(const moe_lora_desc *d, const void *workspace, size_t ws_bytes,
                          int32_t *topk_ids, float *topk_w, float *s1, uint16_t *h,
                          float *s2, float *dn, void *stream);
+
+/* Status of the last moe_lora_forward with T > 0 on `workspace`: copies one
+ * int32 into `status` (a device pointer, like every tensor argument) on
+ * `stream`. 0 means the call ran as specified; MOE_LORA_STATUS_WAIT_TIMEOUT
+ * means a projection wave stopped waiting for the shrink waves of its launch,
+ * and that call's output is not valid. Each forward call with T > 0 clears
+ * the word first. */
+#define MOE_LORA_STATUS_WAIT_TIMEOUT 1
+int moe_lora_read_status(const moe_lora_desc *d, const void *workspace, size_t ws_bytes,
+                         int32_t *status, void *stream);
 
 /* Copy the alignment of the last moe_lora_forward on `workspace` out (same
  * arrays and layout as moe_lora_align produces); any output may be NULL. */

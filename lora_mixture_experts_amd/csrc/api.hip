@@ -281,8 +281,9 @@ int moe_lora_forward(const moe_lora_desc* d, const moe_lora_weights* w, const vo
     auto ok = [&](hipError_t v) { if (e == hipSuccess) e = v; };
     timing_mark(call, 0, s);
     // counts[0..1]: n_b, n_l (alignment); counts[2..3]: producer counts of
-    // the two projections, zeroed by the routing launch
-    ok(launch_route(logits, p.T, p.E, p.k, ids, tw, s, counts + 2, 2));
+    // the two projections; counts[4]: the call's status word; 2..4 are
+    // zeroed by the routing launch
+    ok(launch_route(logits, p.T, p.E, p.k, ids, tw, s, counts + 2, 3));
     timing_mark(call, 1, s);
     ok(launch_align(ids, adapter_ids, p.T, p.k, p.E, p.L, p.bm_b, p.bm_l, p.C_b, p.C_l, sorted_b,
                     blk_e_b, counts, sorted_l, blk_e_l, blk_a_l, counts + 1, slot, lslot, sad,
@@ -317,6 +318,7 @@ int moe_lora_forward(const moe_lora_desc* d, const moe_lora_weights* w, const vo
         ga.gather_token = 1; ga.sorted_l = sorted_l; ga.blk_e_l = blk_e_l; ga.blk_a_l = blk_a_l;
         ga.slot_of_pair = slot; ga.Al = static_cast<const uint16_t*>(w->a_gate_up);
         ga.bm_l = p.bm_l; ga.S_out = s1; ga.done = counts + 2; ga.n_l = counts + 1;
+        ga.status = counts + 4;
     }
     ok(launch_gemm(ga, s));
     timing_mark(call, 4, s);
@@ -395,6 +397,21 @@ int moe_lora_read_alignment(const moe_lora_desc* d, const void* workspace, size_
     cp(blk_a_l, p.off_blk_a_l, p.nblk_l);
     cp(n_l, p.off_counts + 4, 1);
     return e == hipSuccess ? MOE_LORA_OK : MOE_LORA_EHIP;
+}
+
+int moe_lora_read_status(const moe_lora_desc* d, const void* workspace, size_t ws_bytes,
+                         int32_t* status, void* stream) {
+    Plan p;
+    const int rc = make_plan(d, &p);
+    if (rc) return rc;
+    if (!workspace || !status) return MOE_LORA_EINVAL;
+    if (ws_bytes < p.total) return MOE_LORA_EWORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    void* ws = const_cast<void*>(workspace);
+    return hipMemcpyAsync(status, at<int32_t>(ws, p.off_counts + 16), 4, hipMemcpyDeviceToDevice, s) ==
+                   hipSuccess
+               ? MOE_LORA_OK
+               : MOE_LORA_EHIP;
 }
 
 int moe_lora_timing_enable(int32_t max_calls) {

@@ -205,12 +205,16 @@ __device__ __forceinline__ int producer_target(const GemmArgs& a) {
     return (*a.n_l / a.bm_l) * a.prod_ncf * a.s_split;
 }
 
-// Poll until producers_done (bounded by kMaxProducerPolls).
+// Poll until producers_done (bounded by kMaxProducerPolls). A wait that runs
+// out sets the call's status word, so the host can tell that the output is
+// not valid.
 __device__ __forceinline__ void wait_producers(const GemmArgs& a, int target) {
     for (int polls = 0; polls < kMaxProducerPolls; ++polls) {
-        if (producers_done(a, target)) break;
+        if (producers_done(a, target)) return;
         __builtin_amdgcn_s_sleep(2);
     }
+    if ((threadIdx.x & 63) == 0)
+        __hip_atomic_fetch_or(a.status, kStatusWaitTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <bool GATEUP, int FN, int NS>
@@ -989,7 +993,7 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
         return hipErrorInvalidValue;
     if (a.L > 0 && (a.s_split < 1 || a.s_split > (a.prod_units > 0 ? kMaxProducerSplit : kMaxShrinkSplit)))
         return hipErrorInvalidValue;
-    if (a.prod_units < 0 || (a.prod_units > 0 && (a.L <= 0 || a.bm_b != 16 || a.S_hl || !a.done ||
+    if (a.prod_units < 0 || (a.prod_units > 0 && (a.L <= 0 || a.bm_b != 16 || a.S_hl || !a.done || !a.status ||
                                                   !a.n_l || !a.S_out || a.S_out != a.S ||
                                                   a.prod_ncf != (a.r + 15) / 16 || a.bm_l < 16 ||
                                                   a.bm_l > 256 || (a.bm_l & (a.bm_l - 1)))))

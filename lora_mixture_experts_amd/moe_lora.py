@@ -59,6 +59,7 @@ def lib():
             "moe_lora_forward": ([pD, pW, P, P, P, P, P, SZ, P], ctypes.c_int),
             "moe_lora_read_stages": ([pD, P, SZ, P, P, P, P, P, P, P], ctypes.c_int),
             "moe_lora_read_alignment": ([pD, P, SZ, P, P, P, P, P, P, P, P], ctypes.c_int),
+            "moe_lora_read_status": ([pD, P, SZ, P, P], ctypes.c_int),
             "moe_lora_timing_enable": ([I32], ctypes.c_int),
             "moe_lora_timing_read": ([ctypes.POINTER(ctypes.c_float), pI32], ctypes.c_int),
             "moe_lora_kernel_name": ([I32], ctypes.c_char_p),
@@ -74,6 +75,7 @@ def lib():
 EXPORTED = ("moe_lora_strerror", "moe_lora_validate", "moe_lora_block_sizes",
             "moe_lora_workspace_bytes", "moe_lora_align_capacity", "moe_lora_route",
             "moe_lora_align", "moe_lora_forward", "moe_lora_read_stages", "moe_lora_read_alignment",
+            "moe_lora_read_status",
             "moe_lora_timing_enable", "moe_lora_timing_read", "moe_lora_kernel_name")
 
 
@@ -161,6 +163,17 @@ def read_stages(desc, workspace, topk_ids=None, topk_w=None, s1=None, h=None, s2
                                       _ptr(dn), _stream(stream)), "read_stages")
 
 
+STATUS_WAIT_TIMEOUT = 1
+
+
+def read_status(desc, workspace, status, stream=None):
+    """Enqueue a copy of the last forward call's status word into `status`
+    (a device int32 tensor of one element)."""
+    _check(lib().moe_lora_read_status(ctypes.byref(desc), _ptr(workspace),
+                                      ctypes.c_size_t(workspace.numel() * workspace.element_size()),
+                                      _ptr(status), _stream(stream)), "read_status")
+
+
 def read_alignment(desc, workspace, sorted_b=None, blk_e_b=None, n_b=None, sorted_l=None,
                    blk_e_l=None, blk_a_l=None, n_l=None, stream=None):
     _check(lib().moe_lora_read_alignment(ctypes.byref(desc), _ptr(workspace),
@@ -220,6 +233,14 @@ class Layer:
             out = torch.empty((self.desc.T, self.desc.H), dtype=self.out_dtype, device=self.device)
         forward(self.desc, self.weights, x, logits, adapter_ids, out, self.workspace, stream)
         return out
+
+    def status(self, stream=None) -> int:
+        """Status word of the last call (0 = ran as specified); synchronises."""
+        import torch
+        st = torch.full((1,), -1, dtype=torch.int32, device=self.device)
+        read_status(self.desc, self.workspace, st, stream)
+        torch.cuda.synchronize(self.device)
+        return int(st.item())
 
     def stages(self, stream=None):
         import torch

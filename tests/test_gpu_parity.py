@@ -168,6 +168,7 @@ def check_layer(case, dev, ntok=64, bm=(0, 0), stages=False, shrink_launch=False
     mx, mean = metrics(got, ref)
     log(f"  {case.name} bm={ml.block_sizes(layer.desc)} tokens={len(toks)}: max {mx:.2e} mean {mean:.2e}")
     assert np.all(np.isfinite(got))
+    assert layer.status() == 0
     assert mx <= MAX_TOL and mean <= MEAN_TOL, (mx, mean)
     # the alignment the forward pass used is the oracle's, bit for bit
     bb, bl = ml.block_sizes(layer.desc)
@@ -287,6 +288,22 @@ def test_shrinks_inside_projections(dev, name, dims, bm, pure):
     out2 = layer(t["x"], t["logits"], t["adapter_ids"])
     torch.cuda.synchronize()
     assert torch.equal(out1, out2)
+    assert layer.status() == 0
+
+
+def test_status_word_is_cleared_by_each_call(dev):
+    # the status word lives in the workspace and each forward call clears it
+    log("status word")
+    case = build_case("decode")
+    layer, t, _ = run_gpu(case, dev)
+    assert layer.status() == 0
+    # poison the whole workspace, including the status word; a forward call
+    # writes every workspace entry before it reads it (the alignment fills
+    # each view to its capacity, the routing launch clears the counters)
+    layer.workspace.view(torch.int32).fill_(-1)
+    layer(t["x"], t["logits"], t["adapter_ids"])
+    torch.cuda.synchronize()
+    assert layer.status() == 0
 
 
 def _shrink_launch_times(case, dev, bm):

@@ -62,3 +62,27 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_shrink_work_is_counted_in_the_launch_that_ran_it():
+    c = small_case()
+    st = dict(n_experts=3, n_segments=4, P=8, P_lora=6)
+    b, f, lb, lf = bench.algorithmic(c, st)
+    names = ("route", "align", "shrink_gate_up", "gemm_gate_up", "shrink_down", "gemm_down", "combine")
+    # shrinks with launches of their own: per-kernel figures unchanged
+    kus = {k: 10.0 for k in names}
+    assert not bench.shrinks_fused(kus)
+    assert bench.fold_fused(kus, b, f) == (b, f)
+    # shrinks inside the projections (the library reports exactly 0 for them):
+    # their bytes and flops move into the projection launches, totals kept
+    kus_f = dict(kus, shrink_gate_up=0.0, shrink_down=0.0)
+    assert bench.shrinks_fused(kus_f)
+    b2, f2 = bench.fold_fused(kus_f, b, f)
+    assert b2["gemm_gate_up"] == b["gemm_gate_up"] + b["shrink_gate_up"]
+    assert b2["gemm_down"] == b["gemm_down"] + b["shrink_down"]
+    assert f2["gemm_down"] == f["gemm_down"] + f["shrink_down"]
+    assert b2["shrink_gate_up"] == 0 and b2["shrink_down"] == 0
+    assert sum(b2.values()) == sum(b.values())
+    summ = bench.lora_kernels_summary(kus_f, b2)
+    assert summ["shrinks"] == "inside the projection launches"
+    assert summ["bytes"] == sum(b[n] for n in ("shrink_gate_up", "gemm_gate_up", "shrink_down", "gemm_down"))

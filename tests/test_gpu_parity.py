@@ -474,6 +474,48 @@ def test_zero_tokens_is_noop(dev):
     torch.cuda.synchronize()
 
 
+def test_zero_tokens_with_adapters_is_noop(dev):
+    # T = 0 with a LoRA pool: nothing is launched and the output is untouched
+    log("zero tokens with adapters")
+    d = ml.make_desc(0, 64, 64, 4, 2, 3, 16)
+    w = torch.zeros(4 * 3 * 64 * 64, dtype=torch.bfloat16, device=dev)
+    lora = torch.zeros(3 * 4 * 16 * 128, dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(max(ml.workspace_bytes(d), 256), dtype=torch.uint8, device=dev)
+    out = torch.full((4,), 7.0, dtype=torch.float32, device=dev)
+    x = torch.empty(8, dtype=torch.bfloat16, device=dev)
+    lg = torch.empty(4, dtype=torch.float32, device=dev)
+    ad = torch.empty(1, dtype=torch.int32, device=dev)
+    ml.forward(d, ml.weights_struct(w, w, lora, lora, lora, lora), x, lg, ad, out, ws)
+    torch.cuda.synchronize()
+    assert torch.all(out == 7.0)
+
+
+def test_tuning_table_choice_is_used_and_keeps_parity(dev, tmp_path):
+    # a table entry for the tiny shape that differs from every default: the
+    # layer takes its block sizes and shrink placement, and still matches the
+    # oracle
+    from lora_mixture_experts_amd import tuning
+    log("tuning table")
+    case = build_case("tiny")
+    shape = {k: getattr(case, k) for k in tuning.SHAPE_KEYS}
+    tuning.save_entry(str(tmp_path), shape, {"T_max": 64, "block_m_base": 32, "block_m_lora": 64,
+                                             "shrink_launch": True})
+    table = tuning.load(str(tmp_path))
+    t = wl.device_tensors(case, dev)
+    layer = ml.Layer(case.T, case.H, case.I, case.E, case.top_k, case.L, case.r, t["w_gate_up"], t["w_down"],
+                     t["a_gate_up"], t["b_gate_up"], t["a_down"], t["b_down"], tuning=table)
+    assert layer.tuned == tuning.Choice(32, 64, True)
+    assert ml.block_sizes(layer.desc) == (32, 64)
+    assert layer.desc.flags & ml.FLAG_SHRINK_LAUNCH
+    out = layer(t["x"], t["logits"], t["adapter_ids"])
+    torch.cuda.synchronize()
+    ids, w = oracle.route(case.logits, case.top_k)
+    ref = oracle.forward(case, ids, w)
+    mx, mean = metrics(out.cpu().numpy(), ref)
+    assert mx <= MAX_TOL and mean <= MEAN_TOL, (mx, mean)
+    assert layer.status() == 0
+
+
 def test_forward_rejects_small_workspace(dev):
     case = build_case("tiny")
     t = wl.device_tensors(case, dev)

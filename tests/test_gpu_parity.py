@@ -516,6 +516,19 @@ def test_tuning_table_choice_is_used_and_keeps_parity(dev, tmp_path):
     assert layer.status() == 0
 
 
+def test_tuner_writes_a_loadable_table(dev, tmp_path):
+    # the tuner end to end on the tiny shape: every candidate runs, the file
+    # it writes loads, and the stored choice is the fastest it measured
+    from lora_mixture_experts_amd import tune, tuning
+    log("tuner")
+    entry = tune.tune_workload("tiny", str(tmp_path), steps=5)
+    table = tuning.load(str(tmp_path))
+    c = wl.CONFIGS["tiny"]
+    got = table.lookup(c["T"], c["H"], c["I"], c["E"], c["top_k"], c["L"], c["r"])
+    assert got == tuning.Choice(entry["block_m_base"], entry["block_m_lora"], entry["shrink_launch"])
+    assert entry["us"] <= entry["us_library_default"]
+
+
 def test_forward_rejects_small_workspace(dev):
     case = build_case("tiny")
     t = wl.device_tensors(case, dev)

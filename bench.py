@@ -151,22 +151,23 @@ def run_workload(name, steps, warmup, rotate, dev, table=None):
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
+    # five repeats of the same `steps` calls; the reported time is their median
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev0.record()
-    for i in range(steps):
-        step(i)
-    ev1.record()
-    torch.cuda.synchronize()
-    ms = ev0.elapsed_time(ev1) / steps
-    # four more repeats of the same steps, for a median beside the timed value
-    repeats = [ms]
-    for _ in range(4):
+    repeats = []
+    for _ in range(5):
         ev0.record()
         for i in range(steps):
             step(i)
         ev1.record()
         torch.cuda.synchronize()
         repeats.append(ev0.elapsed_time(ev1) / steps)
+    ms = float(np.median(repeats))
+    # a call whose projection waves stopped waiting for the shrink waves of
+    # their launch produced no valid output: such a run is not a measurement
+    bad = [i for i, (layer, _) in enumerate(layers) if layer.status() != 0]
+    if bad:
+        raise SystemExit(f"[{name}] layer status word set on weight copies {bad}: the timed calls "
+                         "did not produce valid output")
 
     # per-kernel durations: HIP events recorded by the library around each
     # kernel on the launch stream, over a second pass of the same steps
@@ -204,7 +205,7 @@ def workload_summary(name, c, st, ms, kus, b, f, lb, lf, repeats_ms, launch=None
     gemm_us = kus["gemm_gate_up"] + kus["gemm_down"]
     out = {"workload": WORKLOAD_NAMES[name], "value": round(c.T / (ms * 1e-3), 1), "unit": "tokens/s",
            "us_per_call": round(ms * 1e3, 2),
-           "us_per_call_median_of_repeats": round(float(np.median(repeats_ms)) * 1e3, 2),
+           "us_per_call_repeats": [round(v * 1e3, 2) for v in repeats_ms],
            "layer_bound": "mfma" if mfma else "hbm",
            "layer_roofline_frac": round(roof_us / (ms * 1e3), 4),
            "kernel_us": {k: round(v, 2) for k, v in kus.items()}, "routing": st, "roofline": roof,
@@ -222,31 +223,37 @@ def workload_summary(name, c, st, ms, kus, b, f, lb, lf, repeats_ms, launch=None
     return out
 
 
-def cpu_baseline(case, ids, budget_s, single_budget_s):
+def cpu_baseline(case, budget_s, single_budget_s, chunk=None):
+    """The fp64 C oracle timed on the host cores over a bounded sample of the
+    workload: consecutive chunks of `chunk` tokens (default: the whole batch)
+    until `budget_s` seconds have passed."""
     import oracle
     ids_, w = oracle.route(case.logits, case.top_k)
     cores = oracle.default_threads()
-    n_tok = case.T
-    toks = np.arange(n_tok, dtype=np.int32)
+    n_tok = min(chunk or case.T, case.T)
 
     def timed(threads, budget):
-        # bounded sample: whole token batches until the time budget is used
-        done, t0 = 0, time.perf_counter()
+        done, t0, c = 0, time.perf_counter(), 0
         while True:
+            lo = (c * n_tok) % case.T
+            toks = np.arange(lo, min(lo + n_tok, case.T), dtype=np.int32)
             oracle.forward(case, ids_, w, tokens=toks, threads=threads)
-            done += n_tok
+            done += len(toks)
+            c += 1
             if time.perf_counter() - t0 >= budget:
                 break
         return done, time.perf_counter() - t0
 
     done, dt = timed(cores, budget_s)
+    what = (f"{done // n_tok} full {case.name} batches of {n_tok}" if n_tok == case.T
+            else f"{done // n_tok} chunks of {n_tok} consecutive tokens of the {case.T}-token {case.name} batch")
     out = dict(value=done / dt, unit="tokens/s", cores=cores, kind="oracle",
-               sample=f"{done} tokens ({done // n_tok} full {case.name} batches of {n_tok}) "
-                      f"through the fp64 C oracle in {dt:.1f}s")
+               us_per_call=round(case.T / (done / dt) * 1e6, 1),
+               sample=f"{done} tokens ({what}) through the fp64 C oracle in {dt:.1f}s")
     if single_budget_s > 0:
         d1, t1 = timed(1, single_budget_s)
         out["single_thread"] = dict(value=d1 / t1, unit="tokens/s", cores=1,
-                                    sample=f"{d1} tokens ({d1 // n_tok} full batches) in {t1:.1f}s")
+                                    sample=f"{d1} tokens in {t1:.1f}s")
     return out
 
 
@@ -308,7 +315,7 @@ def main():
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
         "us_per_call": main_obj["us_per_call"],
-        "us_per_call_median_of_repeats": main_obj["us_per_call_median_of_repeats"],
+        "us_per_call_repeats": main_obj["us_per_call_repeats"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic (seeded, N(0,1) activations/logits, N(0,0.02) weights)",
         "config": {"workload": WORKLOAD_NAMES[args.workload], "global_batch": case.T, "seq_len": 1,
@@ -322,16 +329,23 @@ def main():
         "roofline": main_obj["roofline"],
     }
     others = [w for w in args.also.split(",") if w and w != "none" and w != args.workload]
+    prefill_case = None
     for name in others:
         steps2 = max(5, args.steps // 5) if name in ("prefill", "many") else max(10, args.steps // 2)
         res = run_workload(name, steps2, max(2, args.warmup // 2), args.rotate, dev, table)
         obj = workload_summary(name, res[0], res[2], *res[3:])
         if name == "prefill":
             line["prefill"] = obj
+            prefill_case = res[0]
         else:
             line.setdefault("other_workloads", {})[name] = obj
+        del res
     if args.cpu_budget > 0:
-        line["cpu_baseline"] = cpu_baseline(case, ids, args.cpu_budget, args.cpu_single_budget)
+        line["cpu_baseline"] = cpu_baseline(case, args.cpu_budget, args.cpu_single_budget)
+        if prefill_case is not None:
+            # the prefill-shaped layer on the host: chunks of 400 tokens (a
+            # quarter of one 1600-token request) for about the same budget
+            line["prefill"]["cpu_baseline"] = cpu_baseline(prefill_case, args.cpu_budget, 0, chunk=400)
     print(json.dumps(line), flush=True)
 
 

@@ -7,7 +7,7 @@
 // MFMA K steps on the same accumulators, once per adapter present among the
 // block's rows: acc += S . B^T with S (the shrink output) split into a bf16
 // high part and a bf16 low part so that the rank-r product keeps ~16 bits of
-// S. This is the "LoRA add fused into the expand" of the AWS ML Blog post
+// S. This is the fusion of the LoRA addition into the expand from the AWS ML Blog post
 // "Efficiently serve dozens of fine-tuned models with vLLM on Amazon SageMaker
 // AI and Amazon Bedrock" (section "Kernel optimizations"), taken one step
 // further: the expand writes straight into the base accumulator in registers.

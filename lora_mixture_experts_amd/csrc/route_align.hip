@@ -4,10 +4,11 @@
 // Routing follows the AWS ML Blog post "Efficiently serve dozens of fine-tuned
 // models with vLLM on Amazon SageMaker AI and Amazon Bedrock", section
 // "Implementing multi-LoRA inference for MoE models in vLLM" (a router sends
-// each token to its most relevant experts). The alignment realises the
-// "additional grid dimension corresponding to the LoRA index" and the compound
-// sparsity of several adapters on top of expert routing (same post, section
-// "Tuning kernel configurations for Amazon SageMaker AI and Amazon Bedrock").
+// each token to its most relevant experts). The alignment groups the pairs by
+// expert and adapter slot at once, which gives the LoRA kernels their extra
+// launch axis over adapters and captures how adapter choice thins out the rows
+// of each expert further (same post, section "Tuning kernel configurations for
+// Amazon SageMaker AI and Amazon Bedrock").
 #include <algorithm>
 #include <climits>
 

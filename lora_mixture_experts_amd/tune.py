@@ -58,8 +58,11 @@ def time_choice(case, copies, out, choice, steps, warmup):
         e1.record()
         torch.cuda.synchronize()
         reps.append(e0.elapsed_time(e1) * 1000.0 / steps)
+    # a call whose projection waves stopped waiting for the shrink waves of
+    # their launch produced no valid output: such a choice is not a candidate
+    bad = any(layer.status() != 0 for layer in layers)
     del layers
-    return sorted(reps)[1]
+    return None if bad else sorted(reps)[1]
 
 
 def tune_workload(name, folder, rotate=3, steps=None):
@@ -78,16 +81,21 @@ def tune_workload(name, folder, rotate=3, steps=None):
         if ml.validate(d) != ml.OK:
             continue
         us = time_choice(case, copies, out, choice, steps, warmup=2 if heavy else 5)
-        results.append((us, choice))
         print(json.dumps({"workload": name, "block_m_base": choice[0], "block_m_lora": choice[1],
-                          "shrink_launch": choice[2], "us": round(us, 2)}), flush=True)
+                          "shrink_launch": choice[2], "us": None if us is None else round(us, 2)}),
+              flush=True)
+        if us is not None:
+            results.append((us, choice))
     d0 = ml.make_desc(case.T, case.H, case.I, case.E, case.top_k, case.L, case.r)
     default = ml.block_sizes(d0)
-    us_default = next(us for us, c in results if c == (default[0], default[1], False))
+    us_default = next((us for us, c in results if c == (default[0], default[1], False)), None)
+    if not results:
+        raise RuntimeError(f"{name}: no launch choice produced a valid call")
     us, best = min(results)
     shape = {k: getattr(case, k) for k in tuning.SHAPE_KEYS}
     entry = {"T_max": case.T, "block_m_base": best[0], "block_m_lora": best[1], "shrink_launch": best[2],
-             "us": round(us, 2), "us_library_default": round(us_default, 2)}
+             "us": round(us, 2),
+             "us_library_default": None if us_default is None else round(us_default, 2)}
     path = tuning.save_entry(folder, shape, entry)
     print(json.dumps({"workload": name, "best": entry, "file": os.path.relpath(path)}), flush=True)
     del copies, base

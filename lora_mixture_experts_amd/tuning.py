@@ -17,9 +17,12 @@ A folder holds one JSON file per layer shape (written by
      "entries": [{"T_max": 16, "block_m_base": 16, "block_m_lora": 16,
                   "shrink_launch": false, "us": 307.9}, ...]}
 
-For a call with T tokens the entry with the smallest ``T_max >= T`` applies;
-beyond the largest ``T_max`` the table has no advice and the library's own
-defaults apply.
+An entry covers the token counts ``T_min <= T <= T_max``; ``T_min`` is
+optional and defaults to ``T_max // 2 + 1``, so a choice tuned at one batch
+size is applied only to batches of about that size (the best block sizes
+follow the rows per expert, which grow with T). For a call with T tokens the
+covering entry with the smallest ``T_max`` applies; where no entry covers T
+the table has no advice and the library's own defaults apply.
 """
 from __future__ import annotations
 
@@ -46,12 +49,19 @@ def file_name(H, I, E, top_k, L, r):
     return f"H{H}_I{I}_E{E}_k{top_k}_L{L}_r{r}.json"
 
 
+def t_min_of(e) -> int:
+    """Smallest token count an entry covers."""
+    return int(e["T_min"]) if "T_min" in e else e["T_max"] // 2 + 1
+
+
 def _check_entry(e, where):
     for key in ("T_max", "block_m_base", "block_m_lora"):
         if not isinstance(e.get(key), int):
             raise ValueError(f"{where}: entry needs an integer {key!r}: {e}")
     if e["T_max"] < 1:
         raise ValueError(f"{where}: T_max must be >= 1: {e}")
+    if "T_min" in e and (not isinstance(e["T_min"], int) or not 1 <= e["T_min"] <= e["T_max"]):
+        raise ValueError(f"{where}: T_min must be an integer in [1, T_max]: {e}")
     for key in ("block_m_base", "block_m_lora"):
         if e[key] not in POW2_BLOCKS:
             raise ValueError(f"{where}: {key} must be one of {POW2_BLOCKS}: {e}")
@@ -75,7 +85,7 @@ class Table:
 
     def lookup(self, T, H, I, E, top_k, L, r) -> Choice | None:
         for e in self._by_shape.get(shape_key(H, I, E, top_k, L, r), []):
-            if T <= e["T_max"]:
+            if t_min_of(e) <= T <= e["T_max"]:
                 return Choice(e["block_m_base"], e["block_m_lora"], bool(e.get("shrink_launch", False)))
         return None
 

@@ -56,11 +56,12 @@ def build_case(name, dims=None, seed=None, touched_only=True):
     return wl.make_case(name, seed=seed, dims=dims, experts=experts, lora_blocks=blocks)
 
 
-def run_gpu(case, dev, bm_b=0, bm_l=0, shrink_launch=False):
+def run_gpu(case, dev, bm_b=0, bm_l=0, shrink_launch=False, tuning=None):
     t = wl.device_tensors(case, dev)
     layer = ml.Layer(case.T, case.H, case.I, case.E, case.top_k, case.L, case.r,
                      t["w_gate_up"], t["w_down"], t["a_gate_up"], t["b_gate_up"], t["a_down"],
-                     t["b_down"], block_m_base=bm_b, block_m_lora=bm_l, shrink_launch=shrink_launch)
+                     t["b_down"], block_m_base=bm_b, block_m_lora=bm_l, shrink_launch=shrink_launch,
+                     tuning=tuning)
     out = layer(t["x"], t["logits"], t["adapter_ids"])
     torch.cuda.synchronize()
     return layer, t, out
@@ -159,16 +160,28 @@ def test_align_parity(dev, name, dims, bm):
 
 # ----------------------------------------------------------------------------- the layer
 
-def check_layer(case, dev, ntok=64, bm=(0, 0), stages=False, shrink_launch=False):
+def check_layer(case, dev, bm=(0, 0), stages=False, stage_tokens=64, shrink_launch=False,
+                tuning=None, expect_choice=None):
+    """Run the layer through the C ABI and compare EVERY output element with
+    the oracle (max and mean bars over all T x H values); the alignment the
+    call used is compared bit for bit. With stages=True the intermediates of
+    a sample of stage_tokens tokens (first and last included) are checked
+    too."""
     ids, w = oracle.route(case.logits, case.top_k)
-    toks = sample_tokens(case, ntok)
-    layer, t, out = run_gpu(case, dev, *bm, shrink_launch=shrink_launch)
-    ref, st = oracle.forward(case, ids, w, tokens=toks, stages=True)
-    got = out.cpu().numpy()[toks]
-    mx, mean = metrics(got, ref)
-    log(f"  {case.name} bm={ml.block_sizes(layer.desc)} tokens={len(toks)}: max {mx:.2e} mean {mean:.2e}")
-    assert np.all(np.isfinite(got))
+    layer, t, out = run_gpu(case, dev, *bm, shrink_launch=shrink_launch, tuning=tuning)
+    got = out.cpu().numpy()
     assert layer.status() == 0
+    if tuning is not None:
+        # the layer ran the table's choice (None: no entry, library defaults)
+        assert layer.tuned == expect_choice
+        if expect_choice is not None:
+            assert ml.block_sizes(layer.desc) == (expect_choice.block_m_base, expect_choice.block_m_lora)
+            assert bool(layer.desc.flags & ml.FLAG_SHRINK_LAUNCH) == expect_choice.shrink_launch
+    ref = oracle.forward(case, ids, w)
+    mx, mean = metrics(got, ref)
+    log(f"  {case.name} bm={ml.block_sizes(layer.desc)} tuned={layer.tuned} all {case.T} tokens: "
+        f"max {mx:.2e} mean {mean:.2e}")
+    assert np.all(np.isfinite(got))
     assert mx <= MAX_TOL and mean <= MEAN_TOL, (mx, mean)
     # the alignment the forward pass used is the oracle's, bit for bit
     bb, bl = ml.block_sizes(layer.desc)
@@ -178,6 +191,8 @@ def check_layer(case, dev, ntok=64, bm=(0, 0), stages=False, shrink_launch=False
         np.testing.assert_array_equal(got_al[key], ref_al[key], err_msg=key)
     assert int(got_al["n_b"][0]) == ref_al["n_b"] and int(got_al["n_l"][0]) == ref_al["n_l"]
     if stages:
+        toks = sample_tokens(case, stage_tokens)
+        _, st = oracle.forward(case, ids, w, tokens=toks, stages=True)
         gs = {k: v.cpu() for k, v in layer.stages().items()}
         rows = (toks[:, None] * case.top_k + np.arange(case.top_k)[None, :]).reshape(-1)
         np.testing.assert_array_equal(gs["topk_ids"].numpy().reshape(case.T, case.top_k), ids)
@@ -185,6 +200,7 @@ def check_layer(case, dev, ntok=64, bm=(0, 0), stages=False, shrink_launch=False
         s2 = gs["s2"].numpy()[rows]
         h = gs["h"].float().numpy()[rows]
         dn = gs["dn"].numpy()[rows]
+        del gs
         if case.L > 0 and np.abs(st["s1"]).max() > 0:
             m1 = metrics(s1, st["s1"])
             assert m1[0] < 1e-4, ("s1", m1)
@@ -200,29 +216,30 @@ def check_layer(case, dev, ntok=64, bm=(0, 0), stages=False, shrink_launch=False
     return out
 
 
-@pytest.mark.parametrize("name", ["tiny", "decode", "wide"])
-def test_layer_parity_full(dev, name):
-    log(f"layer {name}")
+def _table():
+    from lora_mixture_experts_amd import tuning
+    return tuning.load(tuning.DEFAULT_FOLDER)
+
+
+@pytest.mark.parametrize("name", list(wl.CONFIGS))
+def test_layer_parity_as_benched(dev, name):
+    # each workload with the launch choice bench.py times: the committed
+    # tuning table's entry at this shape and token count where there is one,
+    # else the library defaults; every token is compared
+    from lora_mixture_experts_amd import tuning
+    log(f"layer {name} (as benched)")
+    table = _table()
     case = build_case(name)
-    check_layer(case, dev, ntok=case.T, stages=True)
+    choice = table.lookup(case.T, *(getattr(case, q) for q in tuning.SHAPE_KEYS))
+    check_layer(case, dev, stages=True, tuning=table, expect_choice=choice)
 
 
-def test_layer_parity_prefill_sampled(dev):
-    log("layer prefill")
-    case = build_case("prefill")
-    check_layer(case, dev, ntok=48, stages=True)
-
-
-def test_layer_parity_many_sampled(dev):
-    log("layer many")
-    case = build_case("many")
-    check_layer(case, dev, ntok=96, stages=True)
-
-
-def test_layer_parity_dense_sampled(dev):
-    # one expert, top-1: the dense multi-LoRA projection pair
-    log("layer dense")
-    check_layer(build_case("dense"), dev, ntok=4, stages=True)
+@pytest.mark.parametrize("name", ["decode", "wide", "dense"])
+def test_layer_parity_library_default(dev, name):
+    # the library's own defaults at the shapes where the committed table
+    # chooses differently (every token compared)
+    log(f"layer {name} (library defaults)")
+    check_layer(build_case(name), dev, stages=True)
 
 
 @pytest.mark.parametrize("bm", [(16, 16), (32, 16), (64, 64), (128, 32), (256, 256)])
@@ -230,7 +247,7 @@ def test_layer_block_sizes(dev, bm):
     log(f"layer block sizes {bm}")
     dims = dict(T=150, H=192, I=320, E=6, top_k=3, L=3, r=16)
     case = build_case("blocks", dims=dims, seed=5)
-    check_layer(case, dev, ntok=150, bm=bm, stages=True)
+    check_layer(case, dev, bm=bm, stages=True)
 
 
 @pytest.mark.parametrize("r,L,bm,pure", [(8, 3, 128, False), (64, 3, 128, True), (128, 2, 256, False),
@@ -248,7 +265,7 @@ def test_pipeline_expand(dev, r, L, bm, pure):
     if pure:
         case.w_gate_up[:] = 0
         case.w_down[:] = 0
-    check_layer(case, dev, ntok=dims["T"], bm=(bm, 16), stages=True)
+    check_layer(case, dev, bm=(bm, 16), stages=True)
 
 
 # 16-row base blocks run the two shrinks as producer waves inside the
@@ -276,8 +293,8 @@ def test_shrinks_inside_projections(dev, name, dims, bm, pure):
     if pure:
         case.w_gate_up[:] = 0
         case.w_down[:] = 0
-    out_f = check_layer(case, dev, ntok=case.T, bm=bm, stages=True)
-    out_s = check_layer(case, dev, ntok=case.T, bm=bm, stages=True, shrink_launch=True)
+    out_f = check_layer(case, dev, bm=bm, stages=True)
+    out_s = check_layer(case, dev, bm=bm, stages=True, shrink_launch=True)
     # the two agree far inside the oracle bars: they differ only in the
     # shrinks' fp32 summation order, which can move an h value across a bf16
     # rounding boundary (one bf16 step is 2^-8 of that value)
@@ -351,7 +368,7 @@ def test_layer_shapes(dev, i):
     dims = RANDOM_DIMS[i]
     log(f"layer shape {dims}")
     case = build_case(f"shape{i}", dims=dims, seed=40 + i)
-    check_layer(case, dev, ntok=dims["T"], stages=True)
+    check_layer(case, dev, stages=True)
 
 
 def test_layer_api_maxima(dev):
@@ -360,7 +377,7 @@ def test_layer_api_maxima(dev):
     log("layer maxima")
     dims = dict(T=24, H=64, I=128, E=1024, top_k=32, L=2, r=128)
     case = build_case("maxima", dims=dims, seed=77)
-    check_layer(case, dev, ntok=dims["T"], stages=True)
+    check_layer(case, dev, stages=True)
 
 
 def test_layer_foreign_adapter_ids(dev):
@@ -370,7 +387,7 @@ def test_layer_foreign_adapter_ids(dev):
     case = build_case("decode", touched_only=False)
     case.adapter_ids[::3] = case.L + 5
     case.adapter_ids[1::4] = -7
-    check_layer(case, dev, ntok=case.T, stages=True)
+    check_layer(case, dev, stages=True)
 
 
 def test_no_adapter_and_zero_b_agree(dev):
@@ -378,7 +395,7 @@ def test_no_adapter_and_zero_b_agree(dev):
     case = build_case("decode", touched_only=False)
     case.adapter_ids[:] = -1
     _, _, out_none = run_gpu(case, dev)
-    check_layer(case, dev, ntok=case.T)
+    check_layer(case, dev)
     case2 = build_case("decode", touched_only=False)
     case2.b_gate_up[:] = 0
     case2.b_down[:] = 0
@@ -393,14 +410,14 @@ def test_pure_lora(dev):
     case = build_case("decode")
     case.w_gate_up[:] = 0
     case.w_down[:] = 0
-    check_layer(case, dev, ntok=case.T, stages=True)
+    check_layer(case, dev, stages=True)
 
 
 def test_single_expert(dev):
     log("layer single expert")
     dims = dict(T=40, H=256, I=512, E=1, top_k=1, L=2, r=32)
     case = build_case("single", dims=dims, seed=9)
-    check_layer(case, dev, ntok=40, stages=True)
+    check_layer(case, dev, stages=True)
 
 
 def test_repeat_calls_reuse_workspace(dev):
@@ -498,7 +515,7 @@ def test_tuning_table_choice_is_used_and_keeps_parity(dev, tmp_path):
     log("tuning table")
     case = build_case("tiny")
     shape = {k: getattr(case, k) for k in tuning.SHAPE_KEYS}
-    tuning.save_entry(str(tmp_path), shape, {"T_max": 64, "block_m_base": 32, "block_m_lora": 64,
+    tuning.save_entry(str(tmp_path), shape, {"T_max": case.T, "block_m_base": 32, "block_m_lora": 64,
                                              "shrink_launch": True})
     table = tuning.load(str(tmp_path))
     t = wl.device_tensors(case, dev)

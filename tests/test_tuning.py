@@ -25,19 +25,59 @@ def test_round_trip_and_bucket_lookup(tmp_path):
     t = tuning.load(d)
     assert len(t) == 3
     args = [SHAPE[k] for k in tuning.SHAPE_KEYS]
-    # the smallest T_max >= T applies
-    assert t.lookup(1, *args) == tuning.Choice(16, 16, True)
+    # an entry covers (T_max / 2, T_max]
+    assert t.lookup(9, *args) == tuning.Choice(16, 16, True)
     assert t.lookup(16, *args) == tuning.Choice(16, 16, True)
-    assert t.lookup(17, *args) == tuning.Choice(64, 16, False)
+    assert t.lookup(257, *args) == tuning.Choice(64, 16, False)
+    assert t.lookup(512, *args) == tuning.Choice(64, 16, False)
     assert t.lookup(6400, *args) == tuning.Choice(128, 32, False)
-    # beyond the largest bucket, or another shape: no advice
-    assert t.lookup(6401, *args) is None
+    assert t.lookup(3201, *args) == tuning.Choice(128, 32, False)
+    # between entries, below the smallest, beyond the largest, or another
+    # shape: no advice (the library's defaults apply)
+    for T in (1, 8, 17, 32, 256, 513, 3200, 6401):
+        assert t.lookup(T, *args) is None, T
     assert t.lookup(16, 2880, 2880, 32, 4, 8, 64) is None
     # entries are kept sorted and replaced by T_max
     tuning.save_entry(d, SHAPE, entry(512, 32))
     t = tuning.load(d)
     assert [e["T_max"] for e in t.entries(*args)] == [16, 512, 6400]
-    assert t.lookup(100, *args) == tuning.Choice(32, 16, False)
+    assert t.lookup(300, *args) == tuning.Choice(32, 16, False)
+
+
+def test_explicit_t_min_widens_an_entry(tmp_path):
+    d = str(tmp_path)
+    e = entry(16, 16, sep=True)
+    e["T_min"] = 1
+    tuning.save_entry(d, SHAPE, e)
+    t = tuning.load(d)
+    args = [SHAPE[k] for k in tuning.SHAPE_KEYS]
+    assert t.lookup(1, *args) == tuning.Choice(16, 16, True)
+    assert t.lookup(17, *args) is None
+    for bad in (0, 17, "1"):
+        e["T_min"] = bad
+        with pytest.raises(ValueError):
+            tuning.save_entry(d, SHAPE, e)
+
+
+def test_a_call_between_committed_entries_gets_the_library_defaults():
+    # the committed decode/prefill shape has entries at T = 16 and 6400;
+    # a 32-token batch must not inherit the prefill choice (128-row blocks)
+    t = tuning.load(tuning.DEFAULT_FOLDER)
+    c = wl.CONFIGS["decode"]
+    args = [c[k] for k in tuning.SHAPE_KEYS]
+    assert t.lookup(16, *args) is not None and t.lookup(6400, *args) is not None
+    assert t.lookup(32, *args) is None
+
+
+def test_every_committed_entry_is_a_benched_workload():
+    # the GPU parity suite checks each committed entry at its own shape and
+    # token count through the workload of that shape; an entry no workload
+    # covers would be timed by no test
+    t = tuning.load(tuning.DEFAULT_FOLDER)
+    have = {(tuning.shape_key(*(d[k] for k in tuning.SHAPE_KEYS)), d["T"]) for d in wl.CONFIGS.values()}
+    for key in t.shapes():
+        for e in t.entries(*key):
+            assert (key, e["T_max"]) in have, (key, e)
 
 
 def test_files_are_named_by_shape(tmp_path):
@@ -47,7 +87,7 @@ def test_files_are_named_by_shape(tmp_path):
     assert doc["shape"] == SHAPE and doc["device"] == "gfx950"
 
 
-@pytest.mark.parametrize("bad", [dict(block_m_base=48), dict(block_m_lora=8), dict(T_max=0),
+@pytest.mark.parametrize("bad", [dict(block_m_base=48), dict(block_m_lora=8), dict(T_max=0), dict(T_min=0),
                                  dict(shrink_launch="yes"), dict(block_m_base=None)])
 def test_invalid_entries_are_rejected(tmp_path, bad):
     e = entry(16, 16)

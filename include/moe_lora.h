@@ -40,6 +40,8 @@ extern "C" {
 #define MOE_LORA_EINVAL (-1)     /* bad dimension, null/misaligned pointer, bad block size */
 #define MOE_LORA_EWORKSPACE (-2) /* workspace smaller than moe_lora_workspace_bytes() */
 #define MOE_LORA_EHIP (-3)       /* a HIP launch or runtime call failed */
+#define MOE_LORA_ESCRATCH (-4)   /* moe_lora_forward_noalloc: the call needs more than
+                                    MOE_LORA_SCRATCH_BYTES of scratch */
 
 /* Shape of one layer call.
  *   T tokens (T == 0 is a no-op), H hidden size, I expert intermediate size
@@ -148,6 +150,33 @@ int moe_lora_align(const moe_lora_desc *d, const int32_t *topk_ids, const int32_
 int moe_lora_forward(const moe_lora_desc *d, const moe_lora_weights *w, const void *x,
                      const float *logits, const int32_t *adapter_ids, void *out,
                      void *workspace, size_t ws_bytes, void *stream);
+
+/* The whole layer without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). Same arguments, results and errors as
+ * moe_lora_forward, which it shares every kernel with, except that the
+ * intermediates live in a static device array of the library
+ * (MOE_LORA_SCRATCH_BYTES = 64 MiB, 256-byte aligned; each GPU the library
+ * runs on holds its own copy from module load until the process ends).
+ *  - The call allocates nothing and calls no allocating routine. Its first
+ *    call on a device looks up that device's address of the array (a host
+ *    call, once per device, with the device current).
+ *  - It works on the CURRENT device: a non-null `stream` must belong to it
+ *    (else MOE_LORA_EINVAL).
+ *  - A call whose moe_lora_workspace_bytes() exceeds MOE_LORA_SCRATCH_BYTES
+ *    returns MOE_LORA_ESCRATCH and enqueues nothing (e.g. the decode-sized
+ *    batches of the hidden = intermediate = 2880, 32-expert layer fit up to
+ *    about 100 tokens; a 6400-token prefill batch does not).
+ *  - Every call on one GPU shares that GPU's array, which keeps the last
+ *    call's contents (each call re-initialises what it reads: the routing
+ *    launch clears its counters and status word, the alignment fills both
+ *    views to capacity). Calls that may overlap on one GPU (different
+ *    streams, or host threads without ordering) RACE on the array: order
+ *    them on one stream. The read-back calls below do not apply to it. */
+#define MOE_LORA_SCRATCH_BYTES ((size_t)64 << 20)
+int moe_lora_forward_noalloc(const moe_lora_desc *d, const moe_lora_weights *w, const void *x,
+                             const float *logits, const int32_t *adapter_ids, void *out,
+                             void *stream);
 
 /* Copy intermediates of the last moe_lora_forward on `workspace` out in pair
  * order (row p = t*k + j); any output may be NULL.

@@ -5,6 +5,7 @@
 #include <algorithm>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "../../include/moe_lora.h"
@@ -170,6 +171,7 @@ const char* moe_lora_strerror(int code) {
         case MOE_LORA_EINVAL: return "invalid argument (dimension, pointer, alignment or block size)";
         case MOE_LORA_EWORKSPACE: return "workspace too small";
         case MOE_LORA_EHIP: return "HIP runtime or launch error";
+        case MOE_LORA_ESCRATCH: return "call needs more scratch than the library's static buffer holds";
         default: return "unknown error";
     }
 }
@@ -239,19 +241,15 @@ int moe_lora_align(const moe_lora_desc* d, const int32_t* topk_ids, const int32_
                : MOE_LORA_EHIP;
 }
 
-int moe_lora_forward(const moe_lora_desc* d, const moe_lora_weights* w, const void* x,
-                     const float* logits, const int32_t* adapter_ids, void* out,
-                     void* workspace, size_t ws_bytes, void* stream) {
-    Plan p;
-    int rc = make_plan(d, &p);
-    if (rc) return rc;
-    if ((rc = check_weights(d, w))) return rc;
-    if (p.T == 0) return MOE_LORA_OK;
-    if (!x || !logits || !adapter_ids || !out || !workspace) return MOE_LORA_EINVAL;
-    if (!aligned16(x) || !aligned16(out) || (reinterpret_cast<uintptr_t>(workspace) % kAlign))
-        return MOE_LORA_EINVAL;
-    if (ws_bytes < p.total) return MOE_LORA_EWORKSPACE;
-    hipStream_t s = static_cast<hipStream_t>(stream);
+}  // extern "C"
+
+namespace {
+
+// The launch sequence of one layer call on a checked plan; `workspace` holds
+// at least p.total bytes, 256-byte aligned.
+int forward_planned(const Plan& p, const moe_lora_desc* d, const moe_lora_weights* w, const void* x,
+                    const float* logits, const int32_t* adapter_ids, void* out, void* workspace,
+                    hipStream_t s) {
 
     int32_t* ids = at<int32_t>(workspace, p.off_ids);
     float* tw = at<float>(workspace, p.off_w);
@@ -344,6 +342,76 @@ int moe_lora_forward(const moe_lora_desc* d, const moe_lora_weights* w, const vo
                       (d->flags & MOE_LORA_FLAG_OUT_BF16) != 0, s));
     timing_mark(call, 7, s);
     return e == hipSuccess ? MOE_LORA_OK : MOE_LORA_EHIP;
+}
+
+// Checks shared by both forward entry points (everything but the workspace).
+int check_forward(const moe_lora_desc* d, const moe_lora_weights* w, const void* x, const float* logits,
+                  const int32_t* adapter_ids, const void* out, Plan* p) {
+    int rc = make_plan(d, p);
+    if (rc) return rc;
+    if ((rc = check_weights(d, w))) return rc;
+    if (p->T == 0) return MOE_LORA_OK;
+    if (!x || !logits || !adapter_ids || !out) return MOE_LORA_EINVAL;
+    if (!aligned16(x) || !aligned16(out)) return MOE_LORA_EINVAL;
+    return MOE_LORA_OK;
+}
+
+// ---- the static scratch of moe_lora_forward_noalloc ------------------------
+// Every GPU the library runs on holds one copy of this array from module load
+// until the process ends. In host code `scratch` names a host-side stand-in,
+// not device memory: its device address is looked up once per device with
+// hipGetSymbolAddress, and only that address is ever handed to a kernel.
+__device__ __attribute__((aligned(256))) uint8_t scratch[MOE_LORA_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's address of `scratch` (looked up on the first call on
+// that device), or null on a HIP error.
+void* scratch_address(int dev) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+        g_scratch_ptr[dev] = ptr;
+    }
+    return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_lora_forward(const moe_lora_desc* d, const moe_lora_weights* w, const void* x,
+                     const float* logits, const int32_t* adapter_ids, void* out,
+                     void* workspace, size_t ws_bytes, void* stream) {
+    Plan p;
+    const int rc = check_forward(d, w, x, logits, adapter_ids, out, &p);
+    if (rc || p.T == 0) return rc;
+    if (!workspace || (reinterpret_cast<uintptr_t>(workspace) % kAlign)) return MOE_LORA_EINVAL;
+    if (ws_bytes < p.total) return MOE_LORA_EWORKSPACE;
+    return forward_planned(p, d, w, x, logits, adapter_ids, out, workspace, static_cast<hipStream_t>(stream));
+}
+
+int moe_lora_forward_noalloc(const moe_lora_desc* d, const moe_lora_weights* w, const void* x,
+                             const float* logits, const int32_t* adapter_ids, void* out, void* stream) {
+    Plan p;
+    const int rc = check_forward(d, w, x, logits, adapter_ids, out, &p);
+    if (rc || p.T == 0) return rc;
+    if (p.total > MOE_LORA_SCRATCH_BYTES) return MOE_LORA_ESCRATCH;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_LORA_EHIP;
+    if (s) {
+        // the scratch address is the current device's: the stream must be on it
+        int sdev = -1;
+        if (hipStreamGetDevice(s, &sdev) != hipSuccess) return MOE_LORA_EHIP;
+        if (sdev != dev) return MOE_LORA_EINVAL;
+    }
+    void* ws = scratch_address(dev);
+    if (!ws) return MOE_LORA_EHIP;
+    return forward_planned(p, d, w, x, logits, adapter_ids, out, ws, s);
 }
 
 int moe_lora_read_stages(const moe_lora_desc* d, const void* workspace, size_t ws_bytes,

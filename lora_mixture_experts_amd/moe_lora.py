@@ -12,7 +12,8 @@ import os
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmoelora.so")
 
-OK, EINVAL, EWORKSPACE, EHIP = 0, -1, -2, -3
+OK, EINVAL, EWORKSPACE, EHIP, ESCRATCH = 0, -1, -2, -3, -4
+SCRATCH_BYTES = 64 << 20
 FLAG_OUT_BF16 = 1
 FLAG_SHRINK_LAUNCH = 2
 NKERNELS = 7
@@ -57,6 +58,7 @@ def lib():
             "moe_lora_route": ([pD, P, P, P, P], ctypes.c_int),
             "moe_lora_align": ([pD, P, P, P, P, P, P, P, P, P, P], ctypes.c_int),
             "moe_lora_forward": ([pD, pW, P, P, P, P, P, SZ, P], ctypes.c_int),
+            "moe_lora_forward_noalloc": ([pD, pW, P, P, P, P, P], ctypes.c_int),
             "moe_lora_read_stages": ([pD, P, SZ, P, P, P, P, P, P, P], ctypes.c_int),
             "moe_lora_read_alignment": ([pD, P, SZ, P, P, P, P, P, P, P, P], ctypes.c_int),
             "moe_lora_read_status": ([pD, P, SZ, P, P], ctypes.c_int),
@@ -74,7 +76,8 @@ def lib():
 
 EXPORTED = ("moe_lora_strerror", "moe_lora_validate", "moe_lora_block_sizes",
             "moe_lora_workspace_bytes", "moe_lora_align_capacity", "moe_lora_route",
-            "moe_lora_align", "moe_lora_forward", "moe_lora_read_stages", "moe_lora_read_alignment",
+            "moe_lora_align", "moe_lora_forward", "moe_lora_forward_noalloc", "moe_lora_read_stages",
+            "moe_lora_read_alignment",
             "moe_lora_read_status",
             "moe_lora_timing_enable", "moe_lora_timing_read", "moe_lora_kernel_name")
 
@@ -153,6 +156,13 @@ def forward(desc, weights: Weights, x, logits, adapter_ids, out, workspace, stre
                                   _ptr(adapter_ids), _ptr(out), _ptr(workspace),
                                   ctypes.c_size_t(workspace.numel() * workspace.element_size()),
                                   _stream(stream)), "forward")
+
+
+def forward_noalloc(desc, weights: Weights, x, logits, adapter_ids, out, stream=None):
+    """The layer with the library's static scratch instead of a workspace
+    (include/moe_lora.h, moe_lora_forward_noalloc)."""
+    _check(lib().moe_lora_forward_noalloc(ctypes.byref(desc), ctypes.byref(weights), _ptr(x), _ptr(logits),
+                                          _ptr(adapter_ids), _ptr(out), _stream(stream)), "forward_noalloc")
 
 
 def read_stages(desc, workspace, topk_ids=None, topk_w=None, s1=None, h=None, s2=None, dn=None,

@@ -120,3 +120,35 @@ def test_strerror_text():
     assert "workspace" in ml.strerror(ml.EWORKSPACE)
     assert ml.strerror(ml.OK) == "ok"
     assert ml.kernel_names()[0] == "route" and len(ml.kernel_names()) == ml.NKERNELS
+
+
+def _noalloc_rc(ds):
+    # fake, 16-byte aligned device addresses: every refusal tested here is
+    # decided on the host before any HIP call or launch
+    lib = ml.lib()
+    p = ctypes.c_void_p(4096)
+    return lib.moe_lora_forward_noalloc(ctypes.byref(ds), ctypes.byref(ml.Weights(*([4096] * 6))),
+                                        p, p, p, p, None)
+
+
+def test_noalloc_refuses_oversized_and_invalid_calls_on_the_host():
+    assert "scratch" in ml.strerror(ml.ESCRATCH)
+    c = wl.CONFIGS["prefill"]
+    big = ml.make_desc(c["T"], c["H"], c["I"], c["E"], c["top_k"], c["L"], c["r"])
+    assert ml.workspace_bytes(big) > ml.SCRATCH_BYTES
+    assert _noalloc_rc(big) == ml.ESCRATCH
+    assert _noalloc_rc(desc(H=2881)) == ml.EINVAL
+    assert _noalloc_rc(desc(T=0)) == ml.OK  # a no-op
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode", "wide", "dense"])
+def test_decode_sized_workloads_fit_the_static_scratch(name):
+    d = wl.CONFIGS[name]
+    ds = ml.make_desc(d["T"], d["H"], d["I"], d["E"], d["top_k"], d["L"], d["r"])
+    assert ml.workspace_bytes(ds) <= ml.SCRATCH_BYTES
+
+
+def test_header_scratch_size_matches_binding():
+    src = open(HEADER).read()
+    m = re.search(r"#define MOE_LORA_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", src)
+    assert m and int(m.group(1)) << int(m.group(2)) == ml.SCRATCH_BYTES

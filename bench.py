@@ -91,17 +91,31 @@ def shrinks_fused(kus):
     return all(kus.get(s, 0.0) == 0.0 for s in SHRINK_OF.values())
 
 
-def fold_fused(kus, b, f):
+def combine_fused(kus):
+    """True when the weighted combine had no launch of its own (the down
+    projection added its weighted rows into the output: the library reports
+    0 us for the combine)."""
+    return kus.get("combine", 0.0) == 0.0
+
+
+def fold_fused(kus, b, f, T=None, H=None, P=None):
     """Per-kernel bytes/flops with each shrink's work counted in the
     projection launch that ran it (when the shrinks have no launch of their
-    own)."""
-    if not shrinks_fused(kus):
-        return b, f
+    own), and, when the combine is folded into the down projection, that
+    launch writing the fp32 output [T][H] once instead of its fp32 rows
+    [P][H] (the routing launch then also clears the output)."""
     b, f = dict(b), dict(f)
-    for g, s in SHRINK_OF.items():
-        b[g] += b.pop(s)
-        f[g] += f.pop(s)
-        b[s] = f[s] = 0
+    if shrinks_fused(kus):
+        for g, s in SHRINK_OF.items():
+            b[g] += b.pop(s)
+            f[g] += f.pop(s)
+            b[s] = f[s] = 0
+    if combine_fused(kus) and T is not None:
+        # drop the fp32 rows [P][H]; write out [T][H] once and read the P
+        # routing weights; the routing launch's clearing of out is its own
+        b["gemm_down"] += -P * H * 4 + T * H * 4 + P * 4
+        b["route"] += T * H * 4
+        b["combine"] = 0
     return b, f
 
 
@@ -141,6 +155,8 @@ def run_workload(name, steps, warmup, rotate, dev, table=None):
     bm_b, bm_l = ml.block_sizes(layer0.desc)
     launch = {"block_m_base": bm_b, "block_m_lora": bm_l,
               "shrink_launch": bool(layer0.desc.flags & ml.FLAG_SHRINK_LAUNCH),
+              "combine": ("own launch, fixed order" if layer0.keeps_down_rows
+                          else "in the down projection's epilogue (fp32 atomic adds)"),
               "from_tuning_table": layer0.tuned is not None}
     out = torch.empty((case.T, case.H), dtype=torch.float32, device=dev)
 
@@ -187,7 +203,7 @@ def run_workload(name, steps, warmup, rotate, dev, table=None):
 def workload_summary(name, c, st, ms, kus, b, f, lb, lf, repeats_ms, launch=None):
     """One workload's object: throughput, per-kernel times, layer roofline and
     the dominant projection kernel against its bound."""
-    b, f = fold_fused(kus, b, f)
+    b, f = fold_fused(kus, b, f, c.T, c.H, c.T * c.top_k)
     dom = max(("gemm_gate_up", "gemm_down"), key=lambda n: kus[n])
     mfma = lf / lb > RIDGE_FLOP_PER_BYTE
     roof_us = max(lb / (HBM_PEAK_GBS * 1e9), lf / (BF16_PEAK_TFLOPS * 1e12)) * 1e6

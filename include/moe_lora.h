@@ -57,9 +57,23 @@ extern "C" {
  *                                   their own even where the library would run
  *                                   them inside the projection launches (for
  *                                   comparison; the results agree to rounding)
+ *     MOE_LORA_FLAG_FUSED_COMBINE   fold the weighted top_k sum into the down
+ *                                   projection: `out` (fp32) is cleared by the
+ *                                   call's first launch and each down row adds
+ *                                   w * row into its token's output row with
+ *                                   fp32 atomic adds. The order of those adds
+ *                                   varies from call to call, so the last bits
+ *                                   of `out` may differ between calls when
+ *                                   top_k > 2. Without the flag the down
+ *                                   projection stores its fp32 rows and a
+ *                                   launch of its own sums each token's rows in
+ *                                   a fixed order: bitwise repeatable (and
+ *                                   faster on MI355X at every measured shape).
+ *                                   Not with OUT_BF16.
  *   any other bit is an error. */
 #define MOE_LORA_FLAG_OUT_BF16 1
 #define MOE_LORA_FLAG_SHRINK_LAUNCH 2
+#define MOE_LORA_FLAG_FUSED_COMBINE 4
 typedef struct moe_lora_desc {
     int32_t T, H, I, E, top_k, L, r;
     int32_t block_m_base, block_m_lora;
@@ -138,7 +152,10 @@ int moe_lora_align(const moe_lora_desc *d, const int32_t *topk_ids, const int32_
  *               this call until the next call that uses it.
  * The gate_up and down LoRA expands add into the base projections' results
  * inside the projection kernels (AWS post, section "Kernel optimizations":
- * the LoRA add is fused into the expand). With 16-row base blocks (few rows
+ * the LoRA add is fused into the expand). The chosen experts' outputs are
+ * then aggregated (AWS post, section "Implementing multi-LoRA inference for
+ * MoE models in vLLM") by a fixed-order launch, or inside the down projection
+ * with MOE_LORA_FLAG_FUSED_COMBINE. With 16-row base blocks (few rows
  * per expert, the default when T*top_k/E <= 8) and at most 1024 producer
  * waves (LoRA-view block capacity x ceil(r/16) x K ranges of up to 4096),
  * the LoRA shrinks run inside the projection launches too, as producer waves
@@ -184,7 +201,10 @@ int moe_lora_forward_noalloc(const moe_lora_desc *d, const moe_lora_weights *w, 
  *   s1 f32 [P][r]  gate_up shrink x.A^T   (0 rows for pairs without adapter)
  *   h  bf16 [P][I] activation as fed to the down projection
  *   s2 f32 [P][r]  down shrink h.A^T       (0 rows for pairs without adapter)
- *   dn f32 [P][H]  down projection output incl. LoRA, before the weighting */
+ *   dn f32 [P][H]  down projection output incl. LoRA, before the weighting;
+ *                  not kept with MOE_LORA_FLAG_FUSED_COMBINE (then a non-NULL
+ *                  dn is MOE_LORA_EINVAL: the down projection added its rows
+ *                  into out directly) */
 int moe_lora_read_stages(const moe_lora_desc *d, const void *workspace, size_t ws_bytes,
                          int32_t *topk_ids, float *topk_w, float *s1, uint16_t *h,
                          float *s2, float *dn, void *stream);

@@ -26,6 +26,7 @@ struct Plan {
     int ksplit;  // K ranges of the down projection (partial sums summed by the combine)
     int ssplit;  // K ranges of the two shrinks (partials summed by the projection kernels)
     bool fused;  // the shrinks run as producer waves inside the projection launches
+    bool fuse_combine;  // the down projection adds its weighted rows into out (no D, no combine launch)
     size_t off_ids, off_w, off_sorted_b, off_blk_e_b, off_counts, off_sorted_l, off_blk_e_l,
         off_blk_a_l, off_slot, off_lslot, off_sad, off_defer, off_s1, off_s2, off_s1hl, off_s2hl,
         off_h, off_d, total;
@@ -59,7 +60,9 @@ int check_desc(const moe_lora_desc* d) {
     if (d->E > 1024 || d->top_k < 1 || d->top_k > d->E || d->top_k > 32) return MOE_LORA_EINVAL;
     if (d->L > 0 && !(d->r == 8 || d->r == 16 || d->r == 32 || d->r == 64 || d->r == 128))
         return MOE_LORA_EINVAL;
-    if (d->flags & ~(MOE_LORA_FLAG_OUT_BF16 | MOE_LORA_FLAG_SHRINK_LAUNCH)) return MOE_LORA_EINVAL;
+    if (d->flags & ~(MOE_LORA_FLAG_OUT_BF16 | MOE_LORA_FLAG_SHRINK_LAUNCH | MOE_LORA_FLAG_FUSED_COMBINE))
+        return MOE_LORA_EINVAL;
+    if ((d->flags & MOE_LORA_FLAG_FUSED_COMBINE) && (d->flags & MOE_LORA_FLAG_OUT_BF16)) return MOE_LORA_EINVAL;
     if (d->block_m_base != 0 && !pow2_in(d->block_m_base, 16, 256)) return MOE_LORA_EINVAL;
     if (d->block_m_lora != 0 && !pow2_in(d->block_m_lora, 16, 256)) return MOE_LORA_EINVAL;
     const long P = static_cast<long>(d->T) * d->top_k;
@@ -85,6 +88,12 @@ int make_plan(const moe_lora_desc* d, Plan* p) {
     p->nblk_b = p->C_b / p->bm_b;
     p->nblk_l = p->C_l / p->bm_l;
     p->ksplit = gemm_down_ksplit(p->H, p->I, p->bm_b, p->nblk_b);
+    // the weighted combine runs in the down projection's epilogue (fp32
+    // atomic adds into out) only on request: the atomics cost the down
+    // projection more than the fixed-order combine launch takes at every
+    // measured shape (decode-shaped layer +7 against 4.5 us, prefill-shaped
+    // +585 against 67 us)
+    p->fuse_combine = (d->flags & MOE_LORA_FLAG_FUSED_COMBINE) != 0;
     // 16-row base blocks (few rows per expert: the projections stream their
     // weights) run the shrinks inside the projection launches, as long as
     // the producer waves stay a small share of the machine (at most about
@@ -125,7 +134,7 @@ int make_plan(const moe_lora_desc* d, Plan* p) {
     p->off_s1hl = take(hlbytes);
     p->off_s2hl = take(hlbytes);
     p->off_h = take(2ul * p->C_b * p->I);
-    p->off_d = take(4ul * p->ksplit * p->C_b * p->H);
+    p->off_d = take(p->fuse_combine ? 0 : 4ul * p->ksplit * p->C_b * p->H);
     p->total = o;
     return MOE_LORA_OK;
 }
@@ -273,6 +282,7 @@ int forward_planned(const Plan& p, const moe_lora_desc* d, const moe_lora_weight
         const bool shrink_launched = p.L > 0 && !p.fused;
         uint8_t* l = &g_timing.launched[static_cast<size_t>(call) * MOE_LORA_NKERNELS];
         l[2] = l[4] = shrink_launched ? 1 : 0;  // shrink_gate_up, shrink_down
+        l[6] = p.fuse_combine ? 0 : 1;          // combine
     }
 
     hipError_t e = hipSuccess;
@@ -281,7 +291,8 @@ int forward_planned(const Plan& p, const moe_lora_desc* d, const moe_lora_weight
     // counts[0..1]: n_b, n_l (alignment); counts[2..3]: producer counts of
     // the two projections; counts[4]: the call's status word; 2..4 are
     // zeroed by the routing launch
-    ok(launch_route(logits, p.T, p.E, p.k, ids, tw, s, counts + 2, 3));
+    ok(launch_route(logits, p.T, p.E, p.k, ids, tw, s, counts + 2, 3,
+                    p.fuse_combine ? static_cast<float*>(out) : nullptr, p.H));
     timing_mark(call, 1, s);
     ok(launch_align(ids, adapter_ids, p.T, p.k, p.E, p.L, p.bm_b, p.bm_l, p.C_b, p.C_l, sorted_b,
                     blk_e_b, counts, sorted_l, blk_e_l, blk_a_l, counts + 1, slot, lslot, sad,
@@ -331,6 +342,11 @@ int forward_planned(const Plan& p, const moe_lora_desc* d, const moe_lora_weight
     ga.X = h; ga.gate_up = 0; ga.W = static_cast<const uint16_t*>(w->w_down); ga.N_out = p.H;
     ga.K = p.I; ga.S = s2; ga.Bl = static_cast<const uint16_t*>(w->b_down); ga.ksplit = p.ksplit;
     ga.S_hl = s2hl;
+    if (p.fuse_combine) {
+        ga.out_acc = static_cast<float*>(out);
+        ga.topk_w = tw;
+        ga.d_out = nullptr;
+    }
     if (p.fused) {
         ga.gather_token = 0; ga.Al = static_cast<const uint16_t*>(w->a_down);
         ga.S_out = s2; ga.done = counts + 3;
@@ -338,8 +354,9 @@ int forward_planned(const Plan& p, const moe_lora_desc* d, const moe_lora_weight
     ok(launch_gemm(ga, s));
     timing_mark(call, 6, s);
 
-    ok(launch_combine(dn, p.ksplit, p.C_b, slot, tw, p.T, p.k, p.H, out,
-                      (d->flags & MOE_LORA_FLAG_OUT_BF16) != 0, s));
+    if (!p.fuse_combine)
+        ok(launch_combine(dn, p.ksplit, p.C_b, slot, tw, p.T, p.k, p.H, out,
+                          (d->flags & MOE_LORA_FLAG_OUT_BF16) != 0, s));
     timing_mark(call, 7, s);
     return e == hipSuccess ? MOE_LORA_OK : MOE_LORA_EHIP;
 }
@@ -423,6 +440,7 @@ int moe_lora_read_stages(const moe_lora_desc* d, const void* workspace, size_t w
     if (p.T == 0) return MOE_LORA_OK;
     if (!workspace) return MOE_LORA_EINVAL;
     if (ws_bytes < p.total) return MOE_LORA_EWORKSPACE;
+    if (dn && p.fuse_combine) return MOE_LORA_EINVAL;  // D is not kept
     hipStream_t s = static_cast<hipStream_t>(stream);
     void* ws = const_cast<void*>(workspace);
     const int32_t* slot = at<int32_t>(ws, p.off_slot);

@@ -15,7 +15,9 @@
 // gate_up: the tile's 16-column fragments alternate gate / up for the same
 // activation columns, so every lane holds matching gate and up values and the
 // SwiGLU epilogue h = silu(gate) * up runs in registers; h is stored in bf16.
-// down: the fp32 result is stored per base slot for the weighted combine.
+// down: the fp32 result is either stored per base slot for the weighted
+// combine launch, or weighted by the routing weight and added atomically into
+// the layer output (the combine folded into this epilogue).
 #include <algorithm>
 #include <type_traits>
 
@@ -32,6 +34,19 @@ __device__ __forceinline__ int w_row_of_frag(int f, int c0, int I) {
 }
 
 __device__ __forceinline__ int row_adapter(const GemmArgs& a, int slot) { return a.slot_adapter[slot]; }
+
+// Down epilogue with the weighted combine folded in: rows 4 i .. 4 i + 3 of a
+// 16 x 16 fragment (base slots slot0 + i, this lane's column col) add
+// w_p * value into out[t] (p = the slot's pair, t = p / top_k); padding slots
+// add nothing. fp32 atomic adds at the L2, with no return value.
+__device__ __forceinline__ void combine_rows(const GemmArgs& a, int slot0, int col, const f32x4& v) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int p = a.sorted_b[slot0 + i];
+        if (p < a.P)
+            unsafeAtomicAdd(a.out_acc + static_cast<size_t>(p / a.top_k) * a.N_out + col, a.topk_w[p] * v[i]);
+    }
+}
 
 // S row chunk (8 values starting at j0) as hi/lo bf16 operands; zero when the
 // row is not in the current adapter run or j is past r. COHERENT: S was
@@ -384,6 +399,9 @@ __global__ __launch_bounds__(64) void k_gemm_skinny(GemmArgs a) {
                 a.h_out[static_cast<size_t>(orow0 + i) * a.N_out + col] =
                     f32_to_bf16_rne(silu(acc[2 * u][i]) * acc[2 * u + 1][i]);
         }
+    } else if (a.out_acc) {
+#pragma unroll
+        for (int f = 0; f < FN; ++f) combine_rows(a, orow0, c0 + 16 * f + lrow, acc[f]);
     } else {
         float* dpart = a.d_out + static_cast<size_t>(z) * a.C_b * a.N_out;
 #pragma unroll
@@ -504,6 +522,12 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& a, f32x4 (&acc)[FM
                 for (int q = 0; q < 4; ++q)
                     a.h_out[static_cast<size_t>(orow0 + q) * a.N_out + col] =
                         f32_to_bf16_rne(silu(acc[i][j][q]) * acc[i][j + 1][q]);
+            }
+        } else if (a.out_acc) {
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int col = c0 + 16 * (wn * FN + j) + lrow;
+                if (col < a.N_out) combine_rows(a, orow0, col, acc[i][j]);
             }
         } else {
             float* dpart = a.d_out + static_cast<size_t>(z) * a.C_b * a.N_out;

@@ -7,9 +7,11 @@
 namespace moelora {
 
 // ---- route + align --------------------------------------------------------
-// zero_words[0 .. n_zero) are set to 0 by the same launch (n_zero <= 256).
+// zero_words[0 .. n_zero) are set to 0 by the same launch (n_zero <= 256);
+// with zero_out, rows 0..T-1 of zero_out [T][H] (fp32) are set to 0 too.
 hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* w,
-                        hipStream_t s, int32_t* zero_words = nullptr, int n_zero = 0);
+                        hipStream_t s, int32_t* zero_words = nullptr, int n_zero = 0,
+                        float* zero_out = nullptr, int H = 0);
 
 // Whether the alignment kernel's LDS holds the key counts of E experts x
 // (L adapters + none) together with at least one histogram row.
@@ -86,6 +88,11 @@ struct GemmArgs {
     // outputs
     uint16_t* h_out;          // [C_b][I]
     float* d_out;             // [ksplit][C_b][H] partial sums over K ranges (down)
+    // down only, instead of d_out: the weighted combine in the epilogue;
+    // out_acc[t][c] += topk_w[p] * D[p][c] for every real row p = t*top_k + j
+    // (fp32 atomic adds into a zeroed out_acc [T][H])
+    float* out_acc;
+    const float* topk_w;
     int ksplit;               // down only: the K range is cut into ksplit equal parts
     // optional bf16 hi/lo copy of S (see ShrinkArgs); the direct-load kernel
     // then runs the expand as extra stages of its LDS pipeline

@@ -26,11 +26,19 @@ constexpr int kRouteMaxPerLane = 16;  // E <= 1024
 __global__ __launch_bounds__(256) void k_route(const float* __restrict__ logits, int T, int E,
                                                int k, int32_t* __restrict__ ids,
                                                float* __restrict__ w,
-                                               int32_t* __restrict__ zero_words, int n_zero) {
+                                               int32_t* __restrict__ zero_words, int n_zero,
+                                               float* __restrict__ zero_out, int H) {
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     // counters that later kernels of the same call count up from zero
     if (blockIdx.x == 0 && threadIdx.x < n_zero) zero_words[threadIdx.x] = 0;
+    // the output rows of this workgroup's tokens, when the down projection
+    // adds its weighted rows into them
+    if (zero_out) {
+        const int t0 = blockIdx.x * 4, nt = min(4, T - t0);
+        f32x4* o = reinterpret_cast<f32x4*>(zero_out + static_cast<size_t>(t0) * H);
+        for (int i = threadIdx.x; i < nt * H / 4; i += 256) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
     if (t >= T) return;
     const float* row = logits + static_cast<size_t>(t) * E;
     const int nper = (E + 63) >> 6;
@@ -84,11 +92,12 @@ __global__ __launch_bounds__(256) void k_route(const float* __restrict__ logits,
 }
 
 hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* w,
-                        hipStream_t s, int32_t* zero_words, int n_zero) {
+                        hipStream_t s, int32_t* zero_words, int n_zero, float* zero_out, int H) {
     if (T == 0) return hipSuccess;
     if (n_zero < 0 || n_zero > 256 || (n_zero > 0 && !zero_words)) return hipErrorInvalidValue;
+    if (zero_out && (H <= 0 || H % 4)) return hipErrorInvalidValue;
     hipLaunchKernelGGL(k_route, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, k, ids, w,
-                       zero_words, n_zero);
+                       zero_words, n_zero, zero_out, H);
     return hipGetLastError();
 }
 

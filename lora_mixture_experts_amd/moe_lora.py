@@ -16,6 +16,7 @@ OK, EINVAL, EWORKSPACE, EHIP, ESCRATCH = 0, -1, -2, -3, -4
 SCRATCH_BYTES = 64 << 20
 FLAG_OUT_BF16 = 1
 FLAG_SHRINK_LAUNCH = 2
+FLAG_FUSED_COMBINE = 4
 NKERNELS = 7
 
 
@@ -215,7 +216,7 @@ class Layer:
 
     def __init__(self, T, H, I, E, top_k, L, r, w_gate_up, w_down, a_gate_up=None, b_gate_up=None,
                  a_down=None, b_down=None, block_m_base=0, block_m_lora=0, out_bf16=False,
-                 shrink_launch=False, tuning=None):
+                 shrink_launch=False, tuning=None, fused_combine=False):
         """tuning: a tuning.Table; when it holds a choice for this shape and
         token count it sets the block sizes and the shrink placement (only if
         none of them is given explicitly)."""
@@ -229,7 +230,11 @@ class Layer:
                 shrink_launch = self.tuned.shrink_launch
         self.desc = make_desc(T, H, I, E, top_k, L, r, block_m_base, block_m_lora,
                               (FLAG_OUT_BF16 if out_bf16 else 0) |
-                              (FLAG_SHRINK_LAUNCH if shrink_launch else 0))
+                              (FLAG_SHRINK_LAUNCH if shrink_launch else 0) |
+                              (FLAG_FUSED_COMBINE if fused_combine else 0))
+        # the down projection's rows are kept (and readable) only when a
+        # separate launch does the weighted combine
+        self.keeps_down_rows = not fused_combine
         self.out_dtype = torch.bfloat16 if out_bf16 else torch.float32
         self.tensors = (w_gate_up, w_down, a_gate_up, b_gate_up, a_down, b_down)
         self.weights = weights_struct(*self.tensors)
@@ -262,9 +267,10 @@ class Layer:
                   s1=torch.empty((P, r), dtype=torch.float32, device=dev),
                   h=torch.empty((P, d.I), dtype=torch.bfloat16, device=dev),
                   s2=torch.empty((P, r), dtype=torch.float32, device=dev),
-                  dn=torch.empty((P, d.H), dtype=torch.float32, device=dev))
+                  dn=(torch.empty((P, d.H), dtype=torch.float32, device=dev) if self.keeps_down_rows
+                      else None))
         read_stages(d, self.workspace, stream=stream, **st)
-        return st
+        return {k: v for k, v in st.items() if v is not None}
 
     def alignment(self, stream=None):
         import torch

@@ -42,8 +42,8 @@ def desc(**over):
 @pytest.mark.parametrize("over", [dict(H=2881), dict(I=100), dict(top_k=0), dict(top_k=33, E=40),
                                   dict(top_k=5, E=4), dict(r=24), dict(E=0), dict(T=-1), dict(L=-1),
                                   dict(bm_b=48), dict(bm_b=8), dict(bm_l=512), dict(E=1025),
-                                  dict(E=128, L=200), dict(E=1024, L=9, top_k=8), dict(flags=4),
-                                  dict(flags=-1), dict(flags=7)])
+                                  dict(E=128, L=200), dict(E=1024, L=9, top_k=8), dict(flags=8), dict(flags=5),
+                                  dict(flags=-1), dict(flags=15)])
 def test_validate_rejects(over):
     assert ml.validate(desc(**over)) == ml.EINVAL
 
@@ -152,3 +152,15 @@ def test_header_scratch_size_matches_binding():
     src = open(HEADER).read()
     m = re.search(r"#define MOE_LORA_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", src)
     assert m and int(m.group(1)) << int(m.group(2)) == ml.SCRATCH_BYTES
+
+
+def test_fused_combine_drops_the_down_rows_from_the_workspace():
+    # with FUSED_COMBINE the down projection adds its weighted rows into out,
+    # so the fp32 [ksplit][C_b][H] buffer is not needed
+    for name, d in wl.CONFIGS.items():
+        args = [d[k] for k in ("T", "H", "I", "E", "top_k", "L", "r")]
+        fused = ml.workspace_bytes(ml.make_desc(*args, flags=ml.FLAG_FUSED_COMBINE))
+        kept = ml.workspace_bytes(ml.make_desc(*args))
+        bf16 = ml.workspace_bytes(ml.make_desc(*args, flags=ml.FLAG_OUT_BF16))
+        C_b, _ = ml.align_capacity(ml.make_desc(*args))
+        assert kept == bf16 and kept - fused >= 4 * C_b * d["H"], name

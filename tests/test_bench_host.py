@@ -86,3 +86,27 @@ def test_shrink_work_is_counted_in_the_launch_that_ran_it():
     summ = bench.lora_kernels_summary(kus_f, b2)
     assert summ["shrinks"] == "inside the projection launches"
     assert summ["bytes"] == sum(b[n] for n in ("shrink_gate_up", "gemm_gate_up", "shrink_down", "gemm_down"))
+
+
+def test_fold_fused_moves_the_combine_into_the_down_projection():
+    c = small_case()
+    st = dict(n_experts=3, n_segments=4, P=8, P_lora=6)
+    b, f, lb, lf = bench.algorithmic(c, st)
+    names = ("route", "align", "shrink_gate_up", "gemm_gate_up", "shrink_down", "gemm_down", "combine")
+    kus = {k: 10.0 for k in names}
+    # every kernel launched: nothing moves
+    b2, _ = bench.fold_fused(kus, b, f, c.T, c.H, 8)
+    assert b2 == b
+    # combine folded: the down launch writes out [T][H] fp32 instead of its
+    # rows [P][H] and reads the P weights; the routing launch clears out
+    kus["combine"] = 0.0
+    b3, _ = bench.fold_fused(kus, b, f, c.T, c.H, 8)
+    assert b3["combine"] == 0
+    assert b3["gemm_down"] == b["gemm_down"] - 8 * c.H * 4 + c.T * c.H * 4 + 8 * 4
+    assert b3["route"] == b["route"] + c.T * c.H * 4
+    # shrinks folded as well
+    kus["shrink_gate_up"] = kus["shrink_down"] = 0.0
+    b4, f4 = bench.fold_fused(kus, b, f, c.T, c.H, 8)
+    assert b4["shrink_gate_up"] == b4["shrink_down"] == 0
+    assert b4["gemm_gate_up"] == b["gemm_gate_up"] + b["shrink_gate_up"]
+    assert f4["gemm_down"] == f["gemm_down"] + f["shrink_down"]

@@ -56,12 +56,12 @@ def build_case(name, dims=None, seed=None, touched_only=True):
     return wl.make_case(name, seed=seed, dims=dims, experts=experts, lora_blocks=blocks)
 
 
-def run_gpu(case, dev, bm_b=0, bm_l=0, shrink_launch=False, tuning=None):
+def run_gpu(case, dev, bm_b=0, bm_l=0, shrink_launch=False, tuning=None, fused_combine=False):
     t = wl.device_tensors(case, dev)
     layer = ml.Layer(case.T, case.H, case.I, case.E, case.top_k, case.L, case.r,
                      t["w_gate_up"], t["w_down"], t["a_gate_up"], t["b_gate_up"], t["a_down"],
                      t["b_down"], block_m_base=bm_b, block_m_lora=bm_l, shrink_launch=shrink_launch,
-                     tuning=tuning)
+                     tuning=tuning, fused_combine=fused_combine)
     out = layer(t["x"], t["logits"], t["adapter_ids"])
     torch.cuda.synchronize()
     return layer, t, out
@@ -161,14 +161,15 @@ def test_align_parity(dev, name, dims, bm):
 # ----------------------------------------------------------------------------- the layer
 
 def check_layer(case, dev, bm=(0, 0), stages=False, stage_tokens=64, shrink_launch=False,
-                tuning=None, expect_choice=None):
+                tuning=None, expect_choice=None, fused_combine=False):
     """Run the layer through the C ABI and compare EVERY output element with
     the oracle (max and mean bars over all T x H values); the alignment the
     call used is compared bit for bit. With stages=True the intermediates of
     a sample of stage_tokens tokens (first and last included) are checked
     too."""
     ids, w = oracle.route(case.logits, case.top_k)
-    layer, t, out = run_gpu(case, dev, *bm, shrink_launch=shrink_launch, tuning=tuning)
+    layer, t, out = run_gpu(case, dev, *bm, shrink_launch=shrink_launch, tuning=tuning,
+                            fused_combine=fused_combine)
     got = out.cpu().numpy()
     assert layer.status() == 0
     if tuning is not None:
@@ -179,8 +180,8 @@ def check_layer(case, dev, bm=(0, 0), stages=False, stage_tokens=64, shrink_laun
             assert bool(layer.desc.flags & ml.FLAG_SHRINK_LAUNCH) == expect_choice.shrink_launch
     ref = oracle.forward(case, ids, w)
     mx, mean = metrics(got, ref)
-    log(f"  {case.name} bm={ml.block_sizes(layer.desc)} tuned={layer.tuned} all {case.T} tokens: "
-        f"max {mx:.2e} mean {mean:.2e}")
+    log(f"  {case.name} bm={ml.block_sizes(layer.desc)} tuned={layer.tuned} fused_combine={fused_combine} "
+        f"all {case.T} tokens: max {mx:.2e} mean {mean:.2e}")
     assert np.all(np.isfinite(got))
     assert mx <= MAX_TOL and mean <= MEAN_TOL, (mx, mean)
     # the alignment the forward pass used is the oracle's, bit for bit
@@ -199,7 +200,9 @@ def check_layer(case, dev, bm=(0, 0), stages=False, stage_tokens=64, shrink_laun
         s1 = gs["s1"].numpy()[rows]
         s2 = gs["s2"].numpy()[rows]
         h = gs["h"].float().numpy()[rows]
-        dn = gs["dn"].numpy()[rows]
+        # the down rows are kept only when a separate launch does the combine
+        assert ("dn" in gs) != fused_combine
+        dn = gs["dn"].numpy()[rows] if "dn" in gs else None
         del gs
         if case.L > 0 and np.abs(st["s1"]).max() > 0:
             m1 = metrics(s1, st["s1"])
@@ -208,8 +211,9 @@ def check_layer(case, dev, bm=(0, 0), stages=False, stage_tokens=64, shrink_laun
             assert m2[0] < 2e-2 and m2[1] < 4e-3, ("s2", m2)
         mh = metrics(h, st["h"])
         assert mh[0] < 1e-2 and mh[1] < 4e-3, ("h", mh)
-        md = metrics(dn, st["d"])
-        assert md[0] < MAX_TOL and md[1] < MEAN_TOL, ("d", md)
+        if dn is not None:
+            md = metrics(dn, st["d"])
+            assert md[0] < MAX_TOL and md[1] < MEAN_TOL, ("d", md)
         # pairs without adapter have zero shrink rows
         noad = np.array([not (0 <= case.adapter_ids[r // case.top_k] < case.L) for r in rows])
         assert np.all(s1[noad] == 0) and np.all(s2[noad] == 0)
@@ -242,12 +246,43 @@ def test_layer_parity_library_default(dev, name):
     check_layer(build_case(name), dev, stages=True)
 
 
+@pytest.mark.parametrize("name", ["tiny", "decode", "wide", "many", "dense"])
+def test_layer_parity_fused_combine(dev, name):
+    # the weighted combine inside the down projection (fp32 atomic adds into
+    # out), with the launch choices as benched; agrees with the fixed-order
+    # combine to fp32 rounding
+    log(f"layer {name} (fused combine)")
+    case = build_case(name)
+    choice = _table().lookup(case.T, case.H, case.I, case.E, case.top_k, case.L, case.r)
+    out = check_layer(case, dev, stages=True, tuning=_table(), fused_combine=True, expect_choice=choice)
+    layer, t, ref = run_gpu(case, dev, tuning=_table())
+    out2 = layer(t["x"], t["logits"], t["adapter_ids"])
+    torch.cuda.synchronize()
+    assert torch.equal(ref, out2)  # the fixed-order combine is bitwise repeatable
+    mx, mean = metrics(out.cpu().numpy(), ref.cpu().numpy())
+    assert mx < 1e-5 and mean < 1e-6, (mx, mean)
+
+
+@pytest.mark.parametrize("fused", [False, True])
 @pytest.mark.parametrize("bm", [(16, 16), (32, 16), (64, 64), (128, 32), (256, 256)])
-def test_layer_block_sizes(dev, bm):
-    log(f"layer block sizes {bm}")
+def test_layer_block_sizes(dev, bm, fused):
+    log(f"layer block sizes {bm} fused_combine={fused}")
     dims = dict(T=150, H=192, I=320, E=6, top_k=3, L=3, r=16)
     case = build_case("blocks", dims=dims, seed=5)
-    check_layer(case, dev, bm=bm, stages=True)
+    check_layer(case, dev, bm=bm, stages=True, fused_combine=fused)
+
+
+@pytest.mark.parametrize("bm", [(16, 16), (32, 16)])
+def test_fused_combine_with_down_k_split(dev, bm):
+    # a long down K (I = 6144) on a small grid: the down projection is cut
+    # into K ranges, and every range adds its weighted partial into out
+    log(f"fused combine with K split {bm}")
+    dims = dict(T=8, H=128, I=6144, E=2, top_k=2, L=2, r=16)
+    case = build_case("ksplit", dims=dims, seed=31)
+    a = check_layer(case, dev, bm=bm, stages=True, fused_combine=True)
+    b = check_layer(case, dev, bm=bm, stages=True)
+    mx, mean = metrics(a.cpu().numpy(), b.cpu().numpy())
+    assert mx < 1e-5 and mean < 1e-6, (mx, mean)
 
 
 @pytest.mark.parametrize("r,L,bm,pure", [(8, 3, 128, False), (64, 3, 128, True), (128, 2, 256, False),
@@ -428,6 +463,14 @@ def test_repeat_calls_reuse_workspace(dev):
     torch.cuda.synchronize()
     # same inputs, same block plan: bitwise identical (no atomics in the path)
     assert torch.equal(out1, out2)
+    # the combine inside the down projection (weighted rows added atomically
+    # into out) agrees to fp32 rounding, on repeated calls too
+    layer_f, t_f, out_f1 = run_gpu(case, dev, fused_combine=True)
+    out_f2 = layer_f(t_f["x"], t_f["logits"], t_f["adapter_ids"])
+    torch.cuda.synchronize()
+    for o in (out_f1, out_f2):
+        mx, mean = metrics(o.cpu().numpy(), out1.cpu().numpy())
+        assert mx < 1e-5 and mean < 1e-6, (mx, mean)
 
 
 def test_bf16_output_is_rounded_fp32_output(dev):
@@ -445,14 +488,17 @@ def test_bf16_output_is_rounded_fp32_output(dev):
                                   out32.to(torch.bfloat16).view(torch.int16).cpu().numpy())
 
 
-def test_graph_replay_matches_eager(dev):
+@pytest.mark.parametrize("fused", [False, True])
+def test_graph_replay_matches_eager(dev, fused):
     # the whole layer captured into one HIP graph (no host sync, no allocation,
     # no memset inside the call) replays to the eager result, also after the
     # inputs change in place, with eager calls on the same workspace between
-    # replays
-    log("graph replay")
+    # replays; bit for bit with the fixed-order combine, to fp32 rounding with
+    # the combine in the down projection (which also shows that every replay
+    # clears out first)
+    log(f"graph replay fused_combine={fused}")
     case = build_case("decode")
-    layer, t, out_eager = run_gpu(case, dev)
+    layer, t, out_eager = run_gpu(case, dev, fused_combine=fused)
     ref = out_eager.clone()
     out = torch.empty_like(ref)
     side = torch.cuda.Stream()
@@ -466,16 +512,23 @@ def test_graph_replay_matches_eager(dev):
         layer(t["x"], t["logits"], t["adapter_ids"], out=out)
     x0 = t["x"].clone()
     x1 = torch.flip(x0, dims=[0]).contiguous()  # the tokens in reverse order
+
+    def same(a, b):
+        if not fused:
+            return torch.equal(a, b)
+        mx, mean = metrics(a.cpu().numpy(), b.cpu().numpy())
+        return mx < 1e-5 and mean < 1e-6
+
     for i in range(4):
         xi = x0 if i % 2 == 0 else x1
         t["x"].copy_(xi)
         want = layer(t["x"], t["logits"], t["adapter_ids"]).clone()  # eager, same workspace
-        out.zero_()
+        out.fill_(12345.0)
         g.replay()
         torch.cuda.synchronize()
-        assert torch.equal(out, want), i
+        assert same(out, want), i
         if i % 2 == 0:
-            assert torch.equal(out, ref)
+            assert same(out, ref)
     t["x"].copy_(x0)
 
 

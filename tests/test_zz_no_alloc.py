@@ -4,9 +4,9 @@ moe_lora_forward (the workspace entry point), through the C ABI.
 Two calls in a row on the same GPU, the second with a smaller batch, so the
 second runs on scratch that still holds the first call's intermediates; each
 must agree with the workspace entry point on the same inputs (the oracle's
-bars; the two share every kernel, so they also agree bit for bit). A call
-that needs more than the static array is refused before anything is
-enqueued.
+bars; with the fixed-order combine the two also agree bit for bit, since
+they share every kernel). A call that needs more than the static array is
+refused before anything is enqueued.
 """
 import sys
 
@@ -39,8 +39,8 @@ def _inputs(case, dev, T):
     return t, t["x"][:T].contiguous(), t["logits"][:T].contiguous(), t["adapter_ids"][:T].contiguous()
 
 
-def _both(case, t, x, lg, ad, T, dev):
-    d = ml.make_desc(T, case.H, case.I, case.E, case.top_k, case.L, case.r)
+def _both(case, t, x, lg, ad, T, dev, flags=0):
+    d = ml.make_desc(T, case.H, case.I, case.E, case.top_k, case.L, case.r, flags=flags)
     wts = ml.weights_struct(t["w_gate_up"], t["w_down"], t["a_gate_up"], t["b_gate_up"], t["a_down"],
                             t["b_down"])
     ws = torch.empty(ml.workspace_bytes(d), dtype=torch.uint8, device=dev)
@@ -59,13 +59,16 @@ def test_noalloc_matches_workspace_entry_point_on_two_calls():
     t, x, lg, ad = _inputs(case, dev, case.T)
     # first call: the 16-token decode batch; second: a 5-token batch (smaller
     # plan, different block counts) on the scratch the first call left behind
-    for T in (case.T, 5):
-        log(f"noalloc decode T={T}")
-        got, ref = _both(case, t, x[:T].contiguous(), lg[:T].contiguous(), ad[:T].contiguous(), T, dev)
-        assert np.all(np.isfinite(got))
-        mx, mean = metrics(got, ref)
-        assert mx <= MAX_TOL and mean <= MEAN_TOL, (T, mx, mean)
-        np.testing.assert_array_equal(got, ref)
+    for flags in (0, ml.FLAG_FUSED_COMBINE):
+        for T in (case.T, 5):
+            log(f"noalloc decode T={T} flags={flags}")
+            got, ref = _both(case, t, x[:T].contiguous(), lg[:T].contiguous(), ad[:T].contiguous(), T, dev,
+                             flags)
+            assert np.all(np.isfinite(got))
+            mx, mean = metrics(got, ref)
+            assert mx <= MAX_TOL and mean <= MEAN_TOL, (T, mx, mean)
+            if not flags & ml.FLAG_FUSED_COMBINE:
+                np.testing.assert_array_equal(got, ref)
 
 
 def test_noalloc_refuses_a_call_larger_than_the_scratch():

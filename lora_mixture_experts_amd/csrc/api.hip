@@ -315,6 +315,7 @@ int forward_planned(const Plan& p, const moe_lora_desc* d, const moe_lora_weight
 
     GemmArgs ga{};
     ga.sorted_b = sorted_b; ga.blk_e_b = blk_e_b; ga.P = p.P; ga.top_k = p.k; ga.bm_b = p.bm_b;
+    ga.n_b_live = counts;
     ga.n_blocks = p.nblk_b; ga.slot_adapter = sad; ga.L = p.L; ga.E = p.E; ga.r = p.r;
     ga.C_b = p.C_b; ga.h_out = h; ga.d_out = dn; ga.ksplit = 1; ga.s_split = p.ssplit;
     ga.X = static_cast<const uint16_t*>(x); ga.gate_up = 1;

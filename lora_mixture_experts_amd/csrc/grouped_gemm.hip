@@ -765,6 +765,38 @@ __device__ __forceinline__ void dma_step(const DmaCtx<FM, FN, A_PW, B_PW>& c, f3
 constexpr int kMaxPipeRuns = 4;
 __device__ __attribute__((aligned(128))) uint16_t g_zero_row[64] = {};
 
+// Tile order of the direct-load kernel. The live tiles (blocks
+// 0 .. n_b / BM - 1 of the base view: the alignment packs every non-empty
+// block first, so no workgroup is spent on an empty block) are numbered
+// without holes: N tiles in groups of kGroupN, and inside a group block-major,
+// so consecutive numbers are the group's N tiles of one block, then of the
+// next block (which is usually the same expert). The hardware deals the 1-D
+// grid's workgroups round-robin to the 8 XCDs, each with its own L2, so
+// workgroup i is the (i / 8)-th of XCD i mod 8. With S workgroups resident per
+// XCD (32 CUs x workgroups per CU), the XCD's k-th workgroup takes tile
+// (8 (k / S) + x) S + k mod S: each XCD works through whole patches of S
+// consecutive tiles (about S / kGroupN blocks x kGroupN N tiles: one expert's
+// weight tiles and the same activation rows), patch x, x + 8, ..., so the
+// workgroups resident on an XCD at a time share their operand slabs in its L2
+// and every XCD gets an equal share of the tiles.
+struct TileOrder {
+    int n_tiles, n_live, per_group;
+    __device__ TileOrder(const GemmArgs& a, int cols, int bm) {
+        n_tiles = (a.N_out + cols - 1) / cols;
+        // uniform: keeps the tile's block, expert and addresses scalar
+        n_live = __builtin_amdgcn_readfirstlane(*a.n_b_live) / bm;
+        per_group = n_live * kGroupN;
+    }
+    __device__ int total() const { return n_live * n_tiles; }
+    // tile number -> (block, N tile)
+    __device__ void at(int t, int& b, int& tile) const {
+        const int g = t / per_group, rem = t - g * per_group;
+        const int w = min(kGroupN, n_tiles - g * kGroupN);  // N tiles in this group
+        b = rem / w;
+        tile = g * kGroupN + (rem - b * w);
+    }
+};
+
 template <int BM, int BNT, int WM, int WN, int NS, bool GATEUP>
 __global__ __launch_bounds__(64 * WM * WN) void k_gemm_dma(GemmArgs a) {
     constexpr int NW = WM * WN;
@@ -775,13 +807,14 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_dma(GemmArgs a) {
     static_assert(!GATEUP || FN % 2 == 0, "gate/up fragments come in pairs");
     static_assert(NS == 2 || NS == 3, "two or three LDS stages");
     constexpr int kCols = tile_cols<BNT, GATEUP>();
-    const int n_tiles = (a.N_out + kCols - 1) / kCols;
-    const int chunk = gridDim.x / kXcds;
-    const int t = (blockIdx.x % kXcds) * chunk + blockIdx.x / kXcds;
-    const int per_group = a.n_blocks * kGroupN;
-    const int ng = t / per_group, rem = t % per_group;
-    const int b = rem / kGroupN, tile = ng * kGroupN + rem % kGroupN;
-    if (tile >= n_tiles) return;
+    const TileOrder order(a, kCols, BM);
+    // the XCD's k-th workgroup (k = i / 8) takes the k-th tile of that XCD's
+    // sequence: round k / S, slot k % S
+    const int S = a.xcd_slots, kx = blockIdx.x / kXcds;
+    const int t = ((kx / S) * kXcds + blockIdx.x % kXcds) * S + kx % S;
+    if (t >= order.total()) return;
+    int b, tile;
+    order.at(t, b, tile);
     const int e = a.blk_e_b[b];
     if (e < 0) return;
     const int lane = threadIdx.x & 63, wave = wave_id();
@@ -953,7 +986,9 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_dma(GemmArgs a) {
 // Launch shapes by block height (rows per block of the base view):
 //   16        skinny: one wave per 16 x 64 tile (gate_up: 32 h columns)
 //   32, 64    tiled:  32 x 128 (1 x 4 waves) and 64 x 128 (2 x 2 waves)
-//   128, 256  direct-load: 128 x 192 and 256 x 192 (2 x 2 waves, 2 stages)
+//   128       direct-load: 128 x 192 (2 x 2 waves, 2 stages, 2 workgroups per CU)
+//   256       direct-load: 256 x 256 (2 x 4 waves of 128 x 64, 2 stages, one
+//             workgroup per CU)
 // These shapes were the fastest of those measured on MI355X for the
 // decode-, many-adapter- and prefill-shaped layers. The column count may
 // leave a partial last tile.
@@ -965,15 +1000,31 @@ constexpr int kSkinnyNSGateUp = 2;
 constexpr int kSkinnyFNDown = 4;
 constexpr int kSkinnyNSDown = 2;
 
+// workgroups of the direct-load kernel resident at once: 256 CUs x the
+// workgroups per CU that its LDS and registers allow
+constexpr int kCus = 256;
+
 template <int BM, int BNT, int WM, int WN, int NS>
 static hipError_t launch_dma(const GemmArgs& a, hipStream_t s) {
+    if (!a.n_b_live) return hipErrorInvalidValue;
     const int cols = a.gate_up ? BNT / 2 : BNT;
     const int n_tiles = (a.N_out + cols - 1) / cols;
-    const dim3 grid(tiled_grid(a.n_blocks, n_tiles)), block(64 * WM * WN);
+    constexpr int lds = 2 * NS * (BM + BNT) * 64;        // bytes (NS stages of bf16 A and B)
+    // by LDS (160 KiB per CU) and by registers (these kernels hold 2 waves per SIMD)
+    constexpr int per_cu = (160 * 1024 / lds) < (8 / (WM * WN)) ? (160 * 1024 / lds) : (8 / (WM * WN));
+    static_assert(per_cu >= 1, "tile does not fit one CU");
+    GemmArgs b = a;
+    b.xcd_slots = kCus / kXcds * per_cu;
+    // every tile of the capacity, in whole rounds of 8 S workgroups
+    const long round = static_cast<long>(kXcds) * b.xcd_slots;
+    const long tiles = static_cast<long>(n_tiles) * a.n_blocks;
+    const long g = (tiles + round - 1) / round * round;
+    if (g > 0x7fffffffL) return hipErrorInvalidValue;
+    const dim3 grid(static_cast<unsigned>(g)), block(64 * WM * WN);
     if (a.gate_up)
-        hipLaunchKernelGGL((k_gemm_dma<BM, BNT, WM, WN, NS, true>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((k_gemm_dma<BM, BNT, WM, WN, NS, true>), grid, block, 0, s, b);
     else
-        hipLaunchKernelGGL((k_gemm_dma<BM, BNT, WM, WN, NS, false>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((k_gemm_dma<BM, BNT, WM, WN, NS, false>), grid, block, 0, s, b);
     return hipGetLastError();
 }
 
@@ -1039,7 +1090,7 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
         case 32: return launch_tiled<32, 128, 1, 4>(a, s);
         case 64: return launch_tiled<64, 128, 2, 2>(a, s);
         case 128: return launch_dma<128, 192, 2, 2, 2>(a, s);
-        case 256: return launch_dma<256, 192, 2, 2, 2>(a, s);
+        case 256: return launch_dma<256, 256, 2, 4, 2>(a, s);
         default: return hipErrorInvalidValue;
     }
 }

@@ -75,6 +75,8 @@ struct GemmArgs {
     const int32_t* sorted_b;
     const int32_t* blk_e_b;
     int P, top_k, bm_b, n_blocks;
+    const int32_t* n_b_live;  // padded length of the base view (live blocks x bm_b), from the alignment
+    int xcd_slots;            // direct-load kernel: workgroups resident per XCD (set by its launcher)
     const uint16_t* W;        // gate_up: [E][2I][H]; down: [E][H][I]
     int N_out;                // gate_up: I (h columns); down: H
     int K;                    // gate_up: H; down: I

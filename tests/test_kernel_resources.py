@@ -28,8 +28,8 @@ MIN_OCCUPANCY = {
     "k_gemm_tiled<64, 128, 2, 2, false>": 3,
     "k_gemm_dma<128, 192, 2, 2, 2, true>": 2,
     "k_gemm_dma<128, 192, 2, 2, 2, false>": 2,
-    "k_gemm_dma<256, 192, 2, 2, 2, true>": 1,
-    "k_gemm_dma<256, 192, 2, 2, 2, false>": 1,
+    "k_gemm_dma<256, 256, 2, 4, 2, true>": 2,
+    "k_gemm_dma<256, 256, 2, 4, 2, false>": 2,
 }
 MIN_OCCUPANCY_SHRINK = {"k_shrink<1>": 8, "k_shrink<2>": 5, "k_shrink<4>": 3, "k_shrink<8>": 1}
 

@@ -443,6 +443,7 @@ struct TileCfg {
 };
 constexpr int kGroupN = 8;
 constexpr int kXcds = 8;
+constexpr int kCus = 256;  // compute units of the MI355X
 
 __device__ __forceinline__ int swz(int row, int chunk) { return row * 64 + ((chunk ^ (row & 7)) << 3); }
 
@@ -450,12 +451,6 @@ __device__ __forceinline__ int swz(int row, int chunk) { return row * 64 + ((chu
 template <int BNT, bool GATEUP>
 __host__ __device__ constexpr int tile_cols() { return GATEUP ? BNT / 2 : BNT; }
 
-// grid size for n_blocks x n_tiles logical tiles
-static inline int tiled_grid(int n_blocks, int n_tiles) {
-    const int groups = (n_tiles + kGroupN - 1) / kGroupN;
-    const long total = static_cast<long>(groups) * n_blocks * kGroupN;
-    return static_cast<int>((total + kXcds - 1) / kXcds * kXcds);
-}
 
 // Tile epilogue shared by the LDS kernels: the LoRA expand for every adapter
 // present among the wave's rows (extra MFMA K steps on the accumulators), then
@@ -543,20 +538,69 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& a, f32x4 (&acc)[FM
     }
 }
 
+// Tile order of the LDS-tiled and direct-load kernels. The live tiles (blocks
+// 0 .. n_b / BM - 1 of the base view: the alignment packs every non-empty
+// block first, so no workgroup is spent on an empty block) are numbered
+// without holes: N tiles in groups of kGroupN, and inside a group block-major,
+// so consecutive numbers are the group's N tiles of one block, then of the
+// next block (which is usually the same expert). The hardware deals the 1-D
+// grid's workgroups round-robin to the 8 XCDs, each with its own L2, so
+// workgroup i is the (i / 8)-th of XCD i mod 8. With S workgroups resident per
+// XCD (32 CUs x workgroups per CU), the XCD's k-th workgroup takes tile
+// (8 (k / S) + x) S + k mod S: each XCD works through whole patches of S
+// consecutive tiles (about S / kGroupN blocks x kGroupN N tiles: one expert's
+// weight tiles and the same activation rows), patch x, x + 8, ..., so the
+// workgroups resident on an XCD at a time share their operand slabs in its L2
+// and every XCD gets an equal share of the tiles.
+struct TileOrder {
+    int n_tiles, n_live, per_group;
+    __device__ TileOrder(const GemmArgs& a, int cols, int bm) {
+        n_tiles = (a.N_out + cols - 1) / cols;
+        // uniform: keeps the tile's block, expert and addresses scalar
+        n_live = __builtin_amdgcn_readfirstlane(*a.n_b_live) / bm;
+        per_group = n_live * kGroupN;
+    }
+    __device__ int total() const { return n_live * n_tiles; }
+    // tile number of workgroup i of the 1-D grid (>= total(): nothing to do).
+    // slots: workgroups resident per XCD. Every full round hands each XCD a
+    // patch of `slots` consecutive tiles; the last, partial round hands each
+    // XCD ceil(rest / 8) of the remaining tiles instead, so that no XCD sits
+    // idle while others work through whole patches. The grid holds whole
+    // rounds of 8 x slots workgroups (at least the tile capacity), so the map
+    // covers every tile below total().
+    __device__ int of_workgroup(int i, int slots) const {
+        const int tot = total();
+        const int k = i / kXcds, x = i % kXcds;
+        const int q = k / slots, m = k % slots;
+        const int full = tot / (kXcds * slots);  // full rounds
+        if (q < full) return (q * kXcds + x) * slots + m;
+        if (q > full) return tot;
+        const int base = full * kXcds * slots;
+        const int S = (tot - base + kXcds - 1) / kXcds;
+        return m < S ? base + x * S + m : tot;
+    }
+    // tile number -> (block, N tile)
+    __device__ void at(int t, int& b, int& tile) const {
+        const int g = t / per_group, rem = t - g * per_group;
+        const int w = min(kGroupN, n_tiles - g * kGroupN);  // N tiles in this group
+        b = rem / w;
+        tile = g * kGroupN + (rem - b * w);
+    }
+};
+
 template <int BM, int BNT, int WM, int WN, bool GATEUP>
 __global__ __launch_bounds__(64 * WM * WN) void k_gemm_tiled(GemmArgs a) {
     using C = TileCfg<BM, BNT, WM, WN>;
     constexpr int FM = C::FM, FN = C::FN;
     static_assert(!GATEUP || FN % 2 == 0, "gate/up fragments come in pairs");
     constexpr int kCols = tile_cols<BNT, GATEUP>();
-    const int n_tiles = (a.N_out + kCols - 1) / kCols;
-    // physical -> logical tile
-    const int chunk = gridDim.x / kXcds;
-    const int t = (blockIdx.x % kXcds) * chunk + blockIdx.x / kXcds;
-    const int per_group = a.n_blocks * kGroupN;
-    const int ng = t / per_group, rem = t % per_group;
-    const int b = rem / kGroupN, tile = ng * kGroupN + rem % kGroupN;
-    if (tile >= n_tiles) return;
+    // the XCD's k-th workgroup of this K range takes the k-th tile of that
+    // XCD's sequence (see TileOrder)
+    const TileOrder order(a, kCols, BM);
+    const int t = order.of_workgroup(blockIdx.x, a.xcd_slots);
+    if (t >= order.total()) return;
+    int b, tile;
+    order.at(t, b, tile);
     const int e = a.blk_e_b[b];
     if (e < 0) return;
     const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
@@ -765,38 +809,6 @@ __device__ __forceinline__ void dma_step(const DmaCtx<FM, FN, A_PW, B_PW>& c, f3
 constexpr int kMaxPipeRuns = 4;
 __device__ __attribute__((aligned(128))) uint16_t g_zero_row[64] = {};
 
-// Tile order of the direct-load kernel. The live tiles (blocks
-// 0 .. n_b / BM - 1 of the base view: the alignment packs every non-empty
-// block first, so no workgroup is spent on an empty block) are numbered
-// without holes: N tiles in groups of kGroupN, and inside a group block-major,
-// so consecutive numbers are the group's N tiles of one block, then of the
-// next block (which is usually the same expert). The hardware deals the 1-D
-// grid's workgroups round-robin to the 8 XCDs, each with its own L2, so
-// workgroup i is the (i / 8)-th of XCD i mod 8. With S workgroups resident per
-// XCD (32 CUs x workgroups per CU), the XCD's k-th workgroup takes tile
-// (8 (k / S) + x) S + k mod S: each XCD works through whole patches of S
-// consecutive tiles (about S / kGroupN blocks x kGroupN N tiles: one expert's
-// weight tiles and the same activation rows), patch x, x + 8, ..., so the
-// workgroups resident on an XCD at a time share their operand slabs in its L2
-// and every XCD gets an equal share of the tiles.
-struct TileOrder {
-    int n_tiles, n_live, per_group;
-    __device__ TileOrder(const GemmArgs& a, int cols, int bm) {
-        n_tiles = (a.N_out + cols - 1) / cols;
-        // uniform: keeps the tile's block, expert and addresses scalar
-        n_live = __builtin_amdgcn_readfirstlane(*a.n_b_live) / bm;
-        per_group = n_live * kGroupN;
-    }
-    __device__ int total() const { return n_live * n_tiles; }
-    // tile number -> (block, N tile)
-    __device__ void at(int t, int& b, int& tile) const {
-        const int g = t / per_group, rem = t - g * per_group;
-        const int w = min(kGroupN, n_tiles - g * kGroupN);  // N tiles in this group
-        b = rem / w;
-        tile = g * kGroupN + (rem - b * w);
-    }
-};
-
 template <int BM, int BNT, int WM, int WN, int NS, bool GATEUP>
 __global__ __launch_bounds__(64 * WM * WN) void k_gemm_dma(GemmArgs a) {
     constexpr int NW = WM * WN;
@@ -808,10 +820,7 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_dma(GemmArgs a) {
     static_assert(NS == 2 || NS == 3, "two or three LDS stages");
     constexpr int kCols = tile_cols<BNT, GATEUP>();
     const TileOrder order(a, kCols, BM);
-    // the XCD's k-th workgroup (k = i / 8) takes the k-th tile of that XCD's
-    // sequence: round k / S, slot k % S
-    const int S = a.xcd_slots, kx = blockIdx.x / kXcds;
-    const int t = ((kx / S) * kXcds + blockIdx.x % kXcds) * S + kx % S;
+    const int t = order.of_workgroup(blockIdx.x, a.xcd_slots);
     if (t >= order.total()) return;
     int b, tile;
     order.at(t, b, tile);
@@ -1000,10 +1009,6 @@ constexpr int kSkinnyNSGateUp = 2;
 constexpr int kSkinnyFNDown = 4;
 constexpr int kSkinnyNSDown = 2;
 
-// workgroups of the direct-load kernel resident at once: 256 CUs x the
-// workgroups per CU that its LDS and registers allow
-constexpr int kCus = 256;
-
 template <int BM, int BNT, int WM, int WN, int NS>
 static hipError_t launch_dma(const GemmArgs& a, hipStream_t s) {
     if (!a.n_b_live) return hipErrorInvalidValue;
@@ -1028,15 +1033,24 @@ static hipError_t launch_dma(const GemmArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <int BM, int BNT, int WM, int WN>
+// PER_CU: workgroups per CU (by LDS and registers: 4 for 32-row tiles, 3 for
+// 64-row tiles)
+template <int BM, int BNT, int WM, int WN, int PER_CU>
 static hipError_t launch_tiled(const GemmArgs& a, hipStream_t s) {
+    if (!a.n_b_live) return hipErrorInvalidValue;
     const int cols = a.gate_up ? BNT / 2 : BNT;
     const int n_tiles = (a.N_out + cols - 1) / cols;
-    const dim3 grid(tiled_grid(a.n_blocks, n_tiles), a.ksplit), block(64 * WM * WN);
+    GemmArgs b = a;
+    b.xcd_slots = kCus / kXcds * PER_CU;
+    const long round = static_cast<long>(kXcds) * b.xcd_slots;
+    const long tiles = static_cast<long>(n_tiles) * a.n_blocks;
+    const long g = (tiles + round - 1) / round * round;
+    if (g > 0x7fffffffL) return hipErrorInvalidValue;
+    const dim3 grid(static_cast<unsigned>(g), a.ksplit), block(64 * WM * WN);
     if (a.gate_up)
-        hipLaunchKernelGGL((k_gemm_tiled<BM, BNT, WM, WN, true>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((k_gemm_tiled<BM, BNT, WM, WN, true>), grid, block, 0, s, b);
     else
-        hipLaunchKernelGGL((k_gemm_tiled<BM, BNT, WM, WN, false>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((k_gemm_tiled<BM, BNT, WM, WN, false>), grid, block, 0, s, b);
     return hipGetLastError();
 }
 
@@ -1087,8 +1101,8 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
         return hipGetLastError();
     }
     switch (a.bm_b) {
-        case 32: return launch_tiled<32, 128, 1, 4>(a, s);
-        case 64: return launch_tiled<64, 128, 2, 2>(a, s);
+        case 32: return launch_tiled<32, 128, 1, 4, 4>(a, s);
+        case 64: return launch_tiled<64, 128, 2, 2, 3>(a, s);
         case 128: return launch_dma<128, 192, 2, 2, 2>(a, s);
         case 256: return launch_dma<256, 256, 2, 4, 2>(a, s);
         default: return hipErrorInvalidValue;

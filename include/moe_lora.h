@@ -70,7 +70,21 @@ extern "C" {
  *                                   a fixed order: bitwise repeatable (and
  *                                   faster on MI355X at every measured shape).
  *                                   Not with OUT_BF16.
- *   any other bit is an error. */
+ *   any other bit is an error.
+ *   Launch tuning (0 = the library's choice; any valid value computes the
+ *   same layer up to the order of fp32 sums; these are what a per-shape
+ *   tuning table sets, AWS post, section "Tuning kernel configurations for
+ *   Amazon SageMaker AI and Amazon Bedrock"):
+ *     down_ksplit    K ranges of the down projection, each adding its own fp32
+ *                    partial (summed in order by the combine): a divisor of
+ *                    I/64; only 1 with base blocks of 128 or 256 rows
+ *     shrink_ksplit  K ranges per LoRA block of the two shrinks when they have
+ *                    launches of their own (1..4, at most min(H, I)/64); where
+ *                    they run inside the projections only their own value
+ *     waves_gate_up, waves_down
+ *                    16-row base blocks: waves per tile that split its K range
+ *                    (1, 2 or 4; each wave keeps >= 4 chunks of 64); other
+ *                    block sizes take only 1 */
 #define MOE_LORA_FLAG_OUT_BF16 1
 #define MOE_LORA_FLAG_SHRINK_LAUNCH 2
 #define MOE_LORA_FLAG_FUSED_COMBINE 4
@@ -78,6 +92,7 @@ typedef struct moe_lora_desc {
     int32_t T, H, I, E, top_k, L, r;
     int32_t block_m_base, block_m_lora;
     int32_t flags;
+    int32_t down_ksplit, shrink_ksplit, waves_gate_up, waves_down;
 } moe_lora_desc;
 
 /* Weights (device pointers, bf16 bits, 16-byte aligned).
@@ -103,6 +118,17 @@ int moe_lora_validate(const moe_lora_desc *d, const moe_lora_weights *w, size_t 
 
 /* Block sizes the library uses for this descriptor (resolves the 0 defaults). */
 int moe_lora_block_sizes(const moe_lora_desc *d, int32_t *block_m_base, int32_t *block_m_lora);
+
+/* The launch choices the library makes for this descriptor (0 defaults
+ * resolved): base / LoRA block rows, down K ranges, shrink K ranges (0 when
+ * L == 0), waves per tile of the two 16-row projections (0 for other block
+ * sizes), whether the shrinks run inside the projection launches, and
+ * whether the combine runs in the down projection. Host only. */
+typedef struct moe_lora_plan_info {
+    int32_t block_m_base, block_m_lora, down_ksplit, shrink_ksplit;
+    int32_t waves_gate_up, waves_down, shrinks_in_projections, combine_in_down;
+} moe_lora_plan_info;
+int moe_lora_plan(const moe_lora_desc *d, moe_lora_plan_info *info);
 
 /* Workspace bytes moe_lora_forward needs for this descriptor. */
 int moe_lora_workspace_bytes(const moe_lora_desc *d, size_t *bytes);

@@ -25,6 +25,7 @@ struct Plan {
     int bm_b, bm_l, C_b, C_l, nblk_b, nblk_l;
     int ksplit;  // K ranges of the down projection (partial sums summed by the combine)
     int ssplit;  // K ranges of the two shrinks (partials summed by the projection kernels)
+    int ksw_gu, ksw_dn;  // 16-row blocks: waves per tile of the two projections
     bool fused;  // the shrinks run as producer waves inside the projection launches
     bool fuse_combine;  // the down projection adds its weighted rows into out (no D, no combine launch)
     size_t off_ids, off_w, off_sorted_b, off_blk_e_b, off_counts, off_sorted_l, off_blk_e_l,
@@ -87,7 +88,19 @@ int make_plan(const moe_lora_desc* d, Plan* p) {
     p->C_l = roundup_i(P + std::min<long>(static_cast<long>(p->E) * p->L, P) * (p->bm_l - 1), p->bm_l);
     p->nblk_b = p->C_b / p->bm_b;
     p->nblk_l = p->C_l / p->bm_l;
-    p->ksplit = gemm_down_ksplit(p->H, p->I, p->bm_b, p->nblk_b);
+    // launch tuning: 0 = the library's choice; results do not depend on any
+    // of these beyond the order of fp32 sums
+    if (d->down_ksplit < 0 || d->shrink_ksplit < 0 || d->waves_gate_up < 0 || d->waves_down < 0)
+        return MOE_LORA_EINVAL;
+    p->ksplit = d->down_ksplit ? d->down_ksplit : gemm_down_ksplit(p->H, p->I, p->bm_b, p->nblk_b);
+    // the direct-load kernels take the whole K range
+    if (p->bm_b >= 128 && p->ksplit != 1) return MOE_LORA_EINVAL;
+    if (p->ksplit > p->I / 64 || (p->I / 64) % p->ksplit) return MOE_LORA_EINVAL;
+    p->ksw_gu = d->waves_gate_up ? d->waves_gate_up : 1;
+    p->ksw_dn = d->waves_down ? d->waves_down : 1;
+    if (p->bm_b != 16 && (p->ksw_gu != 1 || p->ksw_dn != 1)) return MOE_LORA_EINVAL;
+    if (p->bm_b == 16 && (!skinny_waves_ok(p->H, 1, p->ksw_gu) || !skinny_waves_ok(p->I, p->ksplit, p->ksw_dn)))
+        return MOE_LORA_EINVAL;
     // the weighted combine runs in the down projection's epilogue (fp32
     // atomic adds into out) only on request: the atomics cost the down
     // projection more than the fixed-order combine launch takes at every
@@ -105,11 +118,16 @@ int make_plan(const moe_lora_desc* d, Plan* p) {
         const long units = static_cast<long>(p->nblk_l) * ((p->r + 15) / 16) * ss;
         p->fused = units <= kMaxProducerUnits;
     }
-    if (p->fused)
+    if (p->fused) {
         p->ssplit = std::max(producer_ksplit(p->H), producer_ksplit(p->I));
-    else
+        if (d->shrink_ksplit && d->shrink_ksplit != p->ssplit) return MOE_LORA_EINVAL;
+    } else if (p->L > 0 && d->shrink_ksplit) {
+        p->ssplit = d->shrink_ksplit;
+        if (p->ssplit > kMaxShrinkSplit || p->ssplit > std::min(p->H, p->I) / 64) return MOE_LORA_EINVAL;
+    } else {
         p->ssplit = p->L > 0 ? std::min(shrink_ksplit(p->nblk_l, p->H, p->bm_b),
                                         shrink_ksplit(p->nblk_l, p->I, p->bm_b)) : 1;
+    }
     size_t o = 0;
     auto take = [&](size_t bytes) { const size_t at = o; o += up(bytes); return at; };
     p->off_ids = take(4 * P);
@@ -200,6 +218,22 @@ int moe_lora_block_sizes(const moe_lora_desc* d, int32_t* bm_b, int32_t* bm_l) {
     if (rc) return rc;
     if (bm_b) *bm_b = p.bm_b;
     if (bm_l) *bm_l = p.bm_l;
+    return MOE_LORA_OK;
+}
+
+int moe_lora_plan(const moe_lora_desc* d, moe_lora_plan_info* info) {
+    Plan p;
+    const int rc = make_plan(d, &p);
+    if (rc) return rc;
+    if (!info) return MOE_LORA_EINVAL;
+    info->block_m_base = p.bm_b;
+    info->block_m_lora = p.bm_l;
+    info->down_ksplit = p.ksplit;
+    info->shrink_ksplit = p.L > 0 ? p.ssplit : 0;
+    info->waves_gate_up = p.bm_b == 16 ? p.ksw_gu : 0;
+    info->waves_down = p.bm_b == 16 ? p.ksw_dn : 0;
+    info->shrinks_in_projections = p.fused ? 1 : 0;
+    info->combine_in_down = p.fuse_combine ? 1 : 0;
     return MOE_LORA_OK;
 }
 
@@ -321,7 +355,7 @@ int forward_planned(const Plan& p, const moe_lora_desc* d, const moe_lora_weight
     ga.X = static_cast<const uint16_t*>(x); ga.gate_up = 1;
     ga.W = static_cast<const uint16_t*>(w->w_gate_up); ga.N_out = p.I; ga.K = p.H;
     ga.S = s1; ga.Bl = static_cast<const uint16_t*>(w->b_gate_up);
-    ga.S_hl = s1hl; ga.s_hl_stride = s_hl_stride_of(p.r);
+    ga.S_hl = s1hl; ga.s_hl_stride = s_hl_stride_of(p.r); ga.ksw = p.ksw_gu;
     if (p.fused) {
         ga.prod_ncf = (p.r + 15) / 16;
         ga.prod_units = p.nblk_l * ga.prod_ncf * p.ssplit;
@@ -342,7 +376,7 @@ int forward_planned(const Plan& p, const moe_lora_desc* d, const moe_lora_weight
 
     ga.X = h; ga.gate_up = 0; ga.W = static_cast<const uint16_t*>(w->w_down); ga.N_out = p.H;
     ga.K = p.I; ga.S = s2; ga.Bl = static_cast<const uint16_t*>(w->b_down); ga.ksplit = p.ksplit;
-    ga.S_hl = s2hl;
+    ga.S_hl = s2hl; ga.ksw = p.ksw_dn;
     if (p.fuse_combine) {
         ga.out_acc = static_cast<float*>(out);
         ga.topk_w = tw;

@@ -232,16 +232,27 @@ __device__ __forceinline__ void wait_producers(const GemmArgs& a, int target) {
         __hip_atomic_fetch_or(a.status, kStatusWaitTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <bool GATEUP, int FN, int NS>
-__global__ __launch_bounds__(64) void k_gemm_skinny(GemmArgs a) {
-    // 1-D grid: producer units first, then (column tile, block, K range) with
-    // the tile fastest
+// KSW waves per workgroup split the tile's K range into KSW consecutive
+// parts; wave 0 adds the others' partial sums (through LDS, in wave order, so
+// the result is the same on every call), then runs the LoRA expand and the
+// epilogue alone. The library default is one wave per tile: on the
+// decode-shaped layer two waves per down tile measured 118 against 106 us,
+// and on the dense layer's gate_up (800 tiles for 1024 SIMDs) four waves per
+// tile measured 144 against 142 us; a caller or tuning table may still ask
+// for 2 or 4.
+template <bool GATEUP, int FN, int NS, int KSW>
+__global__ __launch_bounds__(64 * KSW) void k_gemm_skinny(GemmArgs a) {
+    const int w = KSW > 1 ? wave_id() : 0;
+    // 1-D grid: producer workgroups first (one producer unit per wave), then
+    // (column tile, block, K range) with the tile fastest
     int wg = blockIdx.x;
-    if (wg < a.prod_units) {
-        shrink_producer(a, wg);
+    const int prod_wgs = (a.prod_units + KSW - 1) / KSW;
+    if (wg < prod_wgs) {
+        const int unit = wg * KSW + w;
+        if (unit < a.prod_units) shrink_producer(a, unit);
         return;
     }
-    wg -= a.prod_units;
+    wg -= prod_wgs;
     constexpr int kCols = GATEUP ? FN * 8 : FN * 16;  // output columns per wave
     const int n_tiles = a.N_out / kCols;
     const int tile = wg % n_tiles, b = (wg / n_tiles) % a.n_blocks;
@@ -254,7 +265,11 @@ __global__ __launch_bounds__(64) void k_gemm_skinny(GemmArgs a) {
     const int Nw = GATEUP ? 2 * a.N_out : a.N_out;
     const int c0 = tile * kCols;
     const int K = a.K;
-    const int Kp = K / a.ksplit, kbeg = z * Kp;  // this workgroup's K range
+    const int Kp = K / a.ksplit;  // this workgroup's K range starts at z Kp
+    // this wave's part of it: 64-wide chunks [q0, q1) (the launcher gives
+    // every wave at least one)
+    const int q0 = w * (Kp / 64) / KSW, q1 = (w + 1) * (Kp / 64) / KSW;
+    const int kbeg = z * Kp + q0 * 64;
 
     const int slot = b * 16 + lrow;
     // Padding rows (sentinel P) re-read the block's first row, which is always
@@ -296,16 +311,16 @@ __global__ __launch_bounds__(64) void k_gemm_skinny(GemmArgs a) {
             for (int f = 0; f < FN; ++f) acc[f] = mfma16x16x32(xb[buf][h], wb[buf][f][h], acc[f]);
     };
 
-    const int nq = Kp / 64;
+    const int nq = q1 - q0;
 #pragma unroll
     for (int st = 0; st + 1 < NS; ++st) load(st, min(st, nq - 1));
     __builtin_amdgcn_sched_barrier(0);
 
     // LoRA expand: acc += S . B^T for every adapter present among the 16 rows
-    // (added once: by the first K range). With S from a separate launch it
-    // runs first, so its latency overlaps the first weight loads; with the
-    // producers in this launch it runs after the base K loop.
-    const bool lora = a.L > 0 && z == 0;
+    // (added once: by the first K range, in its wave 0). With S from a
+    // separate launch it runs first, so its latency overlaps the first weight
+    // loads; with the producers in this launch it runs after the base K loop.
+    const bool lora = a.L > 0 && z == 0 && w == 0;
     const int my_a = lora ? row_adapter(a, slot) : -1;
     // With the producers in this launch the expand runs part-way through or
     // after the base K loop, depending on when the producers finish; it then
@@ -387,6 +402,19 @@ __global__ __launch_bounds__(64) void k_gemm_skinny(GemmArgs a) {
     if (late) {
 #pragma unroll
         for (int f = 0; f < FN; ++f) acc[f] += acc_l[f];
+    }
+    if constexpr (KSW > 1) {
+        __shared__ f32x4 red[KSW - 1][FN][64];
+        if (w > 0) {
+#pragma unroll
+            for (int f = 0; f < FN; ++f) red[w - 1][f][lane] = acc[f];
+        }
+        __syncthreads();
+        if (w > 0) return;
+#pragma unroll
+        for (int v = 0; v < KSW - 1; ++v)
+#pragma unroll
+            for (int f = 0; f < FN; ++f) acc[f] += red[v][f][lane];
     }
 
     const int orow0 = b * 16 + 4 * g;
@@ -1060,6 +1088,14 @@ bool gemm_supported(int N_out, int K, int gate_up, int bm_b) {
     return bm_b == 32 || bm_b == 64 || bm_b == 128 || bm_b == 256;
 }
 
+bool skinny_waves_ok(int K, int ksplit, int ksw) {
+    // one wave per tile takes any K range; with more, every wave keeps at
+    // least 4 chunks of 64 of its workgroup's K range
+    if (ksplit < 1 || K % (64 * ksplit)) return false;
+    if (ksw == 1) return true;
+    return (ksw == 2 || ksw == 4) && K / ksplit / 64 >= 4 * ksw;
+}
+
 int gemm_down_ksplit(int N_out, int K, int bm_b, int n_blocks) {
     if (bm_b >= 128 || n_blocks <= 0) return 1;
     const long cols = bm_b == 16 ? 16 * kSkinnyFNDown : 128;
@@ -1091,13 +1127,20 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
         return hipErrorInvalidValue;
     if (a.bm_b == 16) {
         const int cols = a.gate_up ? kSkinnyFNGateUp * 8 : kSkinnyFNDown * 16;
-        const long total = static_cast<long>(a.N_out / cols) * a.n_blocks * a.ksplit + a.prod_units;
+        const int ksw = a.ksw;
+        if (!(ksw == 1 || ksw == 2 || ksw == 4) || (a.K / a.ksplit) / 64 < ksw) return hipErrorInvalidValue;
+        const long total = static_cast<long>(a.N_out / cols) * a.n_blocks * a.ksplit + (a.prod_units + ksw - 1) / ksw;
         if (total > 0x7fffffffL) return hipErrorInvalidValue;
-        const dim3 grid(static_cast<unsigned>(total)), block(64);
-        if (a.gate_up)
-            hipLaunchKernelGGL((k_gemm_skinny<true, kSkinnyFNGateUp, kSkinnyNSGateUp>), grid, block, 0, s, a);
-        else
-            hipLaunchKernelGGL((k_gemm_skinny<false, kSkinnyFNDown, kSkinnyNSDown>), grid, block, 0, s, a);
+        const dim3 grid(static_cast<unsigned>(total)), block(64 * ksw);
+        if (a.gate_up) {
+            if (ksw == 1) hipLaunchKernelGGL((k_gemm_skinny<true, kSkinnyFNGateUp, kSkinnyNSGateUp, 1>), grid, block, 0, s, a);
+            if (ksw == 2) hipLaunchKernelGGL((k_gemm_skinny<true, kSkinnyFNGateUp, kSkinnyNSGateUp, 2>), grid, block, 0, s, a);
+            if (ksw == 4) hipLaunchKernelGGL((k_gemm_skinny<true, kSkinnyFNGateUp, kSkinnyNSGateUp, 4>), grid, block, 0, s, a);
+        } else {
+            if (ksw == 1) hipLaunchKernelGGL((k_gemm_skinny<false, kSkinnyFNDown, kSkinnyNSDown, 1>), grid, block, 0, s, a);
+            if (ksw == 2) hipLaunchKernelGGL((k_gemm_skinny<false, kSkinnyFNDown, kSkinnyNSDown, 2>), grid, block, 0, s, a);
+            if (ksw == 4) hipLaunchKernelGGL((k_gemm_skinny<false, kSkinnyFNDown, kSkinnyNSDown, 4>), grid, block, 0, s, a);
+        }
         return hipGetLastError();
     }
     switch (a.bm_b) {

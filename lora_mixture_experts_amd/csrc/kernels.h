@@ -96,6 +96,7 @@ struct GemmArgs {
     float* out_acc;
     const float* topk_w;
     int ksplit;               // down only: the K range is cut into ksplit equal parts
+    int ksw;                  // 16-row blocks: waves per tile splitting its K range (1, 2 or 4)
     // optional bf16 hi/lo copy of S (see ShrinkArgs); the direct-load kernel
     // then runs the expand as extra stages of its LDS pipeline
     const uint16_t* S_hl;
@@ -126,6 +127,9 @@ constexpr int32_t kStatusWaitTimeout = 1;
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
 // Whether a tile configuration exists for these sizes.
 bool gemm_supported(int N_out, int K, int gate_up, int bm_b);
+// Whether ksw waves per tile (1, 2 or 4) may split the K range of a 16-row
+// (skinny) projection whose workgroups each own K / ksplit.
+bool skinny_waves_ok(int K, int ksplit, int ksw);
 // K splits for the down projection: enough waves to fill the chip when the
 // grid is small (few blocks, few column tiles, long K); 1 for the large-block
 // kernels. Always divides K / 64.

@@ -28,7 +28,17 @@ class MoeLoraError(RuntimeError):
 
 class Desc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
-                ("T", "H", "I", "E", "top_k", "L", "r", "block_m_base", "block_m_lora", "flags")]
+                ("T", "H", "I", "E", "top_k", "L", "r", "block_m_base", "block_m_lora", "flags",
+                 "down_ksplit", "shrink_ksplit", "waves_gate_up", "waves_down")]
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("block_m_base", "block_m_lora", "down_ksplit", "shrink_ksplit", "waves_gate_up",
+                 "waves_down", "shrinks_in_projections", "combine_in_down")]
+
+    def as_dict(self):
+        return {n: getattr(self, n) for n, _ in self._fields_}
 
 
 class Weights(ctypes.Structure):
@@ -54,6 +64,7 @@ def lib():
             "moe_lora_strerror": ([ctypes.c_int], ctypes.c_char_p),
             "moe_lora_validate": ([pD, pW, SZ], ctypes.c_int),
             "moe_lora_block_sizes": ([pD, pI32, pI32], ctypes.c_int),
+            "moe_lora_plan": ([pD, ctypes.POINTER(PlanInfo)], ctypes.c_int),
             "moe_lora_workspace_bytes": ([pD, pSZ], ctypes.c_int),
             "moe_lora_align_capacity": ([pD, pI32, pI32], ctypes.c_int),
             "moe_lora_route": ([pD, P, P, P, P], ctypes.c_int),
@@ -75,7 +86,7 @@ def lib():
     return _lib
 
 
-EXPORTED = ("moe_lora_strerror", "moe_lora_validate", "moe_lora_block_sizes",
+EXPORTED = ("moe_lora_strerror", "moe_lora_validate", "moe_lora_block_sizes", "moe_lora_plan",
             "moe_lora_workspace_bytes", "moe_lora_align_capacity", "moe_lora_route",
             "moe_lora_align", "moe_lora_forward", "moe_lora_forward_noalloc", "moe_lora_read_stages",
             "moe_lora_read_alignment",
@@ -92,8 +103,21 @@ def _check(rc: int, what: str):
         raise MoeLoraError(rc, what)
 
 
-def make_desc(T, H, I, E, top_k, L, r, block_m_base=0, block_m_lora=0, flags=0) -> Desc:
-    return Desc(T, H, I, E, top_k, L, r, block_m_base, block_m_lora, flags)
+# launch tuning fields of the descriptor (0 = the library's choice)
+TUNING_FIELDS = ("down_ksplit", "shrink_ksplit", "waves_gate_up", "waves_down")
+
+
+def make_desc(T, H, I, E, top_k, L, r, block_m_base=0, block_m_lora=0, flags=0, down_ksplit=0,
+              shrink_ksplit=0, waves_gate_up=0, waves_down=0) -> Desc:
+    return Desc(T, H, I, E, top_k, L, r, block_m_base, block_m_lora, flags, down_ksplit, shrink_ksplit,
+                waves_gate_up, waves_down)
+
+
+def plan(desc: Desc) -> dict:
+    """The launch choices the library makes for a descriptor (host only)."""
+    info = PlanInfo()
+    _check(lib().moe_lora_plan(ctypes.byref(desc), ctypes.byref(info)), "plan")
+    return info.as_dict()
 
 
 def validate(desc: Desc, weights: Weights | None = None, ws_bytes: int = -1) -> int:
@@ -216,22 +240,28 @@ class Layer:
 
     def __init__(self, T, H, I, E, top_k, L, r, w_gate_up, w_down, a_gate_up=None, b_gate_up=None,
                  a_down=None, b_down=None, block_m_base=0, block_m_lora=0, out_bf16=False,
-                 shrink_launch=False, tuning=None, fused_combine=False):
+                 shrink_launch=False, tuning=None, fused_combine=False, **launch):
         """tuning: a tuning.Table; when it holds a choice for this shape and
-        token count it sets the block sizes and the shrink placement (only if
-        none of them is given explicitly)."""
+        token count it sets the block sizes, the shrink placement and the
+        launch tuning fields (only if none of them is given explicitly).
+        launch: any of TUNING_FIELDS (0 = the library's choice)."""
         import torch
+        bad = set(launch) - set(TUNING_FIELDS)
+        if bad:
+            raise TypeError(f"unknown launch options {sorted(bad)}")
         self.tuned = None
-        if tuning is not None and block_m_base == 0 and block_m_lora == 0 and not shrink_launch:
+        if (tuning is not None and block_m_base == 0 and block_m_lora == 0 and not shrink_launch
+                and not any(launch.values())):
             self.tuned = tuning.lookup(T, H, I, E, top_k, L, r)
             if self.tuned is not None:
                 block_m_base = self.tuned.block_m_base
                 block_m_lora = self.tuned.block_m_lora
                 shrink_launch = self.tuned.shrink_launch
+                launch = {f: getattr(self.tuned, f) for f in TUNING_FIELDS}
         self.desc = make_desc(T, H, I, E, top_k, L, r, block_m_base, block_m_lora,
                               (FLAG_OUT_BF16 if out_bf16 else 0) |
                               (FLAG_SHRINK_LAUNCH if shrink_launch else 0) |
-                              (FLAG_FUSED_COMBINE if fused_combine else 0))
+                              (FLAG_FUSED_COMBINE if fused_combine else 0), **launch)
         # the down projection's rows are kept (and readable) only when a
         # separate launch does the weighted combine
         self.keeps_down_rows = not fused_combine

@@ -32,7 +32,23 @@ def candidates(L):
                 yield bm_b, bm_l, True
 
 
-def time_choice(case, copies, out, choice, steps, warmup):
+DOWN_KSPLITS = (1, 2, 3, 4, 5, 6, 8, 10, 12, 16, 20, 25, 32, 50)
+
+
+def split_candidates(case, plan):
+    """Values of each split-K field to try around a resolved plan (the
+    library's own value excluded); the caller keeps whichever is fastest,
+    one field at a time."""
+    out = {"down_ksplit": [d for d in DOWN_KSPLITS
+                           if d != plan["down_ksplit"] and (case.I // 64) % d == 0 and case.I // 64 // d >= 8]}
+    out["shrink_ksplit"] = ([v for v in (1, 2, 3, 4) if v != plan["shrink_ksplit"]]
+                            if case.L > 0 and not plan["shrinks_in_projections"] else [])
+    for f in ("waves_gate_up", "waves_down"):
+        out[f] = [v for v in (1, 2, 4) if v != plan[f]] if plan["block_m_base"] == 16 else []
+    return out
+
+
+def time_choice(case, copies, out, choice, steps, warmup, launch=None):
     import torch
     bm_b, bm_l, sep = choice
     layers = []
@@ -40,7 +56,7 @@ def time_choice(case, copies, out, choice, steps, warmup):
         layers.append(ml.Layer(case.T, case.H, case.I, case.E, case.top_k, case.L, case.r,
                                t["w_gate_up"], t["w_down"], t["a_gate_up"], t["b_gate_up"],
                                t["a_down"], t["b_down"], block_m_base=bm_b, block_m_lora=bm_l,
-                               shrink_launch=sep))
+                               shrink_launch=sep, **(launch or {})))
 
     def step(i):
         t = copies[i % len(copies)]
@@ -92,8 +108,28 @@ def tune_workload(name, folder, rotate=3, steps=None):
     if not results:
         raise RuntimeError(f"{name}: no launch choice produced a valid call")
     us, best = min(results)
+    # then the split-K fields of the best choice, one at a time
+    flags = ml.FLAG_SHRINK_LAUNCH if best[2] else 0
+    plan = ml.plan(ml.make_desc(case.T, case.H, case.I, case.E, case.top_k, case.L, case.r, best[0], best[1],
+                                flags))
+    launch = {}
+    for field, values in split_candidates(case, plan).items():
+        for v in values:
+            trial = dict(launch, **{field: v})
+            d = ml.make_desc(case.T, case.H, case.I, case.E, case.top_k, case.L, case.r, best[0], best[1],
+                             flags, **trial)
+            if ml.validate(d) != ml.OK:
+                continue
+            us_v = time_choice(case, copies, out, best, steps, warmup=2 if heavy else 5, launch=trial)
+            print(json.dumps({"workload": name, "block_m_base": best[0], "block_m_lora": best[1],
+                              "shrink_launch": best[2], **trial,
+                              "us": None if us_v is None else round(us_v, 2)}), flush=True)
+            # keep a change only if it gains more than 1 % (run-to-run noise)
+            if us_v is not None and us_v < 0.99 * us:
+                us, launch = us_v, trial
     shape = {k: getattr(case, k) for k in tuning.SHAPE_KEYS}
     entry = {"T_max": case.T, "block_m_base": best[0], "block_m_lora": best[1], "shrink_launch": best[2],
+             **{k: launch.get(k, 0) for k in tuning.SPLIT_KEYS},
              "us": round(us, 2),
              "us_library_default": None if us_default is None else round(us_default, 2)}
     path = tuning.save_entry(folder, shape, entry)

@@ -5,9 +5,12 @@ on Amazon SageMaker AI and Amazon Bedrock" (section "Tuning kernel
 configurations for Amazon SageMaker AI and Amazon Bedrock") tunes the MoE-LoRA
 kernels per shape and loads the tuned configurations from a user-supplied
 folder. Here a configuration is what the C ABI lets a caller choose without
-changing results: the row blocks of the two alignment views and whether the
-LoRA shrinks get launches of their own. Any valid choice computes the same
-layer (up to fp32 summation order); the table only decides speed.
+changing results: the row blocks of the two alignment views (which also pick
+each projection's tile shape), whether the LoRA shrinks get launches of their
+own, and the split-K factors: K ranges of the down projection and of the
+shrinks, and waves per tile of the 16-row projections. Any valid choice
+computes the same layer (up to fp32 summation order); the table only decides
+speed.
 
 A folder holds one JSON file per layer shape (written by
 ``python -m lora_mixture_experts_amd.tune``)::
@@ -15,7 +18,10 @@ A folder holds one JSON file per layer shape (written by
     {"shape": {"H": 2880, "I": 2880, "E": 32, "top_k": 4, "L": 8, "r": 32},
      "device": "gfx950",
      "entries": [{"T_max": 16, "block_m_base": 16, "block_m_lora": 16,
-                  "shrink_launch": false, "us": 307.9}, ...]}
+                  "shrink_launch": false, "down_ksplit": 0, "shrink_ksplit": 0,
+                  "waves_gate_up": 0, "waves_down": 0, "us": 307.9}, ...]}
+
+The four split-K keys are optional (0 or absent = the library's choice).
 
 An entry covers the token counts ``T_min <= T <= T_max``; ``T_min`` is
 optional and defaults to ``T_max // 2 + 1``, so a choice tuned at one batch
@@ -32,6 +38,7 @@ from dataclasses import dataclass
 
 SHAPE_KEYS = ("H", "I", "E", "top_k", "L", "r")
 POW2_BLOCKS = (16, 32, 64, 128, 256)
+SPLIT_KEYS = ("down_ksplit", "shrink_ksplit", "waves_gate_up", "waves_down")
 
 
 @dataclass(frozen=True)
@@ -39,6 +46,15 @@ class Choice:
     block_m_base: int
     block_m_lora: int
     shrink_launch: bool
+    down_ksplit: int = 0
+    shrink_ksplit: int = 0
+    waves_gate_up: int = 0
+    waves_down: int = 0
+
+
+def choice_of(e) -> Choice:
+    return Choice(e["block_m_base"], e["block_m_lora"], bool(e.get("shrink_launch", False)),
+                  *(int(e.get(k, 0)) for k in SPLIT_KEYS))
 
 
 def shape_key(H, I, E, top_k, L, r):
@@ -67,6 +83,13 @@ def _check_entry(e, where):
             raise ValueError(f"{where}: {key} must be one of {POW2_BLOCKS}: {e}")
     if not isinstance(e.get("shrink_launch", False), bool):
         raise ValueError(f"{where}: shrink_launch must be a boolean: {e}")
+    for key in SPLIT_KEYS:
+        v = e.get(key, 0)
+        if not isinstance(v, int) or isinstance(v, bool) or v < 0:
+            raise ValueError(f"{where}: {key} must be an integer >= 0: {e}")
+    for key in ("waves_gate_up", "waves_down"):
+        if e.get(key, 0) not in (0, 1, 2, 4):
+            raise ValueError(f"{where}: {key} must be 0, 1, 2 or 4: {e}")
 
 
 class Table:
@@ -86,7 +109,7 @@ class Table:
     def lookup(self, T, H, I, E, top_k, L, r) -> Choice | None:
         for e in self._by_shape.get(shape_key(H, I, E, top_k, L, r), []):
             if t_min_of(e) <= T <= e["T_max"]:
-                return Choice(e["block_m_base"], e["block_m_lora"], bool(e.get("shrink_launch", False)))
+                return choice_of(e)
         return None
 
     def shapes(self):

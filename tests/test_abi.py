@@ -164,3 +164,50 @@ def test_fused_combine_drops_the_down_rows_from_the_workspace():
         bf16 = ml.workspace_bytes(ml.make_desc(*args, flags=ml.FLAG_OUT_BF16))
         C_b, _ = ml.align_capacity(ml.make_desc(*args))
         assert kept == bf16 and kept - fused >= 4 * C_b * d["H"], name
+
+
+def test_plan_resolves_the_library_defaults():
+    d = wl.CONFIGS["decode"]
+    p = ml.plan(ml.make_desc(d["T"], d["H"], d["I"], d["E"], d["top_k"], d["L"], d["r"]))
+    assert p["block_m_base"] == 16 and p["down_ksplit"] == 1 and p["waves_gate_up"] == 1
+    assert p["shrinks_in_projections"] == 1 and p["combine_in_down"] == 0
+    d = wl.CONFIGS["prefill"]
+    p = ml.plan(ml.make_desc(d["T"], d["H"], d["I"], d["E"], d["top_k"], d["L"], d["r"]))
+    assert p["block_m_base"] == 128 and p["waves_down"] == 0 and p["shrinks_in_projections"] == 0
+
+
+@pytest.mark.parametrize("over", [
+    dict(down_ksplit=-1), dict(down_ksplit=7),           # 45 chunks: 7 does not divide
+    dict(down_ksplit=2, bm_b=128),                        # direct-load kernels take all of K
+    dict(down_ksplit=90),                                 # more ranges than chunks
+    dict(shrink_ksplit=5), dict(shrink_ksplit=2),         # decode runs the shrinks in the projections (1)
+    dict(waves_gate_up=3), dict(waves_down=8),
+    dict(waves_down=2, bm_b=32),                          # waves per tile only for 16-row blocks
+    dict(waves_down=4, down_ksplit=3),                    # 15 chunks per range < 4 per wave x 4
+])
+def test_validate_rejects_bad_split_fields(over):
+    over = dict(over)
+    bm_b = over.pop("bm_b", 0)
+    d = wl.CONFIGS["decode"]
+    ds = ml.make_desc(d["T"], d["H"], d["I"], d["E"], d["top_k"], d["L"], d["r"], bm_b, 0, **over)
+    assert ml.validate(ds) == ml.EINVAL
+
+
+def test_split_fields_change_only_the_plan_and_workspace():
+    d = wl.CONFIGS["wide"]
+    args = [d[k] for k in ("T", "H", "I", "E", "top_k", "L", "r")]
+    base = ml.make_desc(*args, 32, 16)
+    more = ml.make_desc(*args, 32, 16, down_ksplit=4, shrink_ksplit=1)  # I/64 = 172 chunks
+    assert ml.validate(more) == ml.OK
+    p = ml.plan(more)
+    assert p["down_ksplit"] == 4 and p["shrink_ksplit"] == 1
+    # one fp32 D partial per K range
+    C_b, _ = ml.align_capacity(base)
+    assert ml.workspace_bytes(more) > ml.workspace_bytes(base)
+
+
+def test_one_wave_per_tile_takes_any_k():
+    # the smallest K (one chunk of 64) with 16-row blocks
+    ds = ml.make_desc(37, 64, 64, 70, 7, 3, 8, 16, 16)
+    assert ml.validate(ds) == ml.OK
+    assert ml.validate(ml.make_desc(37, 64, 64, 70, 7, 3, 8, 16, 16, waves_down=2)) == ml.EINVAL

@@ -272,6 +272,45 @@ def test_layer_block_sizes(dev, bm, fused):
     check_layer(case, dev, bm=bm, stages=True, fused_combine=fused)
 
 
+# the split-K launch fields: each value computes the same layer
+SPLIT_CASES = [
+    # 16-row blocks: waves per tile of each projection, with and without a
+    # down K split, and with the shrinks inside the projections (decode)
+    ("decode", None, (16, 16), dict(waves_gate_up=2, waves_down=2)),
+    ("decode", None, (16, 16), dict(waves_gate_up=4, waves_down=2, down_ksplit=3)),
+    ("decode", None, (16, 16), dict(down_ksplit=5)),
+    # 32- and 64-row blocks: down K ranges and separate shrinks split over K
+    ("wide", None, (32, 16), dict(down_ksplit=4, shrink_ksplit=2)),
+    ("kdown", dict(T=40, H=256, I=1024, E=3, top_k=2, L=2, r=16), (64, 16), dict(down_ksplit=16, shrink_ksplit=3)),
+    # 128-row blocks: a split shrink moves the expand out of the pipeline
+    ("kdma", dict(T=300, H=256, I=512, E=2, top_k=1, L=3, r=32), (128, 16), dict(shrink_ksplit=4)),
+]
+
+
+@pytest.mark.parametrize("name,dims,bm,launch", SPLIT_CASES)
+def test_split_fields_keep_parity(dev, name, dims, bm, launch):
+    log(f"split fields {name} {bm} {launch}")
+    case = build_case(name, dims=dims, seed=None if dims is None else 70 + len(name))
+    ids, w = oracle.route(case.logits, case.top_k)
+    ref = oracle.forward(case, ids, w)
+    t = wl.device_tensors(case, dev)
+    layer = ml.Layer(case.T, case.H, case.I, case.E, case.top_k, case.L, case.r, t["w_gate_up"], t["w_down"],
+                     t["a_gate_up"], t["b_gate_up"], t["a_down"], t["b_down"], block_m_base=bm[0],
+                     block_m_lora=bm[1], **launch)
+    plan = ml.plan(layer.desc)
+    for k, v in launch.items():
+        assert plan[k] == v, (k, plan)
+    out = layer(t["x"], t["logits"], t["adapter_ids"])
+    torch.cuda.synchronize()
+    assert layer.status() == 0
+    mx, mean = metrics(out.cpu().numpy(), ref)
+    log(f"  max {mx:.2e} mean {mean:.2e}")
+    assert mx <= MAX_TOL and mean <= MEAN_TOL, (mx, mean)
+    out2 = layer(t["x"], t["logits"], t["adapter_ids"])
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2)
+
+
 @pytest.mark.parametrize("bm", [(16, 16), (32, 16)])
 def test_fused_combine_with_down_k_split(dev, bm):
     # a long down K (I = 6144) on a small grid: the down projection is cut
@@ -569,14 +608,16 @@ def test_tuning_table_choice_is_used_and_keeps_parity(dev, tmp_path):
     case = build_case("tiny")
     shape = {k: getattr(case, k) for k in tuning.SHAPE_KEYS}
     tuning.save_entry(str(tmp_path), shape, {"T_max": case.T, "block_m_base": 32, "block_m_lora": 64,
-                                             "shrink_launch": True})
+                                             "shrink_launch": True, "down_ksplit": 2, "shrink_ksplit": 2})
     table = tuning.load(str(tmp_path))
     t = wl.device_tensors(case, dev)
     layer = ml.Layer(case.T, case.H, case.I, case.E, case.top_k, case.L, case.r, t["w_gate_up"], t["w_down"],
                      t["a_gate_up"], t["b_gate_up"], t["a_down"], t["b_down"], tuning=table)
-    assert layer.tuned == tuning.Choice(32, 64, True)
+    assert layer.tuned == tuning.Choice(32, 64, True, down_ksplit=2, shrink_ksplit=2)
     assert ml.block_sizes(layer.desc) == (32, 64)
     assert layer.desc.flags & ml.FLAG_SHRINK_LAUNCH
+    p = ml.plan(layer.desc)
+    assert p["down_ksplit"] == 2 and p["shrink_ksplit"] == 2
     out = layer(t["x"], t["logits"], t["adapter_ids"])
     torch.cuda.synchronize()
     ids, w = oracle.route(case.logits, case.top_k)
@@ -595,7 +636,7 @@ def test_tuner_writes_a_loadable_table(dev, tmp_path):
     table = tuning.load(str(tmp_path))
     c = wl.CONFIGS["tiny"]
     got = table.lookup(c["T"], c["H"], c["I"], c["E"], c["top_k"], c["L"], c["r"])
-    assert got == tuning.Choice(entry["block_m_base"], entry["block_m_lora"], entry["shrink_launch"])
+    assert got == tuning.choice_of(entry)
     assert entry["us"] <= entry["us_library_default"]
 
 

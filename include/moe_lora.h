@@ -70,6 +70,12 @@ extern "C" {
  *                                   a fixed order: bitwise repeatable (and
  *                                   faster on MI355X at every measured shape).
  *                                   Not with OUT_BF16.
+ *     MOE_LORA_FLAG_NO_SHRINK_WAIT  where the shrinks run inside the
+ *                                   projection launches, projection waves do
+ *                                   not wait for them: each computes the shrink
+ *                                   of its own rows (the path a wait that runs
+ *                                   out takes; same results to rounding,
+ *                                   slower; for tests of that path)
  *   any other bit is an error.
  *   Launch tuning (0 = the library's choice; any valid value computes the
  *   same layer up to the order of fp32 sums; these are what a per-shape
@@ -88,6 +94,7 @@ extern "C" {
 #define MOE_LORA_FLAG_OUT_BF16 1
 #define MOE_LORA_FLAG_SHRINK_LAUNCH 2
 #define MOE_LORA_FLAG_FUSED_COMBINE 4
+#define MOE_LORA_FLAG_NO_SHRINK_WAIT 8
 typedef struct moe_lora_desc {
     int32_t T, H, I, E, top_k, L, r;
     int32_t block_m_base, block_m_lora;
@@ -187,9 +194,10 @@ int moe_lora_align(const moe_lora_desc *d, const int32_t *topk_ids, const int32_
  * the LoRA shrinks run inside the projection launches too, as producer waves
  * beside the base weight stream; the projection waves wait for them, by
  * polling a counter in the workspace, only before their expand. Such a wait
- * is bounded (about a second of polling): if it ever ran out, every wave
- * still ends, the output is not valid, and moe_lora_read_status reports
- * MOE_LORA_STATUS_WAIT_TIMEOUT. */
+ * is bounded (about a second of polling): a wave whose wait runs out
+ * computes the shrink of its own rows instead, so the output is valid
+ * whatever order the hardware starts the waves in, and moe_lora_read_status
+ * reports MOE_LORA_STATUS_SHRINK_FALLBACK (a performance signal). */
 int moe_lora_forward(const moe_lora_desc *d, const moe_lora_weights *w, const void *x,
                      const float *logits, const int32_t *adapter_ids, void *out,
                      void *workspace, size_t ws_bytes, void *stream);
@@ -237,11 +245,12 @@ int moe_lora_read_stages(const moe_lora_desc *d, const void *workspace, size_t w
 
 /* Status of the last moe_lora_forward with T > 0 on `workspace`: copies one
  * int32 into `status` (a device pointer, like every tensor argument) on
- * `stream`. 0 means the call ran as specified; MOE_LORA_STATUS_WAIT_TIMEOUT
- * means a projection wave stopped waiting for the shrink waves of its launch,
- * and that call's output is not valid. Each forward call with T > 0 clears
- * the word first. */
-#define MOE_LORA_STATUS_WAIT_TIMEOUT 1
+ * `stream`. 0 means every projection wave found the shrink of its launch
+ * done; MOE_LORA_STATUS_SHRINK_FALLBACK means at least one wave stopped
+ * waiting for it and computed the shrink of its own rows (the output is
+ * valid; the call was slower than it should be). Each forward call with
+ * T > 0 clears the word first. */
+#define MOE_LORA_STATUS_SHRINK_FALLBACK 1
 int moe_lora_read_status(const moe_lora_desc *d, const void *workspace, size_t ws_bytes,
                          int32_t *status, void *stream);
 

@@ -61,7 +61,8 @@ int check_desc(const moe_lora_desc* d) {
     if (d->E > 1024 || d->top_k < 1 || d->top_k > d->E || d->top_k > 32) return MOE_LORA_EINVAL;
     if (d->L > 0 && !(d->r == 8 || d->r == 16 || d->r == 32 || d->r == 64 || d->r == 128))
         return MOE_LORA_EINVAL;
-    if (d->flags & ~(MOE_LORA_FLAG_OUT_BF16 | MOE_LORA_FLAG_SHRINK_LAUNCH | MOE_LORA_FLAG_FUSED_COMBINE))
+    if (d->flags & ~(MOE_LORA_FLAG_OUT_BF16 | MOE_LORA_FLAG_SHRINK_LAUNCH | MOE_LORA_FLAG_FUSED_COMBINE |
+                     MOE_LORA_FLAG_NO_SHRINK_WAIT))
         return MOE_LORA_EINVAL;
     if ((d->flags & MOE_LORA_FLAG_FUSED_COMBINE) && (d->flags & MOE_LORA_FLAG_OUT_BF16)) return MOE_LORA_EINVAL;
     if (d->block_m_base != 0 && !pow2_in(d->block_m_base, 16, 256)) return MOE_LORA_EINVAL;
@@ -363,6 +364,7 @@ int forward_planned(const Plan& p, const moe_lora_desc* d, const moe_lora_weight
         ga.slot_of_pair = slot; ga.Al = static_cast<const uint16_t*>(w->a_gate_up);
         ga.bm_l = p.bm_l; ga.S_out = s1; ga.done = counts + 2; ga.n_l = counts + 1;
         ga.status = counts + 4;
+        ga.max_polls = (d->flags & MOE_LORA_FLAG_NO_SHRINK_WAIT) ? 0 : kMaxProducerPolls;
     }
     ok(launch_gemm(ga, s));
     timing_mark(call, 4, s);

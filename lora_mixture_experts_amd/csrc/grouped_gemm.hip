@@ -119,12 +119,14 @@ __device__ __forceinline__ u32x4 load_lora_b(const GemmArgs& a, int Nw, int ad, 
 // of a launch of their own. A projection wave multiplies its base K range
 // first and waits for the producers only before its expand.
 
-// Upper bound on the polls of a projection wave waiting for the producers. The
-// hardware dispatches the workgroups of a grid in index order, so every
-// producer (the lowest indices) is resident before any projection wave that
-// could wait for it, and producers never wait; the bound only guarantees that
-// every wave ends (about a second at most).
-constexpr int kMaxProducerPolls = 1 << 20;
+// Projection waves wait for the producers by polling a counter, at most
+// GemmArgs::max_polls times (the library passes kMaxProducerPolls, about a
+// second). The producers have the lowest workgroup indices and never wait, so
+// in practice they are done long before (the dispatcher starts a grid's
+// workgroups in index order). Nothing depends on that: a wave whose wait runs
+// out computes the shrink of its own rows and flags the slow path in the
+// call's status word, so every wave ends and the output is valid whatever the
+// dispatch order.
 
 // One producer unit: the 16 S columns cf of LoRA-view block bl over K range ks,
 // for every real row of the block. Once all of its stores have completed, the
@@ -220,26 +222,88 @@ __device__ __forceinline__ int producer_target(const GemmArgs& a) {
     return (*a.n_l / a.bm_l) * a.prod_ncf * a.s_split;
 }
 
-// Poll until producers_done (bounded by kMaxProducerPolls). A wait that runs
-// out sets the call's status word, so the host can tell that the output is
-// not valid.
-__device__ __forceinline__ void wait_producers(const GemmArgs& a, int target) {
-    for (int polls = 0; polls < kMaxProducerPolls; ++polls) {
-        if (producers_done(a, target)) return;
+// Poll until producers_done, at most a.max_polls times. A wait that runs out
+// returns false and sets the call's status word: the wave then computes the
+// shrink of its own rows (expand_own_shrink), so the output stays valid and
+// the word only tells the host that the slow path ran.
+__device__ __forceinline__ bool wait_producers(const GemmArgs& a, int target) {
+    for (int polls = 0; polls < a.max_polls; ++polls) {
+        if (producers_done(a, target)) return true;
         __builtin_amdgcn_s_sleep(2);
     }
     if ((threadIdx.x & 63) == 0)
-        __hip_atomic_fetch_or(a.status, kStatusWaitTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_or(a.status, kStatusShrinkFallback, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return false;
 }
 
-// KSW waves per workgroup split the tile's K range into KSW consecutive
-// parts; wave 0 adds the others' partial sums (through LDS, in wave order, so
-// the result is the same on every call), then runs the LoRA expand and the
-// epilogue alone. The library default is one wave per tile: on the
-// decode-shaped layer two waves per down tile measured 118 against 106 us,
-// and on the dense layer's gate_up (800 tiles for 1024 SIMDs) four waves per
-// tile measured 144 against 142 us; a caller or tuning table may still ask
-// for 2 or 4.
+// The expand of a projection wave that computes the shrink of its own 16 rows
+// (its wait for the shrink waves of the launch ran out). For each adapter run
+// among the rows and each 32-wide chunk c of the rank, S^T = A . X^T by MFMA
+// over the whole K, the LoRA A rows 32 c .. 32 c + 15 and 32 c + 16 .. 32 c + 31
+// against the wave's 16 X rows (xrow0: this lane's X row at element 16 g).
+// Lane (row, g) then holds S[row][32 c + 4 g + i] and S[row][32 c + 16 + 4 g + i],
+// i < 4: the expand of chunk c takes its K slots in that order and reads the
+// LoRA B operand as two 4-element halves to match. S is split into bf16 hi
+// and lo parts as in load_s_hilo.
+template <bool GATEUP, int FN>
+__device__ __forceinline__ void expand_own_shrink(const GemmArgs& a, int e, int c0, int I, int Nw, int my_a,
+                                                  const uint16_t* xrow0, f32x4 (&dst)[FN]) {
+    const int lane = threadIdx.x & 63, g = lane >> 4, lrow = lane & 15;
+    const int K = a.K, r = a.r;
+    bool pending = my_a >= 0;
+    while (true) {
+        const uint64_t m = ballot64(pending);
+        if (m == 0) break;
+        const int acur = __shfl(my_a, __ffsll(static_cast<long long>(m)) - 1);
+        const bool in_run = pending && my_a == acur;
+        pending = pending && !in_run;
+        const uint16_t* ablk = a.Al + static_cast<size_t>(acur * a.E + e) * r * K;
+        // one 32-wide chunk c of the rank at a time: fragments 2 c and 2 c + 1
+        for (int c = 0; 32 * c < r; ++c) {
+            f32x4 st0 = f32x4{0.f, 0.f, 0.f, 0.f}, st1 = st0;
+            // A rows 32 c + lrow and 32 c + 16 + lrow; rows past r re-read
+            // row lrow % r and their outputs are never used
+            const int ja = 32 * c + lrow, jb = ja + 16;
+            const uint16_t* arow0 = ablk + static_cast<size_t>(ja < r ? ja : lrow % r) * K + 16 * g;
+            const uint16_t* arow1 = ablk + static_cast<size_t>(jb < r ? jb : lrow % r) * K + 16 * g;
+            for (int q = 0; q < K / 64; ++q) {
+                const u32x4 x0 = ld16(xrow0 + q * 64), x1 = ld16(xrow0 + q * 64 + 8);
+                const u32x4 a0 = ld16(arow0 + q * 64), a1 = ld16(arow0 + q * 64 + 8);
+                const u32x4 b0 = ld16(arow1 + q * 64), b1 = ld16(arow1 + q * 64 + 8);
+                st0 = mfma16x16x32(a0, x0, st0);
+                st0 = mfma16x16x32(a1, x1, st0);
+                st1 = mfma16x16x32(b0, x0, st1);
+                st1 = mfma16x16x32(b1, x1, st1);
+            }
+            const int j1 = 32 * c + 4 * g, j2 = j1 + 16;
+            float v[8], rest[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                v[i] = (in_run && j1 + i < r) ? st0[i] : 0.f;
+                v[4 + i] = (in_run && j2 + i < r) ? st1[i] : 0.f;
+            }
+            const u32x4 hi = pack_bf16x8(v);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const uint32_t word = hi[q >> 1];
+                const uint16_t bits = (q & 1) ? static_cast<uint16_t>(word >> 16) : static_cast<uint16_t>(word);
+                rest[q] = v[q] - bf16_to_f32(bits);
+            }
+            const u32x4 lo = pack_bf16x8(rest);
+#pragma unroll
+            for (int f = 0; f < FN; ++f) {
+                const uint16_t* brow =
+                    a.Bl + (static_cast<size_t>(acur * a.E + e) * Nw + w_row_of_frag<GATEUP>(f, c0, I) + lrow) * r;
+                const uint2 h1 = j1 < r ? *reinterpret_cast<const uint2*>(brow + j1) : make_uint2(0, 0);
+                const uint2 h2 = j2 < r ? *reinterpret_cast<const uint2*>(brow + j2) : make_uint2(0, 0);
+                const u32x4 bb = u32x4{h1.x, h1.y, h2.x, h2.y};
+                dst[f] = mfma16x16x32(hi, bb, dst[f]);
+                dst[f] = mfma16x16x32(lo, bb, dst[f]);
+            }
+        }
+    }
+}
+
 template <bool GATEUP, int FN, int NS, int KSW>
 __global__ __launch_bounds__(64 * KSW) void k_gemm_skinny(GemmArgs a) {
     const int w = KSW > 1 ? wave_id() : 0;
@@ -376,7 +440,7 @@ __global__ __launch_bounds__(64 * KSW) void k_gemm_skinny(GemmArgs a) {
     // bounds) and is discarded.
     int q = 0;
     for (; q + NS <= nq; q += NS) {
-        if (!expanded && q == q_mid) {
+        if (!expanded && q == q_mid && a.max_polls > 0) {
             if (producers_done(a, target)) {
                 expand(std::true_type{}, acc_l);
                 expanded = true;
@@ -396,8 +460,10 @@ __global__ __launch_bounds__(64 * KSW) void k_gemm_skinny(GemmArgs a) {
         if (st < nq - q) compute(st);
 
     if (!expanded) {
-        wait_producers(a, target);
-        expand(std::true_type{}, acc_l);
+        if (wait_producers(a, target))
+            expand(std::true_type{}, acc_l);
+        else
+            expand_own_shrink<GATEUP, FN>(a, e, c0, I, Nw, my_a, xrow, acc_l);  // xrow: K offset 0 here
     }
     if (late) {
 #pragma unroll

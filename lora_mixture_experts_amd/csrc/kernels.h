@@ -121,9 +121,12 @@ struct GemmArgs {
     int32_t* done;                // producer completion count, zero at launch
     const int32_t* n_l;           // padded LoRA-view length (live LoRA blocks x bm_l)
     int32_t* status;              // the call's status word (kStatus* bits), zero at launch
+    int max_polls;                // polls of a projection wave waiting for the producers
 };
-// status bit: a projection wave stopped waiting for the producers (output invalid)
-constexpr int32_t kStatusWaitTimeout = 1;
+// status bit: a projection wave stopped waiting for the producers and
+// computed the shrink of its own rows (output valid, slower)
+constexpr int32_t kStatusShrinkFallback = 1;
+constexpr int kMaxProducerPolls = 1 << 20;
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
 // Whether a tile configuration exists for these sizes.
 bool gemm_supported(int N_out, int K, int gate_up, int bm_b);

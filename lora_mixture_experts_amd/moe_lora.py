@@ -17,6 +17,7 @@ SCRATCH_BYTES = 64 << 20
 FLAG_OUT_BF16 = 1
 FLAG_SHRINK_LAUNCH = 2
 FLAG_FUSED_COMBINE = 4
+FLAG_NO_SHRINK_WAIT = 8
 NKERNELS = 7
 
 
@@ -198,7 +199,7 @@ def read_stages(desc, workspace, topk_ids=None, topk_w=None, s1=None, h=None, s2
                                       _ptr(dn), _stream(stream)), "read_stages")
 
 
-STATUS_WAIT_TIMEOUT = 1
+STATUS_SHRINK_FALLBACK = 1
 
 
 def read_status(desc, workspace, status, stream=None):
@@ -240,7 +241,7 @@ class Layer:
 
     def __init__(self, T, H, I, E, top_k, L, r, w_gate_up, w_down, a_gate_up=None, b_gate_up=None,
                  a_down=None, b_down=None, block_m_base=0, block_m_lora=0, out_bf16=False,
-                 shrink_launch=False, tuning=None, fused_combine=False, **launch):
+                 shrink_launch=False, tuning=None, fused_combine=False, no_shrink_wait=False, **launch):
         """tuning: a tuning.Table; when it holds a choice for this shape and
         token count it sets the block sizes, the shrink placement and the
         launch tuning fields (only if none of them is given explicitly).
@@ -261,7 +262,8 @@ class Layer:
         self.desc = make_desc(T, H, I, E, top_k, L, r, block_m_base, block_m_lora,
                               (FLAG_OUT_BF16 if out_bf16 else 0) |
                               (FLAG_SHRINK_LAUNCH if shrink_launch else 0) |
-                              (FLAG_FUSED_COMBINE if fused_combine else 0), **launch)
+                              (FLAG_FUSED_COMBINE if fused_combine else 0) |
+                              (FLAG_NO_SHRINK_WAIT if no_shrink_wait else 0), **launch)
         # the down projection's rows are kept (and readable) only when a
         # separate launch does the weighted combine
         self.keeps_down_rows = not fused_combine
@@ -280,7 +282,9 @@ class Layer:
         return out
 
     def status(self, stream=None) -> int:
-        """Status word of the last call (0 = ran as specified); synchronises."""
+        """Status word of the last call (0 = every projection wave found the
+        shrink of its launch done; STATUS_SHRINK_FALLBACK = some wave computed
+        its own, output still valid); synchronises."""
         import torch
         st = torch.full((1,), -1, dtype=torch.int32, device=self.device)
         read_status(self.desc, self.workspace, st, stream)

@@ -42,8 +42,8 @@ def desc(**over):
 @pytest.mark.parametrize("over", [dict(H=2881), dict(I=100), dict(top_k=0), dict(top_k=33, E=40),
                                   dict(top_k=5, E=4), dict(r=24), dict(E=0), dict(T=-1), dict(L=-1),
                                   dict(bm_b=48), dict(bm_b=8), dict(bm_l=512), dict(E=1025),
-                                  dict(E=128, L=200), dict(E=1024, L=9, top_k=8), dict(flags=8), dict(flags=5),
-                                  dict(flags=-1), dict(flags=15)])
+                                  dict(E=128, L=200), dict(E=1024, L=9, top_k=8), dict(flags=16), dict(flags=5),
+                                  dict(flags=-1), dict(flags=31)])
 def test_validate_rejects(over):
     assert ml.validate(desc(**over)) == ml.EINVAL
 

@@ -382,11 +382,57 @@ def test_shrinks_inside_projections(dev, name, dims, bm, pure):
     assert layer.status() == 0
 
 
+@pytest.mark.parametrize("name,dims,bm,pure", FUSED_CASES)
+def test_projection_waves_compute_their_own_shrink(dev, name, dims, bm, pure):
+    # the path a projection wave takes when its bounded wait for the shrink
+    # waves of its launch runs out, forced for every wave from the host: each
+    # computes the shrink of its own rows, the output still matches the
+    # oracle, and the status word reports the slow path
+    log(f"own shrink {name} bm={bm} pure={pure}")
+    case = build_case(name, dims=dims, seed=None if dims is None else 90 + len(name))
+    if pure:
+        case.w_gate_up[:] = 0
+        case.w_down[:] = 0
+    ids, w = oracle.route(case.logits, case.top_k)
+    ref = oracle.forward(case, ids, w)
+    t = wl.device_tensors(case, dev)
+    mk = lambda **kw: ml.Layer(case.T, case.H, case.I, case.E, case.top_k, case.L, case.r, t["w_gate_up"],
+                               t["w_down"], t["a_gate_up"], t["b_gate_up"], t["a_down"], t["b_down"],
+                               block_m_base=bm[0], block_m_lora=bm[1], **kw)
+    own = mk(no_shrink_wait=True)
+    assert ml.plan(own.desc)["shrinks_in_projections"] == 1
+    out = own(t["x"], t["logits"], t["adapter_ids"])
+    torch.cuda.synchronize()
+    assert own.status() == ml.STATUS_SHRINK_FALLBACK
+    mx, mean = metrics(out.cpu().numpy(), ref)
+    log(f"  max {mx:.2e} mean {mean:.2e}")
+    assert np.all(np.isfinite(out.cpu().numpy()))
+    assert mx <= MAX_TOL and mean <= MEAN_TOL, (mx, mean)
+    # and agrees with the producers' path far inside the oracle bars
+    normal = mk()
+    out_n = normal(t["x"], t["logits"], t["adapter_ids"])
+    torch.cuda.synchronize()
+    assert normal.status() == 0
+    mx, mean = metrics(out.cpu().numpy(), out_n.cpu().numpy())
+    assert mx < MAX_TOL / 10 and mean < MEAN_TOL / 10, (mx, mean)
+
+
 def test_status_word_is_cleared_by_each_call(dev):
     # the status word lives in the workspace and each forward call clears it
     log("status word")
     case = build_case("decode")
     layer, t, _ = run_gpu(case, dev)
+    assert layer.status() == 0
+    # a call that sets it (every projection wave computes its own shrink),
+    # then a normal call on the same workspace clears it again
+    own = ml.Layer(case.T, case.H, case.I, case.E, case.top_k, case.L, case.r, t["w_gate_up"], t["w_down"],
+                   t["a_gate_up"], t["b_gate_up"], t["a_down"], t["b_down"], no_shrink_wait=True)
+    own.workspace = layer.workspace
+    own(t["x"], t["logits"], t["adapter_ids"])
+    torch.cuda.synchronize()
+    assert layer.status() == ml.STATUS_SHRINK_FALLBACK
+    layer(t["x"], t["logits"], t["adapter_ids"])
+    torch.cuda.synchronize()
     assert layer.status() == 0
     # poison the whole workspace, including the status word; a forward call
     # writes every workspace entry before it reads it (the alignment fills

@@ -20,8 +20,14 @@ from lora_mixture_experts_amd import build as B
 
 # minimum waves per SIMD, by kernel name prefix (demangled form)
 MIN_OCCUPANCY = {
-    "k_gemm_skinny<true, 4, 2, ": 3,  # every waves-per-tile variant
-    "k_gemm_skinny<false, 4, 2, ": 3,
+    # one wave per tile (the library's choice); the 2- and 4-wave variants
+    # are tuning options
+    "k_gemm_skinny<true, 4, 2, 1>": 3,
+    "k_gemm_skinny<false, 4, 2, 1>": 3,
+    "k_gemm_skinny<true, 4, 2, 2>": 2,
+    "k_gemm_skinny<true, 4, 2, 4>": 2,
+    "k_gemm_skinny<false, 4, 2, 2>": 2,
+    "k_gemm_skinny<false, 4, 2, 4>": 2,
     "k_gemm_tiled<32, 128, 1, 4, true>": 4,
     "k_gemm_tiled<32, 128, 1, 4, false>": 4,
     "k_gemm_tiled<64, 128, 2, 2, true>": 3,

@@ -146,9 +146,9 @@ int make_plan(const moe_lora_desc* d, Plan* p) {
     const size_t sbytes = p->L > 0 ? 4ul * p->ssplit * p->C_b * p->r : 0;
     p->off_s1 = take(sbytes);
     p->off_s2 = take(sbytes);
-    // the direct-load kernels (128- and 256-row blocks, never a split shrink)
-    // run the expand in their pipeline from a bf16 hi/lo copy of S
-    p->s_hl = p->L > 0 && p->bm_b >= 128 && p->ssplit == 1;
+    // the LDS kernels (32- to 256-row blocks, never a split shrink) run the
+    // expand in their pipeline from a bf16 hi/lo copy of S
+    p->s_hl = p->L > 0 && p->bm_b >= 32 && p->ssplit == 1;
     const size_t hlbytes = p->s_hl ? 2ul * p->C_b * s_hl_stride_of(p->r) : 0;
     p->off_s1hl = take(hlbytes);
     p->off_s2hl = take(hlbytes);

@@ -750,12 +750,63 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_tiled(GemmArgs a) {
     const bool wlive = a.sorted_b[wrow_base] < a.P;
     u32x4 ra[2][C::A_LD], rb[2][C::B_LD];
     const int nk = Kp / 64;
+
+    // LoRA expand as extra stages of the same pipeline, for every adapter run
+    // of the tile (rows are ordered by adapter, so each adapter's rows form one
+    // run; no cap on the number of runs): per run, s_hl_stride / 64 stages
+    // whose A rows are the run's rows of S as bf16 [hi | lo | zeros] (rows of
+    // other adapters load zeros) and whose B rows are the run's LoRA B rows,
+    // each read twice (column j of both the hi and the lo part). The loads of
+    // a run are then in flight while earlier stages multiply, instead of each
+    // run waiting for its own loads in the epilogue. Only the first K range
+    // adds the LoRA term.
+    static_assert(BM <= 64, "one lane per tile row");
+    int nruns = 0;
+    int row_ad[C::A_LD];
+#pragma unroll
+    for (int i = 0; i < C::A_LD; ++i) row_ad[i] = -1;
+    const bool pipe_expand = a.L > 0 && a.S_hl != nullptr && z == 0;
+    // lane l: the adapter of tile row l; starts: the first row of each run
+    // (wave-uniform)
+    const int adr = pipe_expand && lane < BM ? a.slot_adapter[row0 + lane] : -1;
+    uint64_t starts = 0;
+    if (pipe_expand) {
+        int prev = __shfl(adr, (lane + 63) & 63);
+        if (lane == 0) prev = -2;
+        starts = ballot64(adr >= 0 && adr != prev);
+        nruns = __popcll(starts);
+#pragma unroll
+        for (int i = 0; i < C::A_LD; ++i) row_ad[i] = __shfl(adr, ld_row + C::ROWS_PER_PASS * i);
+    }
+    // adapter of run q: the lane of the q-th set bit of starts
+    auto run_adapter = [&](int q) {
+        uint64_t m = starts;
+        for (int i = 0; i < q; ++i) m &= m - 1;
+        return __builtin_amdgcn_readlane(adr, __ffsll(static_cast<long long>(m)) - 1);
+    };
+    const int spr = pipe_expand ? a.s_hl_stride / 64 : 0;  // stages per run
+    const int nk_all = nk + nruns * spr;
     auto gload = [&](int set, int kt) {
-        const int k0 = kt * 64;
+        if (kt < nk) {
+            const int k0 = kt * 64;
 #pragma unroll
-        for (int i = 0; i < C::A_LD; ++i) ra[set][i] = ld16(asrc[i] + k0);
+            for (int i = 0; i < C::A_LD; ++i) ra[set][i] = ld16(asrc[i] + k0);
 #pragma unroll
-        for (int i = 0; i < C::B_LD; ++i) rb[set][i] = ld16(bsrc[i] + k0);
+            for (int i = 0; i < C::B_LD; ++i) rb[set][i] = ld16(bsrc[i] + k0);
+            return;
+        }
+        const int t = kt - nk, q = t / spr, sub = t - q * spr;
+        const int ad = run_adapter(q);
+        const int col = sub * 64 + ld_chunk * 8;
+#pragma unroll
+        for (int i = 0; i < C::A_LD; ++i)
+            ra[set][i] = row_ad[i] == ad
+                             ? ld16(a.S_hl + static_cast<size_t>(row0 + ld_row + C::ROWS_PER_PASS * i) * a.s_hl_stride + col)
+                             : u32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int i = 0; i < C::B_LD; ++i)
+            rb[set][i] = ld16(a.Bl + (static_cast<size_t>(ad * a.E + e) * Nw + wrow_of(ld_row + C::ROWS_PER_PASS * i)) * a.r +
+                              (col & (a.r - 1)));
     };
     auto lstore = [&](int buf, int set) {
 #pragma unroll
@@ -797,26 +848,26 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_tiled(GemmArgs a) {
     // compiler keeps exact wait counts across the unrolled loop.
     gload(0, 0);
     lstore(0, 0);
-    gload(1, min(1, nk - 1));
+    gload(1, min(1, nk_all - 1));
     __syncthreads();
     int kt = 0;
-    for (; kt + 1 < nk; kt += 2) {
-        gload(0, min(kt + 2, nk - 1));
+    for (; kt + 1 < nk_all; kt += 2) {
+        gload(0, min(kt + 2, nk_all - 1));
         __builtin_amdgcn_sched_barrier(0);
         compute(0);
         __builtin_amdgcn_sched_barrier(0);
         lstore(1, 1);
         __syncthreads();
-        gload(1, min(kt + 3, nk - 1));
+        gload(1, min(kt + 3, nk_all - 1));
         __builtin_amdgcn_sched_barrier(0);
         compute(1);
         __builtin_amdgcn_sched_barrier(0);
         lstore(0, 0);
         __syncthreads();
     }
-    if (nk & 1) compute(0);
+    if (nk_all & 1) compute(0);
 
-    tile_epilogue<FM, FN, GATEUP>(a, acc, wlive, wrow_base, wn, c0, e, kc, lrow, wrow_of, z);
+    tile_epilogue<FM, FN, GATEUP>(a, acc, wlive, wrow_base, wn, c0, e, kc, lrow, wrow_of, z, !pipe_expand);
 }
 
 // ===========================================================================
@@ -898,9 +949,8 @@ __device__ __forceinline__ void dma_step(const DmaCtx<FM, FN, A_PW, B_PW>& c, f3
     }
 }
 
-// adapter runs per tile that the direct-load kernel expands inside its
-// pipeline, and the zero row its LoRA stages read for rows outside a run
-constexpr int kMaxPipeRuns = 4;
+// the zero row that the direct-load kernel's LoRA stages read for rows
+// outside the run being expanded
 __device__ __attribute__((aligned(128))) uint16_t g_zero_row[64] = {};
 
 template <int BM, int BNT, int WM, int WN, int NS, bool GATEUP>
@@ -976,60 +1026,64 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_dma(GemmArgs a) {
     const int nk = K / 64;
 
     // LoRA expand as extra pipeline stages. The tile's rows hold one expert
-    // and are ordered by adapter, so the adapters form runs. For each run
-    // (up to kMaxPipeRuns) the pipeline appends s_hl_stride / 64 stages whose
-    // A rows are the run's rows of S as bf16 [hi | lo | zeros] (other rows
-    // read a zero row) and whose B rows are the run's LoRA B rows, each read
-    // twice (once against hi, once against lo): the same MFMAs as the
-    // epilogue expand, now fed through LDS with their loads in flight while
-    // earlier stages multiply. Tiles with more runs use the epilogue.
-    int nruns = 0, run0 = 0, run1 = 0, run2 = 0, run3 = 0;
+    // and are ordered by adapter, so the adapters form runs. For each run the
+    // pipeline appends s_hl_stride / 64 stages whose A rows are the run's
+    // rows of S as bf16 [hi | lo | zeros] (other rows read a zero row) and
+    // whose B rows are the run's LoRA B rows, each read twice (once against
+    // hi, once against lo): the same MFMAs as the epilogue expand, now fed
+    // through LDS with their loads in flight while earlier stages multiply.
+    constexpr int RPL = BM / 64;  // tile rows per lane
+    int nruns = 0;
     bool pipe_expand = false;
     int row_ad[A_PW];
 #pragma unroll
     for (int i = 0; i < A_PW; ++i) row_ad[i] = -1;
+    int adq[RPL];            // lane l: adapter of tile row 64 q + l
+    uint64_t starts[RPL];    // first rows of the runs (wave-uniform)
+#pragma unroll
+    for (int q = 0; q < RPL; ++q) {
+        adq[q] = -1;
+        starts[q] = 0;
+    }
     if (a.L > 0 && a.S_hl != nullptr) {
-        constexpr int RPL = BM / 64;  // tile rows per lane
-        int adq[RPL];
+        pipe_expand = true;
 #pragma unroll
         for (int q = 0; q < RPL; ++q) adq[q] = a.slot_adapter[row0 + 64 * q + lane];
-        uint64_t starts[RPL];
-        int total = 0;
 #pragma unroll
         for (int q = 0; q < RPL; ++q) {
             int prev = __shfl(adq[q], (lane + 63) & 63);
             const int carry = q > 0 ? __shfl(adq[q > 0 ? q - 1 : 0], 63) : -2;
             if (lane == 0) prev = carry;
             starts[q] = ballot64(adq[q] >= 0 && adq[q] != prev);
-            total += __popcll(starts[q]);
+            nruns += __popcll(starts[q]);
         }
-        if (total <= kMaxPipeRuns) {
-            pipe_expand = true;
 #pragma unroll
-            for (int q = 0; q < RPL; ++q) {
-                uint64_t m = starts[q];
-                while (m) {
-                    const int v = __shfl(adq[q], __ffsll(static_cast<long long>(m)) - 1);
-                    if (nruns == 0) run0 = v;
-                    else if (nruns == 1) run1 = v;
-                    else if (nruns == 2) run2 = v;
-                    else run3 = v;
-                    ++nruns;
-                    m &= m - 1;
-                }
-            }
+        for (int i = 0; i < A_PW; ++i) {
+            const int r = 8 * (wave * A_PW + i) + lr;  // 8 rows of one 64-row group
+            const int qi = (8 * (wave * A_PW + i)) / 64;
+            int v = adq[0];
 #pragma unroll
-            for (int i = 0; i < A_PW; ++i) {
-                const int r = 8 * (wave * A_PW + i) + lr;  // 8 rows of one 64-row group
-                const int qi = (8 * (wave * A_PW + i)) / 64;
-                int v = adq[0];
-#pragma unroll
-                for (int q = 1; q < RPL; ++q)
-                    if (q == qi) v = adq[q];
-                row_ad[i] = __shfl(v, r & 63);
-            }
+            for (int q = 1; q < RPL; ++q)
+                if (q == qi) v = adq[q];
+            row_ad[i] = __shfl(v, r & 63);
         }
     }
+    // adapter of run n: the row of the n-th run start, counted over the
+    // 64-row groups in order
+    auto run_adapter = [&](int n) {
+        int ad = -1;
+#pragma unroll
+        for (int q = 0; q < RPL; ++q) {
+            const int c = __popcll(starts[q]);
+            if (ad < 0 && n < c) {
+                uint64_t m = starts[q];
+                for (int i = 0; i < n; ++i) m &= m - 1;
+                ad = __builtin_amdgcn_readlane(adq[q], __ffsll(static_cast<long long>(m)) - 1);
+            }
+            n -= c;
+        }
+        return ad;
+    };
     const int spr = pipe_expand ? a.s_hl_stride / 64 : 0;  // stages per run
     const int nk_all = nk + nruns * spr;
     auto issue = [&](int stage, uint16_t* ab, uint16_t* bb) {
@@ -1038,7 +1092,7 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_dma(GemmArgs a) {
             return;
         }
         const int t = stage - nk, q = t / spr, sub = t - q * spr;
-        const int ad = q == 0 ? run0 : q == 1 ? run1 : q == 2 ? run2 : run3;
+        const int ad = run_adapter(q);
 #pragma unroll
         for (int i = 0; i < A_PW; ++i) {
             const int r = 8 * (wave * A_PW + i) + lr;

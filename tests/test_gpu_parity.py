@@ -326,13 +326,15 @@ def test_fused_combine_with_down_k_split(dev, bm):
 
 @pytest.mark.parametrize("r,L,bm,pure", [(8, 3, 128, False), (64, 3, 128, True), (128, 2, 256, False),
                                           (32, 4, 128, False), (128, 4, 128, True),
-                                          (32, 6, 128, False), (16, 7, 256, True)])
+                                          (32, 6, 128, False), (16, 7, 256, True),
+                                          (64, 24, 128, True), (8, 40, 256, False), (32, 20, 64, True),
+                                          (16, 33, 32, False)])
 def test_pipeline_expand(dev, r, L, bm, pure):
     # 128- and 256-row blocks run the LoRA expand as extra stages of their
-    # LDS pipeline when a tile holds at most 4 adapter runs (L <= 4 here,
-    # L = 4 reaching the limit) and in the epilogue otherwise (L = 6, 7:
-    # tiles with more runs); pure: base weights zero, so the output is the
-    # LoRA path alone
+    # LDS pipeline, one group of stages per adapter run of the tile (L up to
+    # 7 runs here; the epilogue expand is left to split shrinks, see the
+    # split-field cases); pure: base weights zero, so the output is the LoRA
+    # path alone
     log(f"pipeline expand r={r} L={L} bm={bm} pure={pure}")
     dims = dict(T=300, H=128, I=192, E=2, top_k=1, L=L, r=r)
     case = build_case(f"pipe{r}_{L}", dims=dims, seed=60 + r + L)

@@ -44,9 +44,14 @@ int default_bm_base(int P, int E) {
     }
     const long avg = (P + E - 1) / E;  // mean rows per expert
     if (avg <= 8) return 16;    // weight streaming: one 16-row block per expert
-    if (avg <= 16) return 32;
-    if (avg <= 96) return 64;   // still HBM-bound: register-staged 64-row tiles
-    return 128;                 // MFMA-bound: direct-to-LDS 128 x 192 tiles
+    // 64-row register-staged tiles: the skewed wide-expert layer (16 rows
+    // per expert on average, up to ~50) measured 505 us against 516 us with
+    // 32-row tiles
+    if (avg <= 16) return 64;
+    // direct-to-LDS 128 x 192 tiles: at 64 rows per expert (many-adapter
+    // layer) one block per expert streams its weights once: 629 us against
+    // 753 us with 64-row blocks, which split most experts in two
+    return 128;
 }
 
 // LoRA view blocks of 16 rows measured fastest for every configuration tried

@@ -74,7 +74,6 @@ int check_desc(const moe_lora_desc* d) {
     if (d->block_m_lora != 0 && !pow2_in(d->block_m_lora, 16, 256)) return MOE_LORA_EINVAL;
     const long P = static_cast<long>(d->T) * d->top_k;
     if (P > (1L << 24)) return MOE_LORA_EINVAL;
-    if (static_cast<long>(d->E) * (d->L + 1) > 9712) return MOE_LORA_EINVAL;
     if (!align_fits(d->E, d->L)) return MOE_LORA_EINVAL;
     return MOE_LORA_OK;
 }
@@ -147,7 +146,7 @@ int make_plan(const moe_lora_desc* d, Plan* p) {
     p->off_slot = take(4 * P);
     p->off_lslot = take(4 * P);
     p->off_sad = take(4ul * p->C_b);
-    p->off_defer = take(4ul * align_defer_ints(p->E, p->L));
+    p->off_defer = take(4ul * align_defer_ints(p->P, p->E, p->L));
     const size_t sbytes = p->L > 0 ? 4ul * p->ssplit * p->C_b * p->r : 0;
     p->off_s1 = take(sbytes);
     p->off_s2 = take(sbytes);
@@ -275,7 +274,8 @@ int moe_lora_route(const moe_lora_desc* d, const float* logits, int32_t* ids, fl
 
 int moe_lora_align(const moe_lora_desc* d, const int32_t* topk_ids, const int32_t* adapter_ids,
                    int32_t* sorted_b, int32_t* blk_e_b, int32_t* n_b, int32_t* sorted_l,
-                   int32_t* blk_e_l, int32_t* blk_a_l, int32_t* n_l, void* stream) {
+                   int32_t* blk_e_l, int32_t* blk_a_l, int32_t* n_l, void* workspace, size_t ws_bytes,
+                   void* stream) {
     Plan p;
     const int rc = make_plan(d, &p);
     if (rc) return rc;
@@ -283,9 +283,19 @@ int moe_lora_align(const moe_lora_desc* d, const int32_t* topk_ids, const int32_
     if (!topk_ids || !adapter_ids || !sorted_b || !blk_e_b || !n_b || !sorted_l || !blk_e_l ||
         !blk_a_l || !n_l)
         return MOE_LORA_EINVAL;
+    // the alignment's scratch is the forward pass's (same region of a
+    // workspace of moe_lora_workspace_bytes)
+    int32_t* defer = nullptr;
+    if (workspace) {
+        if (reinterpret_cast<uintptr_t>(workspace) % kAlign) return MOE_LORA_EINVAL;
+        if (ws_bytes < p.total) return MOE_LORA_EWORKSPACE;
+        defer = at<int32_t>(workspace, p.off_defer);
+    } else if (!align_single_workgroup(p.P, p.E, p.L)) {
+        return MOE_LORA_EWORKSPACE;
+    }
     return launch_align(topk_ids, adapter_ids, p.T, p.k, p.E, p.L, p.bm_b, p.bm_l, p.C_b, p.C_l,
                         sorted_b, blk_e_b, n_b, sorted_l, blk_e_l, blk_a_l, n_l, nullptr,
-                        nullptr, nullptr, nullptr, static_cast<hipStream_t>(stream)) == hipSuccess
+                        nullptr, nullptr, defer, static_cast<hipStream_t>(stream)) == hipSuccess
                ? MOE_LORA_OK
                : MOE_LORA_EHIP;
 }

@@ -13,9 +13,12 @@ hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* ids, 
                         hipStream_t s, int32_t* zero_words = nullptr, int n_zero = 0,
                         float* zero_out = nullptr, int H = 0);
 
-// Whether the alignment kernel's LDS holds the key counts of E experts x
-// (L adapters + none) together with at least one histogram row.
+// Whether the alignment handles E experts x (L adapters + none) keys: in one
+// workgroup (its LDS holds the key counts with at least one histogram row),
+// or spread over several launches (up to 36864 keys).
 bool align_fits(int E, int L);
+// Whether P pairs take the one-workgroup path (which needs no workspace).
+bool align_single_workgroup(int P, int E, int L);
 
 hipError_t launch_align(const int32_t* topk_ids, const int32_t* adapter_ids, int T, int k,
                         int E, int L, int bm_b, int bm_l, int C_b, int C_l,
@@ -23,8 +26,10 @@ hipError_t launch_align(const int32_t* topk_ids, const int32_t* adapter_ids, int
                         int32_t* sorted_l, int32_t* blk_e_l, int32_t* blk_a_l, int32_t* n_l,
                         int32_t* slot_of_pair, int32_t* lslot_of_pair, int32_t* slot_adapter,
                         int32_t* defer, hipStream_t s);
-// ints of scratch the alignment may use to split its scatter off (0 = none)
-int align_defer_ints(int E, int L);
+// ints of workspace the alignment of P pairs may use: the one-workgroup path
+// to split its scatter off, the multi-launch path for its histograms and
+// segment starts (which it needs)
+int align_defer_ints(int P, int E, int L);
 
 // ---- LoRA shrink ----------------------------------------------------------
 // S[slot][j] = X[row] . A[a][e][j] for the real rows of each LoRA-view block.

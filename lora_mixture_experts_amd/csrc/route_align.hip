@@ -143,7 +143,6 @@ static void align_ranges(int P, int E, int L, int* nr, int* R) {
     *R = r;
 }
 
-bool align_fits(int E, int L) { return align_max_ranges(E, L) > 0; }
 
 __device__ __forceinline__ uint64_t match_key(int key, bool valid, int nbits) {
     uint64_t m = ballot64(valid);
@@ -400,10 +399,173 @@ __global__ __launch_bounds__(64) void k_align_scatter(AlignKeys keyf, AlignOut o
     scatter_range(keyf, o, r * R, min(P, (r + 1) * R), h, bpos, lpos, L, nbits);
 }
 
-int align_defer_ints(int E, int L) {
-    const int maxr = align_max_ranges(E, L);
+// ---------------------------------------------------------------------------
+// Alignment for key counts beyond one workgroup's histogram rows (E (L+1) up
+// to kAlignMaxKeys, e.g. 256 experts x 128 adapters): the same counting sort,
+// spread over four launches so that no single workgroup holds more than one
+// int per key in LDS.
+//   1. k_align_hist: workgroup r counts the keys of pair range r in LDS and
+//      writes its row H[r][key] to the workspace.
+//   2. k_align_colscan: one thread per key turns its column of H into
+//      exclusive per-range offsets (in place) and the key's total cnt[key].
+//   3. k_align_offsets: one workgroup derives the expert totals, both views'
+//      segment starts (bpos, lpos: block scans in LDS, one array at a time),
+//      the padding sentinels, the tails and the block maps (each expert /
+//      segment writes its own blocks, so no search is needed).
+//   4. k_align_scatter_g: workgroup r (one wave) scatters range r as in the
+//      one-workgroup path, with its running offsets in LDS and the segment
+//      starts read from the workspace.
+// The result is the same as the one-workgroup path's, bit for bit.
+constexpr int kAlignMaxKeys = 36864;   // an int per key in a workgroup's LDS (+ E ints)
+constexpr int kAlignMultiMaxRanges = 64;
+
+bool align_fits(int E, int L) {
+    return align_max_ranges(E, L) > 0 || static_cast<long>(E) * (L + 1) <= kAlignMaxKeys;
+}
+
+// batches of at least this many pairs take the multi-launch path too
+constexpr int kAlignMultiMinPairs = 1 << 30;
+
+static bool align_multi(int P, int E, int L) { return align_max_ranges(E, L) <= 0 || P >= kAlignMultiMinPairs; }
+bool align_single_workgroup(int P, int E, int L) { return !align_multi(P, E, L); }
+
+// ranges of the multi-workgroup path: at least 256 pairs each, at most 64
+static void align_multi_ranges(int P, int* nr, int* R) {
+    int n = std::min(kAlignMultiMaxRanges, std::max(1, (P + 255) / 256));
+    int r = (P + n - 1) / n;
+    r = std::max(64, (r + 63) / 64 * 64);
+    *nr = std::max(1, (P + r - 1) / r);
+    *R = r;
+}
+
+__global__ __launch_bounds__(256) void k_align_hist(AlignKeys keyf, int P, int R, int nkeys,
+                                                    int32_t* __restrict__ H) {
+    extern __shared__ int hl[];
+    const int r = blockIdx.x, tid = threadIdx.x;
+    for (int i = tid; i < nkeys; i += 256) hl[i] = 0;
+    __syncthreads();
+    const int lo = r * R, hi = min(P, lo + R);
+    for (int p = lo + tid; p < hi; p += 256) atomicAdd(&hl[keyf(p)], 1);  // order-free: counts only
+    __syncthreads();
+    int32_t* row = H + static_cast<size_t>(r) * nkeys;
+    for (int i = tid; i < nkeys; i += 256) row[i] = hl[i];
+}
+
+__global__ __launch_bounds__(256) void k_align_colscan(int32_t* __restrict__ H, int nr, int nkeys,
+                                                       int32_t* __restrict__ cnt) {
+    const int key = blockIdx.x * 256 + threadIdx.x;
+    if (key >= nkeys) return;
+    int run = 0;
+    for (int r0 = 0; r0 < nr; r0 += 8) {
+        int c[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) c[u] = r0 + u < nr ? H[static_cast<size_t>(r0 + u) * nkeys + key] : 0;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            if (r0 + u < nr) H[static_cast<size_t>(r0 + u) * nkeys + key] = run;
+            run += c[u];
+        }
+    }
+    cnt[key] = run;
+}
+
+__global__ __launch_bounds__(kAlignThreads) void k_align_offsets(
+    int E, int L, int P, int bm_b_log2, int bm_l_log2, int C_b, int C_l, const int32_t* __restrict__ cnt,
+    int32_t* __restrict__ bpos, int32_t* __restrict__ lpos, AlignOut o, int32_t* __restrict__ blk_e_b,
+    int32_t* __restrict__ n_b_out, int32_t* __restrict__ blk_e_l, int32_t* __restrict__ blk_a_l,
+    int32_t* __restrict__ n_l_out) {
+    extern __shared__ int lds[];
+    const int L1 = L + 1, nkeys = E * L1, nseg = E * L;
+    const int bm_b = 1 << bm_b_log2, bm_l = 1 << bm_l_log2;
+    int* buf = lds;           // [nkeys] scan buffer: base view, then LoRA view
+    int* ne = buf + nkeys;    // [E] pairs per expert
+    int* red = ne + E;        // [65]
+    const int tid = threadIdx.x;
+    for (int e = tid; e < E; e += kAlignThreads) ne[e] = 0;
+    __syncthreads();
+    for (int key = tid; key < nkeys; key += kAlignThreads) {
+        const int c = cnt[key];
+        if (c) atomicAdd(&ne[key / L1], c);
+    }
+    __syncthreads();
+
+    // base view: keys in (expert, adapter') order, each expert padded after
+    // its last key; expert e's blocks start at its first key
+    for (int key = tid; key < nkeys; key += kAlignThreads) {
+        const int e = key / L1;
+        buf[key] = cnt[key] + (key % L1 == L ? ((ne[e] + bm_b - 1) & ~(bm_b - 1)) - ne[e] : 0);
+    }
+    __syncthreads();
+    const int n_b = block_excl_scan(buf, nkeys, red);
+    for (int key = tid; key < nkeys; key += kAlignThreads) bpos[key] = buf[key];
+    for (int e = tid; e < E; e += kAlignThreads) {
+        const int last = e * L1 + L;
+        const int base = buf[last] + cnt[last];
+        const int np = ((ne[e] + bm_b - 1) & ~(bm_b - 1)) - ne[e];
+        for (int i = 0; i < np; ++i) {
+            o.sorted_b[base + i] = P;
+            if (o.slot_adapter) o.slot_adapter[base + i] = -1;
+        }
+        const int b0 = buf[e * L1] >> bm_b_log2, nb = (ne[e] + bm_b - 1) >> bm_b_log2;
+        for (int i = 0; i < nb; ++i) blk_e_b[b0 + i] = e;
+    }
+    for (int i = n_b + tid; i < C_b; i += kAlignThreads) {
+        o.sorted_b[i] = P;
+        if (o.slot_adapter) o.slot_adapter[i] = -1;
+    }
+    for (int i = (n_b >> bm_b_log2) + tid; i < (C_b >> bm_b_log2); i += kAlignThreads) blk_e_b[i] = -1;
+    __syncthreads();  // buf is reused
+
+    // LoRA view: segments (expert, adapter < L), each padded to bm_l
+    for (int sg = tid; sg < nseg; sg += kAlignThreads)
+        buf[sg] = (cnt[(sg / L) * L1 + sg % L] + bm_l - 1) & ~(bm_l - 1);
+    __syncthreads();
+    const int n_l = block_excl_scan(buf, nseg, red);
+    for (int sg = tid; sg < nseg; sg += kAlignThreads) {
+        lpos[sg] = buf[sg];
+        const int c = cnt[(sg / L) * L1 + sg % L];
+        const int np = ((c + bm_l - 1) & ~(bm_l - 1)) - c;
+        for (int i = 0; i < np; ++i) o.sorted_l[buf[sg] + c + i] = P;
+        const int b0 = buf[sg] >> bm_l_log2, nb = (c + bm_l - 1) >> bm_l_log2;
+        for (int i = 0; i < nb; ++i) {
+            blk_e_l[b0 + i] = sg / L;
+            blk_a_l[b0 + i] = sg % L;
+        }
+    }
+    for (int i = n_l + tid; i < C_l; i += kAlignThreads) o.sorted_l[i] = P;
+    for (int i = (n_l >> bm_l_log2) + tid; i < (C_l >> bm_l_log2); i += kAlignThreads) {
+        blk_e_l[i] = -1;
+        blk_a_l[i] = -1;
+    }
+    if (tid == 0) {
+        *n_b_out = n_b;
+        *n_l_out = n_l;
+    }
+}
+
+__global__ __launch_bounds__(64) void k_align_scatter_g(AlignKeys keyf, AlignOut o, int P, int R,
+                                                        const int32_t* __restrict__ H,
+                                                        const int32_t* __restrict__ bpos,
+                                                        const int32_t* __restrict__ lpos) {
+    extern __shared__ int hr[];  // [nkeys] running offsets of this range
+    const int nkeys = keyf.E * (keyf.L + 1);
+    const int r = blockIdx.x, lane = threadIdx.x;
+    for (int i = lane; i < nkeys; i += 64) hr[i] = H[static_cast<size_t>(r) * nkeys + i];
+    __syncthreads();
+    const int nbits = nkeys > 1 ? 32 - __clz(nkeys - 1) : 0;
+    scatter_range(keyf, o, r * R, min(P, (r + 1) * R), hr, bpos, lpos, keyf.L, nbits);
+}
+
+int align_defer_ints(int P, int E, int L) {
     const int nkeys = E * (L + 1);
-    return maxr > 0 ? (maxr + 1) * nkeys + E * L : 0;
+    if (!align_multi(P, E, L)) {
+        const int maxr = align_max_ranges(E, L);
+        return (maxr + 1) * nkeys + E * L;
+    }
+    int nr, R;
+    align_multi_ranges(std::max(P, 1), &nr, &R);
+    // H [nr][nkeys], cnt [nkeys], bpos [nkeys], lpos [E L]
+    return nr * nkeys + 2 * nkeys + E * L;
 }
 
 hipError_t launch_align(const int32_t* topk_ids, const int32_t* adapter_ids, int T, int k,
@@ -412,14 +574,46 @@ hipError_t launch_align(const int32_t* topk_ids, const int32_t* adapter_ids, int
                         int32_t* sorted_l, int32_t* blk_e_l, int32_t* blk_a_l, int32_t* n_l,
                         int32_t* slot_of_pair, int32_t* lslot_of_pair, int32_t* slot_adapter,
                         int32_t* defer, hipStream_t s) {
-    if (align_max_ranges(E, L) <= 0) return hipErrorInvalidValue;
+    if (!align_fits(E, L)) return hipErrorInvalidValue;
     if ((bm_b & (bm_b - 1)) || (bm_l & (bm_l - 1))) return hipErrorInvalidValue;
     const int P = T * k;
     if (P == 0) return hipSuccess;
-    int nr, R;
-    align_ranges(P, E, L, &nr, &R);
     const AlignKeys keyf{topk_ids, adapter_ids, k, E, L};
     const AlignOut o{sorted_b, sorted_l, slot_of_pair, lslot_of_pair, slot_adapter};
+    if (align_multi(P, E, L)) {
+        if (!defer) return hipErrorInvalidValue;  // the multi-workgroup path needs its workspace
+        int nr, R;
+        align_multi_ranges(P, &nr, &R);
+        const int nkeys = E * (L + 1);
+        int32_t* H = defer;
+        int32_t* cnt = H + static_cast<size_t>(nr) * nkeys;
+        int32_t* bpos = cnt + nkeys;
+        int32_t* lpos = bpos + nkeys;
+        const size_t lds_keys = sizeof(int) * nkeys;
+        const size_t lds_off = sizeof(int) * (nkeys + E + 65);
+        // dynamic LDS beyond 64 KiB is opted into per kernel (once)
+        static bool lds_raised = false;
+        if (!lds_raised) {
+            constexpr int kMaxDyn = 160 * 1024;
+            if (hipFuncSetAttribute(reinterpret_cast<const void*>(k_align_hist),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, kMaxDyn) != hipSuccess ||
+                hipFuncSetAttribute(reinterpret_cast<const void*>(k_align_offsets),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, kMaxDyn) != hipSuccess ||
+                hipFuncSetAttribute(reinterpret_cast<const void*>(k_align_scatter_g),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, kMaxDyn) != hipSuccess)
+                return hipErrorInvalidValue;
+            lds_raised = true;
+        }
+        hipLaunchKernelGGL(k_align_hist, dim3(nr), dim3(256), lds_keys, s, keyf, P, R, nkeys, H);
+        hipLaunchKernelGGL(k_align_colscan, dim3((nkeys + 255) / 256), dim3(256), 0, s, H, nr, nkeys, cnt);
+        hipLaunchKernelGGL(k_align_offsets, dim3(1), dim3(kAlignThreads), lds_off, s, E,
+                           L, P, __builtin_ctz(bm_b), __builtin_ctz(bm_l), C_b, C_l, cnt, bpos, lpos, o, blk_e_b,
+                           n_b, blk_e_l, blk_a_l, n_l);
+        hipLaunchKernelGGL(k_align_scatter_g, dim3(nr), dim3(64), lds_keys, s, keyf, o, P, R, H, bpos, lpos);
+        return hipGetLastError();
+    }
+    int nr, R;
+    align_ranges(P, E, L, &nr, &R);
     // one workgroup does everything for small batches; large ones hand the
     // scattered stores to one workgroup per range
     const size_t scatter_lds = sizeof(int) * (2 * E * (L + 1) + E * L);

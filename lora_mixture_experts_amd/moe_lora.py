@@ -69,7 +69,7 @@ def lib():
             "moe_lora_workspace_bytes": ([pD, pSZ], ctypes.c_int),
             "moe_lora_align_capacity": ([pD, pI32, pI32], ctypes.c_int),
             "moe_lora_route": ([pD, P, P, P, P], ctypes.c_int),
-            "moe_lora_align": ([pD, P, P, P, P, P, P, P, P, P, P], ctypes.c_int),
+            "moe_lora_align": ([pD] + [P] * 9 + [P, SZ, P], ctypes.c_int),
             "moe_lora_forward": ([pD, pW, P, P, P, P, P, SZ, P], ctypes.c_int),
             "moe_lora_forward_noalloc": ([pD, pW, P, P, P, P, P], ctypes.c_int),
             "moe_lora_read_stages": ([pD, P, SZ, P, P, P, P, P, P, P], ctypes.c_int),
@@ -166,10 +166,14 @@ def route(desc, logits, topk_ids, topk_w, stream=None):
 
 
 def align(desc, topk_ids, adapter_ids, sorted_b, blk_e_b, n_b, sorted_l, blk_e_l, blk_a_l, n_l,
-          stream=None):
+          workspace=None, stream=None):
+    """workspace: a uint8 device tensor of >= workspace_bytes(desc) bytes, or
+    None (accepted up to E*(L+1) = 9712 keys)."""
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().moe_lora_align(ctypes.byref(desc), _ptr(topk_ids), _ptr(adapter_ids),
                                 _ptr(sorted_b), _ptr(blk_e_b), _ptr(n_b), _ptr(sorted_l),
-                                _ptr(blk_e_l), _ptr(blk_a_l), _ptr(n_l), _stream(stream)), "align")
+                                _ptr(blk_e_l), _ptr(blk_a_l), _ptr(n_l), _ptr(workspace),
+                                ctypes.c_size_t(ws_bytes), _stream(stream)), "align")
 
 
 def weights_struct(w_gate_up, w_down, a_gate_up=None, b_gate_up=None, a_down=None, b_down=None):

@@ -42,7 +42,7 @@ def desc(**over):
 @pytest.mark.parametrize("over", [dict(H=2881), dict(I=100), dict(top_k=0), dict(top_k=33, E=40),
                                   dict(top_k=5, E=4), dict(r=24), dict(E=0), dict(T=-1), dict(L=-1),
                                   dict(bm_b=48), dict(bm_b=8), dict(bm_l=512), dict(E=1025),
-                                  dict(E=128, L=200), dict(E=1024, L=9, top_k=8), dict(flags=16), dict(flags=5),
+                                  dict(E=128, L=300), dict(E=1024, L=36, top_k=8), dict(flags=16), dict(flags=5),
                                   dict(flags=-1), dict(flags=31)])
 def test_validate_rejects(over):
     assert ml.validate(desc(**over)) == ml.EINVAL
@@ -76,10 +76,13 @@ def test_shrink_launch_flag_keeps_the_decode_workspace_size():
 
 
 def test_validate_key_limit_edge():
-    # E * (L + 1) = 9712 is the largest expert x adapter key count accepted
-    assert ml.validate(desc(E=972, L=9, top_k=8)) == ml.EINVAL  # 9720
-    assert ml.validate(desc(E=1024, L=8, top_k=8)) == ml.OK
-    assert ml.validate(desc(E=607, L=15, top_k=8)) == ml.OK  # 9712
+    # up to E * (L + 1) = 9712 keys one workgroup aligns; beyond, up to
+    # 36864, the multi-launch path does (e.g. 256 experts x 128 adapters)
+    assert ml.validate(desc(E=607, L=15, top_k=8)) == ml.OK     # 9712
+    assert ml.validate(desc(E=972, L=9, top_k=8)) == ml.OK      # 9720
+    assert ml.validate(desc(E=256, L=128, top_k=8)) == ml.OK    # 33024
+    assert ml.validate(desc(E=1024, L=35, top_k=8)) == ml.OK    # 36864
+    assert ml.validate(desc(E=1024, L=36, top_k=8)) == ml.EINVAL  # 37888
 
 
 def test_validate_checks_weight_pointers():

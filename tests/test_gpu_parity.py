@@ -114,7 +114,7 @@ def test_route_ties(dev):
         np.testing.assert_array_equal(ids.cpu().numpy(), ref_ids)
 
 
-def gpu_align(dev, ids, ad, dims, bm_b, bm_l):
+def gpu_align(dev, ids, ad, dims, bm_b, bm_l, workspace=True):
     d = ml.make_desc(dims["T"], dims["H"], dims["I"], dims["E"], dims["top_k"], dims["L"], dims["r"],
                      bm_b, bm_l)
     C_b, C_l = ml.align_capacity(d)
@@ -122,7 +122,8 @@ def gpu_align(dev, ids, ad, dims, bm_b, bm_l):
     z = lambda n: torch.full((n,), -7, dtype=torch.int32, device=dev)
     out = dict(sorted_b=z(C_b), blk_e_b=z(C_b // bb), n_b=z(1), sorted_l=z(C_l), blk_e_l=z(C_l // bl),
                blk_a_l=z(C_l // bl), n_l=z(1))
-    ml.align(d, torch.from_numpy(ids).to(dev), torch.from_numpy(ad).to(dev), **out)
+    ws = torch.full((ml.workspace_bytes(d),), 0xA5, dtype=torch.uint8, device=dev) if workspace else None
+    ml.align(d, torch.from_numpy(ids).to(dev), torch.from_numpy(ad).to(dev), workspace=ws, **out)
     torch.cuda.synchronize()
     return {k: v.cpu().numpy() for k, v in out.items()}, (bb, bl)
 
@@ -135,7 +136,13 @@ ALIGN_CASES = [("tiny", {}, (16, 16)), ("decode", {}, (16, 16)), ("decode", {}, 
                ("big", dict(T=20000, H=64, I=64, E=64, top_k=8, L=16, r=8), (256, 128)),
                # key counts near the limit: one histogram range, one wave scatters
                ("keys", dict(T=300, H=64, I=64, E=256, top_k=8, L=32, r=8), (16, 16)),
-               ("maxkeys", dict(T=4000, H=64, I=64, E=607, top_k=8, L=15, r=8), (32, 16))]
+               ("maxkeys", dict(T=4000, H=64, I=64, E=607, top_k=8, L=15, r=8), (32, 16)),
+               # beyond one workgroup's histogram rows: the multi-launch path
+               ("keys256", dict(T=2000, H=64, I=64, E=256, top_k=8, L=128, r=8), (16, 16)),
+               ("keys256b", dict(T=6400, H=64, I=64, E=256, top_k=8, L=128, r=8), (128, 64)),
+               ("keystop", dict(T=4000, H=64, I=64, E=1024, top_k=8, L=35, r=8), (32, 16)),
+               ("keysfew", dict(T=5, H=64, I=64, E=256, top_k=4, L=40, r=8), (16, 16)),
+               ("keys9720", dict(T=3000, H=64, I=64, E=972, top_k=8, L=9, r=8), (64, 32))]
 
 
 @pytest.mark.parametrize("name,dims,bm", ALIGN_CASES)
@@ -144,7 +151,7 @@ def test_align_parity(dev, name, dims, bm):
     dims = dims or wl.CONFIGS[name]
     logits, _, ad, _ = wl.routing_only(name, dims=dims)
     ids, _ = oracle.route(logits, dims["top_k"])
-    if name in ("odd", "big"):  # out-of-range adapter ids count as "none"
+    if name in ("odd", "big", "keys256b"):  # out-of-range adapter ids count as "none"
         ad = ad.copy()
         ad[::5] = dims["L"] + 3
         ad[1::7] = -9
@@ -156,6 +163,16 @@ def test_align_parity(dev, name, dims, bm):
     again, _ = gpu_align(dev, ids, ad, dims, *bm)
     for key in got:
         np.testing.assert_array_equal(again[key], got[key])
+    # without a workspace: the same result where one workgroup suffices,
+    # refused where the histograms need the workspace
+    if dims["E"] * (dims["L"] + 1) <= 9712:
+        nows, _ = gpu_align(dev, ids, ad, dims, *bm, workspace=False)
+        for key in got:
+            np.testing.assert_array_equal(nows[key], got[key])
+    else:
+        with pytest.raises(ml.MoeLoraError) as ei:
+            gpu_align(dev, ids, ad, dims, *bm, workspace=False)
+        assert ei.value.code == ml.EWORKSPACE
 
 
 # ----------------------------------------------------------------------------- the layer
@@ -490,6 +507,15 @@ def test_layer_shapes(dev, i):
     dims = RANDOM_DIMS[i]
     log(f"layer shape {dims}")
     case = build_case(f"shape{i}", dims=dims, seed=40 + i)
+    check_layer(case, dev, stages=True)
+
+
+def test_layer_many_experts_and_adapters(dev):
+    # 256 experts x 40 adapters (10496 keys): the alignment runs on the
+    # multi-launch path inside the forward pass
+    log("layer 256 experts x 40 adapters")
+    dims = dict(T=300, H=64, I=128, E=256, top_k=8, L=40, r=8)
+    case = build_case("keyslayer", dims=dims, seed=81)
     check_layer(case, dev, stages=True)
 
 

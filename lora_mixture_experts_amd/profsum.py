@@ -63,6 +63,8 @@ def label(kernel_name: str) -> str | None:
     if fn.startswith("k_gemm"):
         return "gemm_gate_up" if "true" in targs.split(", ") else "gemm_down"
     return {"k_route": "route", "k_align": "align", "k_align_scatter": "align_scatter",
+            "k_align_hist": "align_hist", "k_align_colscan": "align_colscan",
+            "k_align_offsets": "align_offsets", "k_align_scatter_g": "align_scatter",
             "k_shrink": "shrink", "k_combine": "combine", "k_gather_f32": "gather_f32",
             "k_gather_bf16": "gather_bf16"}.get(fn, fn)
 

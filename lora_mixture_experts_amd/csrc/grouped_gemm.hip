@@ -304,7 +304,7 @@ __device__ __forceinline__ void expand_own_shrink(const GemmArgs& a, int e, int 
     }
 }
 
-template <bool GATEUP, int FN, int NS, int KSW>
+template <bool GATEUP, int FN, int NS, int KSW, bool PAIR>
 __global__ __launch_bounds__(64 * KSW) void k_gemm_skinny(GemmArgs a) {
     const int w = KSW > 1 ? wave_id() : 0;
     // 1-D grid: producer workgroups first (one producer unit per wave), then
@@ -394,26 +394,77 @@ __global__ __launch_bounds__(64 * KSW) void k_gemm_skinny(GemmArgs a) {
     f32x4 acc_l[FN];
 #pragma unroll
     for (int f = 0; f < FN; ++f) acc_l[f] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // With PAIR, the rows' S chunk is read once per 32 of r (rows without an
+    // adapter read zeros) and each adapter run masks it to its own rows; runs
+    // are taken two at a time, so that the LoRA B loads of both are in flight
+    // together (8 adapters among 16 rows would otherwise be 8 dependent
+    // load-then-multiply rounds). It holds more registers (two waves per
+    // SIMD instead of three), so the launcher picks it only for grids that
+    // do not fill three waves per SIMD anyway.
     auto expand = [&](auto coherent, f32x4 (&dst)[FN]) {
-        bool pending = my_a >= 0;
-        while (true) {
-            const uint64_t m = ballot64(pending);
-            if (m == 0) break;
-            const int leader = __ffsll(static_cast<long long>(m)) - 1;
-            const int acur = __shfl(my_a, leader);
-            const bool in_run = pending && my_a == acur;
-            pending = pending && !in_run;
+        if constexpr (PAIR) {
             for (int kk = 0; kk < a.r; kk += 32) {
                 const int j0 = kk + g * 8;
-                u32x4 hi, lo, bb[FN];
+                u32x4 hi, lo;
+                load_s_hilo<decltype(coherent)::value>(a, slot, my_a >= 0, j0, hi, lo);
+                bool pending = my_a >= 0;
+                while (true) {
+                    uint64_t m = ballot64(pending);
+                    if (m == 0) break;
+                    const int a0 = __shfl(my_a, __ffsll(static_cast<long long>(m)) - 1);
+                    const bool in0 = pending && my_a == a0;
+                    pending = pending && !in0;
+                    m = ballot64(pending);
+                    const int a1 = m ? __shfl(my_a, __ffsll(static_cast<long long>(m)) - 1) : -1;
+                    const bool in1 = m != 0 && pending && my_a == a1;
+                    pending = pending && !in1;
+                    u32x4 b0[FN], b1[FN];
 #pragma unroll
-                for (int f = 0; f < FN; ++f)
-                    bb[f] = load_lora_b(a, Nw, acur, e, w_row_of_frag<GATEUP>(f, c0, I) + lrow, j0);
-                load_s_hilo<decltype(coherent)::value>(a, slot, in_run, j0, hi, lo);
+                    for (int f = 0; f < FN; ++f)
+                        b0[f] = load_lora_b(a, Nw, a0, e, w_row_of_frag<GATEUP>(f, c0, I) + lrow, j0);
+                    if (a1 >= 0) {
 #pragma unroll
-                for (int f = 0; f < FN; ++f) {
-                    dst[f] = mfma16x16x32(hi, bb[f], dst[f]);
-                    dst[f] = mfma16x16x32(lo, bb[f], dst[f]);
+                        for (int f = 0; f < FN; ++f)
+                            b1[f] = load_lora_b(a, Nw, a1, e, w_row_of_frag<GATEUP>(f, c0, I) + lrow, j0);
+                    }
+                    const u32x4 z{0, 0, 0, 0};
+                    const u32x4 h0 = in0 ? hi : z, l0 = in0 ? lo : z;
+#pragma unroll
+                    for (int f = 0; f < FN; ++f) {
+                        dst[f] = mfma16x16x32(h0, b0[f], dst[f]);
+                        dst[f] = mfma16x16x32(l0, b0[f], dst[f]);
+                    }
+                    if (a1 >= 0) {
+                        const u32x4 h1 = in1 ? hi : z, l1 = in1 ? lo : z;
+#pragma unroll
+                        for (int f = 0; f < FN; ++f) {
+                            dst[f] = mfma16x16x32(h1, b1[f], dst[f]);
+                            dst[f] = mfma16x16x32(l1, b1[f], dst[f]);
+                        }
+                    }
+                }
+            }
+        } else {
+            bool pending = my_a >= 0;
+            while (true) {
+                const uint64_t m = ballot64(pending);
+                if (m == 0) break;
+                const int leader = __ffsll(static_cast<long long>(m)) - 1;
+                const int acur = __shfl(my_a, leader);
+                const bool in_run = pending && my_a == acur;
+                pending = pending && !in_run;
+                for (int kk = 0; kk < a.r; kk += 32) {
+                    const int j0 = kk + g * 8;
+                    u32x4 hi, lo, bb[FN];
+#pragma unroll
+                    for (int f = 0; f < FN; ++f)
+                        bb[f] = load_lora_b(a, Nw, acur, e, w_row_of_frag<GATEUP>(f, c0, I) + lrow, j0);
+                    load_s_hilo<decltype(coherent)::value>(a, slot, in_run, j0, hi, lo);
+#pragma unroll
+                    for (int f = 0; f < FN; ++f) {
+                        dst[f] = mfma16x16x32(hi, bb[f], dst[f]);
+                        dst[f] = mfma16x16x32(lo, bb[f], dst[f]);
+                    }
                 }
             }
         }
@@ -1254,15 +1305,23 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
         const long total = static_cast<long>(a.N_out / cols) * a.n_blocks * a.ksplit + (a.prod_units + ksw - 1) / ksw;
         if (total > 0x7fffffffL) return hipErrorInvalidValue;
         const dim3 grid(static_cast<unsigned>(total)), block(64 * ksw);
+        // paired adapter runs where the grid holds at most two waves per SIMD
+        const bool pair = total * ksw <= 2L * kCus * 4;
+#define MOELORA_SKINNY(G, FN, NS, W)                                                                  \
+    do {                                                                                              \
+        if (pair) hipLaunchKernelGGL((k_gemm_skinny<G, FN, NS, W, true>), grid, block, 0, s, a);     \
+        else hipLaunchKernelGGL((k_gemm_skinny<G, FN, NS, W, false>), grid, block, 0, s, a);         \
+    } while (0)
         if (a.gate_up) {
-            if (ksw == 1) hipLaunchKernelGGL((k_gemm_skinny<true, kSkinnyFNGateUp, kSkinnyNSGateUp, 1>), grid, block, 0, s, a);
-            if (ksw == 2) hipLaunchKernelGGL((k_gemm_skinny<true, kSkinnyFNGateUp, kSkinnyNSGateUp, 2>), grid, block, 0, s, a);
-            if (ksw == 4) hipLaunchKernelGGL((k_gemm_skinny<true, kSkinnyFNGateUp, kSkinnyNSGateUp, 4>), grid, block, 0, s, a);
+            if (ksw == 1) MOELORA_SKINNY(true, kSkinnyFNGateUp, kSkinnyNSGateUp, 1);
+            if (ksw == 2) MOELORA_SKINNY(true, kSkinnyFNGateUp, kSkinnyNSGateUp, 2);
+            if (ksw == 4) MOELORA_SKINNY(true, kSkinnyFNGateUp, kSkinnyNSGateUp, 4);
         } else {
-            if (ksw == 1) hipLaunchKernelGGL((k_gemm_skinny<false, kSkinnyFNDown, kSkinnyNSDown, 1>), grid, block, 0, s, a);
-            if (ksw == 2) hipLaunchKernelGGL((k_gemm_skinny<false, kSkinnyFNDown, kSkinnyNSDown, 2>), grid, block, 0, s, a);
-            if (ksw == 4) hipLaunchKernelGGL((k_gemm_skinny<false, kSkinnyFNDown, kSkinnyNSDown, 4>), grid, block, 0, s, a);
+            if (ksw == 1) MOELORA_SKINNY(false, kSkinnyFNDown, kSkinnyNSDown, 1);
+            if (ksw == 2) MOELORA_SKINNY(false, kSkinnyFNDown, kSkinnyNSDown, 2);
+            if (ksw == 4) MOELORA_SKINNY(false, kSkinnyFNDown, kSkinnyNSDown, 4);
         }
+#undef MOELORA_SKINNY
         return hipGetLastError();
     }
     switch (a.bm_b) {

@@ -21,13 +21,20 @@ from lora_mixture_experts_amd import build as B
 # minimum waves per SIMD, by kernel name prefix (demangled form)
 MIN_OCCUPANCY = {
     # one wave per tile (the library's choice); the 2- and 4-wave variants
-    # are tuning options
-    "k_gemm_skinny<true, 4, 2, 1>": 3,
-    "k_gemm_skinny<false, 4, 2, 1>": 3,
-    "k_gemm_skinny<true, 4, 2, 2>": 2,
-    "k_gemm_skinny<true, 4, 2, 4>": 2,
-    "k_gemm_skinny<false, 4, 2, 2>": 2,
-    "k_gemm_skinny<false, 4, 2, 4>": 2,
+    # are tuning options; the paired-run variants (last argument true) run
+    # only grids of at most two waves per SIMD
+    "k_gemm_skinny<true, 4, 2, 1, false>": 3,
+    "k_gemm_skinny<false, 4, 2, 1, false>": 3,
+    "k_gemm_skinny<true, 4, 2, 2, false>": 2,
+    "k_gemm_skinny<true, 4, 2, 4, false>": 2,
+    "k_gemm_skinny<false, 4, 2, 2, false>": 2,
+    "k_gemm_skinny<false, 4, 2, 4, false>": 2,
+    "k_gemm_skinny<true, 4, 2, 1, true>": 2,
+    "k_gemm_skinny<false, 4, 2, 1, true>": 2,
+    "k_gemm_skinny<true, 4, 2, 2, true>": 2,
+    "k_gemm_skinny<true, 4, 2, 4, true>": 2,
+    "k_gemm_skinny<false, 4, 2, 2, true>": 2,
+    "k_gemm_skinny<false, 4, 2, 4, true>": 2,
     "k_gemm_tiled<32, 128, 1, 4, true>": 4,
     "k_gemm_tiled<32, 128, 1, 4, false>": 4,
     "k_gemm_tiled<64, 128, 2, 2, true>": 3,

@@ -61,7 +61,11 @@ def label(kernel_name: str) -> str | None:
         return None
     fn, targs = m.group(1), (m.group(2) or "")
     if fn.startswith("k_gemm"):
-        return "gemm_gate_up" if "true" in targs.split(", ") else "gemm_down"
+        # the projection flag: the first template argument of the 16-row
+        # kernel, the last one of the tiled and direct-load kernels
+        args = [t.strip() for t in targs.split(",")] if targs else []
+        flag = args[0] if fn == "k_gemm_skinny" and args else (args[-1] if args else "")
+        return "gemm_gate_up" if flag == "true" else "gemm_down"
     return {"k_route": "route", "k_align": "align", "k_align_scatter": "align_scatter",
             "k_align_hist": "align_hist", "k_align_colscan": "align_colscan",
             "k_align_offsets": "align_offsets", "k_align_scatter_g": "align_scatter",

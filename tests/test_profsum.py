@@ -9,6 +9,9 @@ def test_kernel_labels():
     assert profsum.label("void moelora::k_gemm_skinny<false, 4>(moelora::GemmArgs)") == "gemm_down"
     assert profsum.label("void moelora::k_gemm_dma<128, 192, 2, 2, 2, true>(moelora::GemmArgs)") == "gemm_gate_up"
     assert profsum.label("void moelora::k_gemm_tiled<64, 128, 2, 2, false>(moelora::GemmArgs)") == "gemm_down"
+    # the 16-row kernel's flag is its first argument, whatever follows it
+    assert profsum.label("void moelora::k_gemm_skinny<false, 4, 2, 1, true>(moelora::GemmArgs)") == "gemm_down"
+    assert profsum.label("void moelora::k_gemm_skinny<true, 4, 2, 2, false>(moelora::GemmArgs)") == "gemm_gate_up"
     assert profsum.label("void moelora::k_shrink<2>(moelora::ShrinkArgs)") == "shrink"
     assert profsum.label("__amd_rocclr_copyBuffer") is None
 

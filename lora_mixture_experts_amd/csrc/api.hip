@@ -54,10 +54,14 @@ int default_bm_base(int P, int E) {
     return 128;
 }
 
-// LoRA view blocks of 16 rows measured fastest for every configuration tried
-// (decode, prefill, many, wide): the shrink's 256-thread workgroups then hold
-// one fragment per K part, and padding per (expert, adapter) segment is least.
-int default_bm_lora() { return 16; }
+// LoRA view blocks: 64 rows once the (expert, adapter) segments average at
+// least 32 rows, so that each block's shrink reads its LoRA A once for four
+// 16-row fragments (prefill-shaped layer: both shrinks 134 -> 93 us); 16 rows
+// otherwise, where the padding of each segment would cost more (decode,
+// many-adapter and wide-expert layers).
+int default_bm_lora(int P, int E, int L) {
+    return L > 0 && static_cast<long>(P) >= 32L * E * L ? 64 : 16;
+}
 
 int check_desc(const moe_lora_desc* d) {
     if (!d) return MOE_LORA_EINVAL;
@@ -85,7 +89,7 @@ int make_plan(const moe_lora_desc* d, Plan* p) {
     p->r = d->L > 0 ? d->r : 8;
     p->P = d->T * d->top_k;
     p->bm_b = d->block_m_base ? d->block_m_base : default_bm_base(p->P, p->E);
-    p->bm_l = d->block_m_lora ? d->block_m_lora : default_bm_lora();
+    p->bm_l = d->block_m_lora ? d->block_m_lora : default_bm_lora(p->P, p->E, p->L);
     if (!gemm_supported(p->I, p->H, 1, p->bm_b) || !gemm_supported(p->H, p->I, 0, p->bm_b))
         return MOE_LORA_EINVAL;
     const long P = p->P;

@@ -22,7 +22,13 @@ namespace moelora {
 constexpr int kShrinkThreads = 256;
 constexpr int kShrinkWaves = kShrinkThreads / 64;
 
+// At most this many 16-row fragments are multiplied together against one
+// load of a wave's LoRA A chunk (bounded by the registers the accumulators
+// and operand buffers take); the launcher takes min(fragments per block, it).
 template <int FN>
+constexpr int shrink_group() { return FN <= 2 ? 4 : 8 / FN; }
+
+template <int FN, int G>
 __global__ __launch_bounds__(kShrinkThreads) void k_shrink(ShrinkArgs a) {
     const int b = blockIdx.x;
     const int e = a.blk_e_l[b];
@@ -30,16 +36,13 @@ __global__ __launch_bounds__(kShrinkThreads) void k_shrink(ShrinkArgs a) {
     const int ad = a.blk_a_l[b];
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int kc = lane >> 4, lrow = lane & 15;
-    const int nfm = a.bm_l / 16;                         // 16-row fragments in the block (1..16)
-    const int nkp = nfm >= kShrinkWaves ? 1 : kShrinkWaves / nfm;  // K parts per fragment
-    const int fstride = kShrinkWaves / nkp;              // fragments in flight per round
-    const int kp = wave % nkp;
+    const int nfm = a.bm_l / 16;  // 16-row fragments in the block (1..16)
     // K in chunks of 64; this workgroup owns chunks [z0, z1) (its K range)
-    // and this wave [q0, q1) of them
+    // and wave w the w-th quarter [q0, q1) of them, for every fragment
     const int nqa = a.K / 64, z = blockIdx.y;
     const int z0 = z * nqa / a.ksplit, z1 = (z + 1) * nqa / a.ksplit;
     const int nq = z1 - z0;
-    const int q0 = z0 + kp * nq / nkp, q1 = z0 + (kp + 1) * nq / nkp;
+    const int q0 = z0 + wave * nq / kShrinkWaves, q1 = z0 + (wave + 1) * nq / kShrinkWaves;
 
     // B operand rows (LoRA A rows j = fn*16 + lrow); columns j >= r (r = 8)
     // re-read row j - 8 and are never stored, so loads stay unconditional
@@ -51,45 +54,62 @@ __global__ __launch_bounds__(kShrinkThreads) void k_shrink(ShrinkArgs a) {
         brow[fn] = Abase + static_cast<size_t>(j < a.r ? j : j - 8) * a.K + kc * 16;
     }
     const int p_first = a.sorted_l[b * a.bm_l];
-    __shared__ f32x4 red[kShrinkWaves][FN][64];
+    __shared__ f32x4 red[kShrinkWaves][G][FN][64];
 
-    // rounds of fstride fragments (every wave runs the same number of rounds,
-    // so the barriers below match)
-    for (int fm = wave / nkp; fm < nfm; fm += fstride) {
-        // A operand row (block row fm*16 + lrow); padding rows re-read the
+    // groups of G fragments: each K chunk of A is loaded once per wave and
+    // multiplied against the chunk of every fragment of the group
+    for (int fg = 0; fg < nfm; fg += G) {
+        // A operand rows (block row fm*16 + lrow); padding rows re-read the
         // block's first (real) row, merging into the same memory requests, and
         // their outputs are never stored. Lane (lrow, kc) reads 32 contiguous
         // bytes (elements 16 kc .. 16 kc + 15) of each 64-wide chunk, so a pair
-        // of wave-wide loads consumes whole 128-byte lines.
-        int p = a.sorted_l[b * a.bm_l + fm * 16 + lrow];
-        if (p >= a.P) p = p_first;
-        const size_t row = a.gather_token ? static_cast<size_t>(p / a.top_k)
-                                          : static_cast<size_t>(a.slot_of_pair[p]);
-        const uint16_t* xrow = a.X + row * a.K + kc * 16;
-
-        f32x4 acc[FN];
+        // of wave-wide loads consumes whole 128-byte lines. Fragments made
+        // only of padding (or past the block) are skipped (uniform per wave).
+        const uint16_t* xrow[G];
+        bool live[G];
 #pragma unroll
-        for (int fn = 0; fn < FN; ++fn) acc[fn] = f32x4{0.f, 0.f, 0.f, 0.f};
-        u32x4 xb[2][2], wb[2][FN][2];
+        for (int g = 0; g < G; ++g) {
+            const int fm = fg + g;
+            live[g] = fm < nfm && a.sorted_l[b * a.bm_l + min(fm, nfm - 1) * 16] < a.P;
+            int p = a.sorted_l[b * a.bm_l + min(fm, nfm - 1) * 16 + lrow];
+            if (p >= a.P) p = p_first;
+            const size_t row = a.gather_token ? static_cast<size_t>(p / a.top_k)
+                                              : static_cast<size_t>(a.slot_of_pair[p]);
+            xrow[g] = a.X + row * a.K + kc * 16;
+        }
+
+        f32x4 acc[G][FN];
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) acc[g][fn] = f32x4{0.f, 0.f, 0.f, 0.f};
+        u32x4 xb[2][G][2], wb[2][FN][2];
         auto load = [&](int buf, int q) {
             const int k0 = q * 64;
-#pragma unroll
-            for (int h = 0; h < 2; ++h) xb[buf][h] = ld16(xrow + k0 + 8 * h);
 #pragma unroll
             for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
                 for (int h = 0; h < 2; ++h) wb[buf][fn][h] = ld16(brow[fn] + k0 + 8 * h);
+#pragma unroll
+            for (int g = 0; g < G; ++g)
+                if (live[g]) {
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) xb[buf][g][h] = ld16(xrow[g] + k0 + 8 * h);
+                }
         };
         auto compute = [&](int buf) {
 #pragma unroll
             for (int h = 0; h < 2; ++h)
 #pragma unroll
-                for (int fn = 0; fn < FN; ++fn) acc[fn] = mfma16x16x32(xb[buf][h], wb[buf][fn][h], acc[fn]);
+                for (int g = 0; g < G; ++g)
+                    if (live[g]) {
+#pragma unroll
+                        for (int fn = 0; fn < FN; ++fn)
+                            acc[g][fn] = mfma16x16x32(xb[buf][g][h], wb[buf][fn][h], acc[g][fn]);
+                    }
         };
-        // fragments made only of padding are skipped (uniform per wave)
-        const bool live = a.sorted_l[b * a.bm_l + fm * 16] < a.P;
         const int n = q1 - q0;
-        if (live && n > 0) {
+        if (n > 0) {
             // two-stage register pipeline (as in the skinny projection kernel)
             load(0, q0);
             int q = q0;
@@ -106,50 +126,55 @@ __global__ __launch_bounds__(kShrinkThreads) void k_shrink(ShrinkArgs a) {
             if (n & 1) compute(0);
         }
 
-        // add the K parts of the fragment in order 0..nkp-1 and store
-        if (nkp > 1) {
-            __syncthreads();  // the previous round's partials have been read
+        // add the four K quarters of each fragment in order 0..3 (wave g
+        // finishes fragment fg + g) and store
+        __syncthreads();  // the previous group's partials have been read
 #pragma unroll
-            for (int fn = 0; fn < FN; ++fn) red[wave][fn][lane] = acc[fn];
-            __syncthreads();
-            if (kp == 0) {
+        for (int g = 0; g < G; ++g)
 #pragma unroll
-                for (int fn = 0; fn < FN; ++fn)
-                    for (int w = 1; w < nkp; ++w) acc[fn] += red[wave + w][fn][lane];
+            for (int fn = 0; fn < FN; ++fn) red[wave][g][fn][lane] = acc[g][fn];
+        __syncthreads();
+        for (int g = wave; g < G; g += kShrinkWaves) {
+            const int fm = fg + g;
+            if (fm >= nfm || a.sorted_l[b * a.bm_l + fm * 16] >= a.P) continue;
+            f32x4 sum[FN];
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) {
+                sum[fn] = red[0][g][fn][lane];
+                for (int w = 1; w < kShrinkWaves; ++w) sum[fn] += red[w][g][fn][lane];
             }
-        }
-        if (kp != 0 || !live) continue;
-        int oslot[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int q = a.sorted_l[b * a.bm_l + fm * 16 + 4 * kc + i];
-            oslot[i] = q < a.P ? a.slot_of_pair[q] : -1;
-        }
-#pragma unroll
-        for (int fn = 0; fn < FN; ++fn) {
-            const int j = fn * 16 + lrow;
-            if (j < a.r) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    if (oslot[i] >= 0) a.S[(static_cast<size_t>(z) * a.C_b + oslot[i]) * a.r + j] = acc[fn][i];
-            }
-        }
-        if (a.S_hl) {
-            // the bf16 copy: hi = bf16(s), lo = bf16(s - hi), then zeros to
-            // the row end (only when 2r is below one 64-wide K step)
+            int oslot[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                if (oslot[i] < 0) continue;
-                uint16_t* row = a.S_hl + static_cast<size_t>(oslot[i]) * a.s_hl_stride;
+                const int q = a.sorted_l[b * a.bm_l + fm * 16 + 4 * kc + i];
+                oslot[i] = q < a.P ? a.slot_of_pair[q] : -1;
+            }
 #pragma unroll
-                for (int fn = 0; fn < FN; ++fn) {
-                    const int j = fn * 16 + lrow;
-                    if (j < a.r) {
-                        const uint16_t hi = f32_to_bf16_rne(acc[fn][i]);
-                        row[j] = hi;
-                        row[a.r + j] = f32_to_bf16_rne(acc[fn][i] - bf16_to_f32(hi));
-                        if constexpr (FN == 1)
-                            for (int q = 2 * a.r + j; q < a.s_hl_stride; q += a.r) row[q] = 0;
+            for (int fn = 0; fn < FN; ++fn) {
+                const int j = fn * 16 + lrow;
+                if (j < a.r) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (oslot[i] >= 0) a.S[(static_cast<size_t>(z) * a.C_b + oslot[i]) * a.r + j] = sum[fn][i];
+                }
+            }
+            if (a.S_hl) {
+                // the bf16 copy: hi = bf16(s), lo = bf16(s - hi), then zeros to
+                // the row end (only when 2r is below one 64-wide K step)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    if (oslot[i] < 0) continue;
+                    uint16_t* row = a.S_hl + static_cast<size_t>(oslot[i]) * a.s_hl_stride;
+#pragma unroll
+                    for (int fn = 0; fn < FN; ++fn) {
+                        const int j = fn * 16 + lrow;
+                        if (j < a.r) {
+                            const uint16_t hi = f32_to_bf16_rne(sum[fn][i]);
+                            row[j] = hi;
+                            row[a.r + j] = f32_to_bf16_rne(sum[fn][i] - bf16_to_f32(hi));
+                            if constexpr (FN == 1)
+                                for (int q = 2 * a.r + j; q < a.s_hl_stride; q += a.r) row[q] = 0;
+                        }
                     }
                 }
             }
@@ -175,13 +200,24 @@ hipError_t launch_shrink(const ShrinkArgs& a, hipStream_t s) {
     if (a.ksplit < 1 || a.ksplit > a.K / 64) return hipErrorInvalidValue;
     if (a.S_hl && (a.ksplit != 1 || a.s_hl_stride != s_hl_stride_of(a.r))) return hipErrorInvalidValue;
     const dim3 grid(a.n_blocks, a.ksplit), block(kShrinkThreads);
+    const int nfm = a.bm_l / 16;
+#define MOELORA_SHRINK(FN)                                                                            \
+    do {                                                                                              \
+        const int g = std::min(nfm, shrink_group<FN>());                                              \
+        if (g == 1) hipLaunchKernelGGL((k_shrink<FN, 1>), grid, block, 0, s, a);                      \
+        if constexpr (shrink_group<FN>() >= 2)                                                        \
+            if (g == 2) hipLaunchKernelGGL((k_shrink<FN, (shrink_group<FN>() >= 2 ? 2 : 1)>), grid, block, 0, s, a); \
+        if constexpr (shrink_group<FN>() >= 4)                                                        \
+            if (g == 4) hipLaunchKernelGGL((k_shrink<FN, (shrink_group<FN>() >= 4 ? 4 : 1)>), grid, block, 0, s, a); \
+    } while (0)
     switch ((a.r + 15) / 16) {
-        case 1: hipLaunchKernelGGL(k_shrink<1>, grid, block, 0, s, a); break;
-        case 2: hipLaunchKernelGGL(k_shrink<2>, grid, block, 0, s, a); break;
-        case 4: hipLaunchKernelGGL(k_shrink<4>, grid, block, 0, s, a); break;
-        case 8: hipLaunchKernelGGL(k_shrink<8>, grid, block, 0, s, a); break;
+        case 1: MOELORA_SHRINK(1); break;
+        case 2: MOELORA_SHRINK(2); break;
+        case 4: MOELORA_SHRINK(4); break;
+        case 8: MOELORA_SHRINK(8); break;
         default: return hipErrorInvalidValue;
     }
+#undef MOELORA_SHRINK
     return hipGetLastError();
 }
 

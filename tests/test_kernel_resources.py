@@ -44,7 +44,10 @@ MIN_OCCUPANCY = {
     "k_gemm_dma<256, 256, 2, 4, 2, true>": 2,
     "k_gemm_dma<256, 256, 2, 4, 2, false>": 2,
 }
-MIN_OCCUPANCY_SHRINK = {"k_shrink<1>": 8, "k_shrink<2>": 5, "k_shrink<4>": 3, "k_shrink<8>": 1}
+# one fragment per wave group (16-row LoRA blocks), and the groups of 2 or 4
+# fragments that share one load of the LoRA A chunk (larger blocks)
+MIN_OCCUPANCY_SHRINK = {"k_shrink<1, 1>": 6, "k_shrink<2, 1>": 5, "k_shrink<4, 1>": 3, "k_shrink<8, 1>": 2,
+                        "k_shrink<1, 4>": 3, "k_shrink<2, 4>": 2, "k_shrink<4, 2>": 2}
 
 
 def _demangle(names):

@@ -258,6 +258,20 @@ __device__ __forceinline__ void scatter_range(const AlignKeys& keyf, const Align
     }
 }
 
+// a[from .. to) = v by the whole workgroup; 16-byte stores where a is
+// 16-byte aligned and from, to are multiples of 4 (the view capacities and
+// lengths are multiples of the block heights, so the library's own buffers
+// always take that path)
+__device__ __forceinline__ void fill_tail(int32_t* a, int from, int to, int v) {
+    if ((reinterpret_cast<uintptr_t>(a) & 15) == 0 && (from & 3) == 0 && (to & 3) == 0) {
+        const int4 q{v, v, v, v};
+        for (int i = (from >> 2) + static_cast<int>(threadIdx.x); i < (to >> 2); i += blockDim.x)
+            reinterpret_cast<int4*>(a)[i] = q;
+    } else {
+        for (int i = from + static_cast<int>(threadIdx.x); i < to; i += blockDim.x) a[i] = v;
+    }
+}
+
 __global__ __launch_bounds__(kAlignThreads) void k_align(
     AlignKeys keyf, AlignOut o, int T, int bm_b_log2, int bm_l_log2, int C_b, int C_l, int nr,
     int R, int32_t* __restrict__ blk_e_b, int32_t* __restrict__ n_b_out,
@@ -329,16 +343,17 @@ __global__ __launch_bounds__(kAlignThreads) void k_align(
             if (o.slot_adapter) o.slot_adapter[slot] = -1;
         }
     }
-    for (int i = n_b + tid; i < C_b; i += kAlignThreads) {
-        o.sorted_b[i] = P;
-        if (o.slot_adapter) o.slot_adapter[i] = -1;
+    // the tails past n_b and n_l
+    fill_tail(o.sorted_b, n_b, C_b, P);
+    if (o.slot_adapter) fill_tail(o.slot_adapter, n_b, C_b, -1);
+    // each (expert, adapter) segment writes its own padding slots
+    for (int s = tid; s < nseg; s += kAlignThreads) {
+        const int e = s / L;
+        const int c = cnt[e * L1 + (s - e * L)];
+        const int base = lpos[s] + c, pad = ((c + bm_l - 1) & ~(bm_l - 1)) - c;
+        for (int i = 0; i < pad; ++i) o.sorted_l[base + i] = P;
     }
-    for (int idx = tid; idx < (nseg << bm_l_log2); idx += kAlignThreads) {
-        const int s = idx >> bm_l_log2, i = idx & (bm_l - 1);
-        const int c = cnt[(s / L) * L1 + s % L];
-        if (i < ((c + bm_l - 1) & ~(bm_l - 1)) - c) o.sorted_l[lpos[s] + c + i] = P;
-    }
-    for (int i = n_l + tid; i < C_l; i += kAlignThreads) o.sorted_l[i] = P;
+    fill_tail(o.sorted_l, n_l, C_l, P);
     for (int b = tid; b < (C_b >> bm_b_log2); b += kAlignThreads) {
         const int pos = b << bm_b_log2;
         int e = -1;

@@ -77,9 +77,14 @@ def sample_tokens(case, n):
 
 # ----------------------------------------------------------------------------- route / align
 
+# boundary shapes: 64 experts x 8 picks, 7 experts, 65 experts, 9 picks
 ROUTE_CASES = [("tiny", {}), ("decode", {}), ("prefill", {}), ("wide", {}), ("many", {}),
                ("odd", dict(T=37, H=64, I=64, E=70, top_k=7, L=3, r=8)),
-               ("one", dict(T=1, H=64, I=64, E=1, top_k=1, L=0, r=8))]
+               ("one", dict(T=1, H=64, I=64, E=1, top_k=1, L=0, r=8)),
+               ("lane_max", dict(T=300, H=64, I=64, E=64, top_k=8, L=2, r=8)),
+               ("lane_e7", dict(T=257, H=64, I=64, E=7, top_k=3, L=2, r=8)),
+               ("wave_e65", dict(T=33, H=64, I=64, E=65, top_k=8, L=2, r=8)),
+               ("wave_k9", dict(T=33, H=64, I=64, E=64, top_k=9, L=2, r=8))]
 
 
 @pytest.mark.parametrize("name,dims", ROUTE_CASES)
@@ -104,14 +109,18 @@ def test_route_ties(dev):
                        [0.5] * 6,
                        [-1.0, -2.0, -1.0, -2.0, -3.0, -1.0]], np.float32)
     logits = np.concatenate([logits, np.repeat(logits[:1], 70, axis=0)])
-    for k in (1, 2, 4, 6):
-        ref_ids, _ = oracle.route(logits, k)
-        d = ml.make_desc(logits.shape[0], 64, 64, 6, k, 0, 8)
-        ids = torch.empty((logits.shape[0], k), dtype=torch.int32, device=dev)
-        w = torch.empty((logits.shape[0], k), dtype=torch.float32, device=dev)
-        ml.route(d, torch.from_numpy(logits).to(dev), ids, w)
-        torch.cuda.synchronize()
-        np.testing.assert_array_equal(ids.cpu().numpy(), ref_ids)
+    # 6 experts (one logit per lane) and the same ties spread over 72 experts
+    # (two logits on some lanes)
+    wide = np.tile(logits, (1, 12))
+    for lg in (logits, wide):
+        for k in (1, 2, 4, 6):
+            ref_ids, _ = oracle.route(lg, k)
+            d = ml.make_desc(lg.shape[0], 64, 64, lg.shape[1], k, 0, 8)
+            ids = torch.empty((lg.shape[0], k), dtype=torch.int32, device=dev)
+            w = torch.empty((lg.shape[0], k), dtype=torch.float32, device=dev)
+            ml.route(d, torch.from_numpy(np.ascontiguousarray(lg)).to(dev), ids, w)
+            torch.cuda.synchronize()
+            np.testing.assert_array_equal(ids.cpu().numpy(), ref_ids)
 
 
 def gpu_align(dev, ids, ad, dims, bm_b, bm_l, workspace=True):

@@ -354,34 +354,24 @@ __global__ __launch_bounds__(kAlignThreads) void k_align(
         for (int i = 0; i < pad; ++i) o.sorted_l[base + i] = P;
     }
     fill_tail(o.sorted_l, n_l, C_l, P);
-    for (int b = tid; b < (C_b >> bm_b_log2); b += kAlignThreads) {
-        const int pos = b << bm_b_log2;
-        int e = -1;
-        if (pos < n_b) {
-            int lo = 0, hi = E - 1;  // largest e with start(e) <= pos
-            while (lo < hi) {
-                const int mid = (lo + hi + 1) >> 1;
-                if (bpos[mid * L1] <= pos) lo = mid; else hi = mid - 1;
-            }
-            e = lo;
-        }
-        blk_e_b[b] = e;
+    // block maps: each expert (base view) and each (expert, adapter) segment
+    // (LoRA view) writes the entries of its own blocks; blocks past n_b / n_l
+    // get -1
+    for (int e = tid; e < E; e += kAlignThreads) {
+        const int b0 = bpos[e * L1] >> bm_b_log2, nb = (ne[e] + bm_b - 1) >> bm_b_log2;
+        for (int j = 0; j < nb; ++j) blk_e_b[b0 + j] = e;
     }
-    for (int b = tid; b < (C_l >> bm_l_log2); b += kAlignThreads) {
-        const int pos = b << bm_l_log2;
-        int e = -1, a = -1;
-        if (pos < n_l) {
-            int lo = 0, hi = nseg - 1;  // largest segment with start <= pos
-            while (lo < hi) {
-                const int mid = (lo + hi + 1) >> 1;
-                if (lpos[mid] <= pos) lo = mid; else hi = mid - 1;
-            }
-            e = lo / L;
-            a = lo % L;
+    fill_tail(blk_e_b, n_b >> bm_b_log2, C_b >> bm_b_log2, -1);
+    for (int s = tid; s < nseg; s += kAlignThreads) {
+        const int e = s / L, a = s - e * L;
+        const int b0 = lpos[s] >> bm_l_log2, nb = (cnt[e * L1 + a] + bm_l - 1) >> bm_l_log2;
+        for (int j = 0; j < nb; ++j) {
+            blk_e_l[b0 + j] = e;
+            blk_a_l[b0 + j] = a;
         }
-        blk_e_l[b] = e;
-        blk_a_l[b] = a;
     }
+    fill_tail(blk_e_l, n_l >> bm_l_log2, C_l >> bm_l_log2, -1);
+    fill_tail(blk_a_l, n_l >> bm_l_log2, C_l >> bm_l_log2, -1);
     if (tid == 0) {
         *n_b_out = n_b;
         *n_l_out = n_l;

@@ -12,7 +12,10 @@ Default workload: the decode-shaped layer (16 tokens, hidden = intermediate =
 and dense (one expert) layers follow in "other_workloads".
 
 Weight copies are rotated between calls so that the working set of
-consecutive calls exceeds the 256 MB Infinity Cache.
+consecutive calls exceeds the 256 MB Infinity Cache. Where a layer runs the
+16-row projection kernels (decode-sized batches) it is given packed copies of
+its base weights, as a serving process would prepare once at load time
+(--row-layout: without them); config.launch.packed_weights says which.
 """
 import argparse
 import json
@@ -132,7 +135,7 @@ def lora_kernels_summary(kus, b):
             "hbm_frac": round(gbs / HBM_PEAK_GBS, 4) if gbs else None}
 
 
-def run_workload(name, steps, warmup, rotate, dev, table=None):
+def run_workload(name, steps, warmup, rotate, dev, table=None, packed=True):
     import torch
 
     import oracle
@@ -150,14 +153,16 @@ def run_workload(name, steps, warmup, rotate, dev, table=None):
         tens = base if i == 0 else {k: v.clone() for k, v in base.items()}
         layers.append((ml.Layer(case.T, case.H, case.I, case.E, case.top_k, case.L, case.r,
                                 tens["w_gate_up"], tens["w_down"], tens["a_gate_up"],
-                                tens["b_gate_up"], tens["a_down"], tens["b_down"], tuning=table), tens))
+                                tens["b_gate_up"], tens["a_down"], tens["b_down"], tuning=table,
+                                packed_weights=packed), tens))
     layer0 = layers[0][0]
     bm_b, bm_l = ml.block_sizes(layer0.desc)
     launch = {"block_m_base": bm_b, "block_m_lora": bm_l,
               "shrink_launch": bool(layer0.desc.flags & ml.FLAG_SHRINK_LAUNCH),
               "combine": ("own launch, fixed order" if layer0.keeps_down_rows
                           else "in the down projection's epilogue (fp32 atomic adds)"),
-              "from_tuning_table": layer0.tuned is not None}
+              "from_tuning_table": layer0.tuned is not None,
+              "packed_weights": layer0.packed}
     out = torch.empty((case.T, case.H), dtype=torch.float32, device=dev)
 
     def step(i):
@@ -290,6 +295,8 @@ def main():
                     help="tuning folder (per-shape block sizes and shrink placement); default: the "
                          "package's configs folder when it exists")
     ap.add_argument("--no-tuning", action="store_true", help="use the library's default choices")
+    ap.add_argument("--row-layout", action="store_true",
+                    help="do not give the 16-row kernels packed copies of the base weights")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MiB",
                     help="first run one plain device-to-device copy of this size, as the "
                          "reference dispatch for scaling HBM byte counters")
@@ -323,7 +330,7 @@ def main():
         else:
             table_dir = None
     case, ids, st, ms, kus, b, f, lbytes, lflops, reps, launch = run_workload(
-        args.workload, args.steps, args.warmup, args.rotate, dev, table)
+        args.workload, args.steps, args.warmup, args.rotate, dev, table, not args.row_layout)
     main_obj = workload_summary(args.workload, case, st, ms, kus, b, f, lbytes, lflops, reps, launch)
     line = {
         "metric": "MoE-LoRA layer tokens/s + us/call (decode 16 tok, prefill 6400 tok); % roofline",
@@ -349,7 +356,7 @@ def main():
     prefill_case = None
     for name in others:
         steps2 = max(5, args.steps // 5) if name in ("prefill", "many") else max(10, args.steps // 2)
-        res = run_workload(name, steps2, max(2, args.warmup // 2), args.rotate, dev, table)
+        res = run_workload(name, steps2, max(2, args.warmup // 2), args.rotate, dev, table, not args.row_layout)
         obj = workload_summary(name, res[0], res[2], *res[3:])
         if name == "prefill":
             line["prefill"] = obj

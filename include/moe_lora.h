@@ -109,11 +109,33 @@ typedef struct moe_lora_desc {
  *   b_gate_up [L][E][2I][r]  LoRA expand of gate_up
  *   a_down    [L][E][r][I]
  *   b_down    [L][E][H][r]
+ *   w_gate_up_packed, w_down_packed: optional copies of w_gate_up / w_down
+ *             written by moe_lora_pack_weights (same sizes); NULL = none.
+ *             Where a call runs the 16-row kernels they read these instead,
+ *             with bitwise-equal results.
  * The four LoRA pointers may be NULL when L == 0. */
 typedef struct moe_lora_weights {
     const void *w_gate_up, *w_down;
     const void *a_gate_up, *b_gate_up, *a_down, *b_down;
+    const void *w_gate_up_packed, *w_down_packed;
 } moe_lora_weights;
+
+/* Copies of the base weights in the order in which the 16-row projection
+ * kernels (few rows per expert: decode-sized batches) stream them, for
+ * callers that can hold a second copy. In the row layout each wave reads 64
+ * rows at the matrix pitch, and pitches with large power-of-two factors
+ * (8 or 10 KiB, e.g. hidden sizes 4096 or 5120) stream up to about a fifth
+ * slower; in the packed copy the bytes a wave reads for one 64-wide K chunk
+ * of its tile form one contiguous 8 KiB block, and its blocks follow each
+ * other. The packed order depends only on E, H and I.
+ *   w_gate_up, w_down           the row-layout weights (as in moe_lora_weights)
+ *   w_gate_up_packed, w_down_packed   outputs, same sizes, 16-byte aligned,
+ *                               not overlapping the inputs
+ * Either pair may be NULL (that projection is not packed). Enqueued on
+ * `stream`. Returns MOE_LORA_EINVAL for a shape the 16-row kernels do not
+ * take (I a multiple of 32 and H of 64 are needed). */
+int moe_lora_pack_weights(const moe_lora_desc *d, const void *w_gate_up, const void *w_down,
+                          void *w_gate_up_packed, void *w_down_packed, void *stream);
 
 /* Human-readable text of an error code (static storage). */
 const char *moe_lora_strerror(int code);

@@ -175,6 +175,9 @@ int check_weights(const moe_lora_desc* d, const moe_lora_weights* w) {
         for (const void* q : l)
             if (!q || !aligned16(q)) return MOE_LORA_EINVAL;
     }
+    if ((w->w_gate_up_packed && (!aligned16(w->w_gate_up_packed) || !pack_skinny_supported(d->I, d->H, 1))) ||
+        (w->w_down_packed && (!aligned16(w->w_down_packed) || !pack_skinny_supported(d->H, d->I, 0))))
+        return MOE_LORA_EINVAL;
     return MOE_LORA_OK;
 }
 
@@ -261,6 +264,25 @@ int moe_lora_align_capacity(const moe_lora_desc* d, int32_t* C_b, int32_t* C_l) 
     if (rc) return rc;
     if (C_b) *C_b = p.C_b;
     if (C_l) *C_l = p.C_l;
+    return MOE_LORA_OK;
+}
+
+int moe_lora_pack_weights(const moe_lora_desc* d, const void* w_gate_up, const void* w_down,
+                          void* w_gate_up_packed, void* w_down_packed, void* stream) {
+    const int rc = check_desc(d);
+    if (rc) return rc;
+    const bool gu = w_gate_up_packed != nullptr, dn = w_down_packed != nullptr;
+    if ((gu && (!w_gate_up || !aligned16(w_gate_up) || !aligned16(w_gate_up_packed) ||
+                !pack_skinny_supported(d->I, d->H, 1))) ||
+        (dn && (!w_down || !aligned16(w_down) || !aligned16(w_down_packed) || !pack_skinny_supported(d->H, d->I, 0))))
+        return MOE_LORA_EINVAL;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (gu && launch_pack_skinny(static_cast<const uint16_t*>(w_gate_up), static_cast<uint16_t*>(w_gate_up_packed),
+                                 d->E, d->I, d->H, 1, s) != hipSuccess)
+        return MOE_LORA_EHIP;
+    if (dn && launch_pack_skinny(static_cast<const uint16_t*>(w_down), static_cast<uint16_t*>(w_down_packed), d->E,
+                                 d->H, d->I, 0, s) != hipSuccess)
+        return MOE_LORA_EHIP;
     return MOE_LORA_OK;
 }
 
@@ -374,6 +396,7 @@ int forward_planned(const Plan& p, const moe_lora_desc* d, const moe_lora_weight
     ga.C_b = p.C_b; ga.h_out = h; ga.d_out = dn; ga.ksplit = 1; ga.s_split = p.ssplit;
     ga.X = static_cast<const uint16_t*>(x); ga.gate_up = 1;
     ga.W = static_cast<const uint16_t*>(w->w_gate_up); ga.N_out = p.I; ga.K = p.H;
+    ga.Wp = p.bm_b == 16 ? static_cast<const uint16_t*>(w->w_gate_up_packed) : nullptr;
     ga.S = s1; ga.Bl = static_cast<const uint16_t*>(w->b_gate_up);
     ga.S_hl = s1hl; ga.s_hl_stride = s_hl_stride_of(p.r); ga.ksw = p.ksw_gu;
     if (p.fused) {
@@ -396,6 +419,7 @@ int forward_planned(const Plan& p, const moe_lora_desc* d, const moe_lora_weight
     timing_mark(call, 5, s);
 
     ga.X = h; ga.gate_up = 0; ga.W = static_cast<const uint16_t*>(w->w_down); ga.N_out = p.H;
+    ga.Wp = p.bm_b == 16 ? static_cast<const uint16_t*>(w->w_down_packed) : nullptr;
     ga.K = p.I; ga.S = s2; ga.Bl = static_cast<const uint16_t*>(w->b_down); ga.ksplit = p.ksplit;
     ga.S_hl = s2hl; ga.ksw = p.ksw_dn;
     if (p.fuse_combine) {

@@ -349,11 +349,28 @@ __global__ __launch_bounds__(64 * KSW) void k_gemm_skinny(GemmArgs a) {
     } else {
         xrow = a.X + static_cast<size_t>(slot) * K + kbeg + g * 16;
     }
+    // Weight operand: the 64 rows of the tile at the matrix pitch, or the
+    // packed copy, where the tile's 64-wide K chunk q is one 8 KiB block
+    // [fragment][half][lane][8] (lane = 16 g + lrow) and the blocks of
+    // consecutive chunks follow each other. wq, wh: elements per K chunk and
+    // per 16-byte half.
     const uint16_t* wrow[FN];
+    int wq, wh;
+    if (a.Wp) {
+        const uint16_t* wt =
+            a.Wp + (static_cast<size_t>(e * n_tiles + tile) * (K / 64) + kbeg / 64) * (FN * 1024) + lane * 8;
 #pragma unroll
-    for (int f = 0; f < FN; ++f)
-        wrow[f] = a.W + (static_cast<size_t>(e) * Nw + w_row_of_frag<GATEUP>(f, c0, I) + lrow) * K +
-                  kbeg + g * 16;
+        for (int f = 0; f < FN; ++f) wrow[f] = wt + f * 1024;
+        wq = FN * 1024;
+        wh = 512;
+    } else {
+#pragma unroll
+        for (int f = 0; f < FN; ++f)
+            wrow[f] = a.W + (static_cast<size_t>(e) * Nw + w_row_of_frag<GATEUP>(f, c0, I) + lrow) * K +
+                      kbeg + g * 16;
+        wq = 64;
+        wh = 8;
+    }
 
     f32x4 acc[FN];
 #pragma unroll
@@ -366,7 +383,7 @@ __global__ __launch_bounds__(64 * KSW) void k_gemm_skinny(GemmArgs a) {
 #pragma unroll
         for (int f = 0; f < FN; ++f)
 #pragma unroll
-            for (int h = 0; h < 2; ++h) wb[buf][f][h] = ld16(wrow[f] + k0 + 8 * h);
+            for (int h = 0; h < 2; ++h) wb[buf][f][h] = ld16(wrow[f] + static_cast<size_t>(q) * wq + h * wh);
     };
     auto compute = [&](int buf) {
 #pragma unroll
@@ -1250,6 +1267,58 @@ static hipError_t launch_tiled(const GemmArgs& a, hipStream_t s) {
         hipLaunchKernelGGL((k_gemm_tiled<BM, BNT, WM, WN, true>), grid, block, 0, s, b);
     else
         hipLaunchKernelGGL((k_gemm_tiled<BM, BNT, WM, WN, false>), grid, block, 0, s, b);
+    return hipGetLastError();
+}
+
+// The packed copy of W for the 16-row kernel: for expert e, column tile t and
+// 64-wide K chunk q, one block of FN x 1 KiB, [fragment f][half h][lane][8]:
+// lane (16 g + n) of (f, h) holds W[row of fragment f + n][64 q + 16 g + 8 h
+// ... + 8], the 16 bytes that lane loads for that fragment and half. One
+// thread copies one 16-byte piece.
+template <bool GATEUP>
+__global__ __launch_bounds__(256) void k_pack_skinny(const uint16_t* __restrict__ W, uint16_t* __restrict__ Wp,
+                                                     int E, int N_out, int K) {
+    constexpr int FN = GATEUP ? kSkinnyFNGateUp : kSkinnyFNDown;
+    constexpr int kCols = GATEUP ? FN * 8 : FN * 16;
+    const int n_tiles = N_out / kCols, nq = K / 64;
+    const int I = GATEUP ? N_out : 0;
+    const int Nw = GATEUP ? 2 * N_out : N_out;
+    const long total = static_cast<long>(E) * n_tiles * nq * FN * 128;
+    for (long i = static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x; i < total;
+         i += static_cast<long>(gridDim.x) * blockDim.x) {
+        const int lane = static_cast<int>(i & 63);
+        long r = i >> 6;
+        const int h = static_cast<int>(r & 1);
+        r >>= 1;
+        const int f = static_cast<int>(r % FN);
+        r /= FN;
+        const int q = static_cast<int>(r % nq);
+        r /= nq;
+        const int t = static_cast<int>(r % n_tiles);
+        const int e = static_cast<int>(r / n_tiles);
+        const int row = w_row_of_frag<GATEUP>(f, t * kCols, I) + (lane & 15);
+        const int col = q * 64 + 16 * (lane >> 4) + 8 * h;
+        *reinterpret_cast<u32x4*>(Wp + i * 8) =
+            *reinterpret_cast<const u32x4*>(W + (static_cast<size_t>(e) * Nw + row) * K + col);
+    }
+}
+
+bool pack_skinny_supported(int N_out, int K, int gate_up) {
+    const int cols = gate_up ? kSkinnyFNGateUp * 8 : kSkinnyFNDown * 16;
+    return N_out > 0 && K > 0 && N_out % cols == 0 && K % 64 == 0;
+}
+
+hipError_t launch_pack_skinny(const uint16_t* W, uint16_t* Wp, int E, int N_out, int K, int gate_up,
+                              hipStream_t s) {
+    if (!pack_skinny_supported(N_out, K, gate_up) || E <= 0) return hipErrorInvalidValue;
+    const long pieces = static_cast<long>(E) * (gate_up ? 2 : 1) * N_out * (K / 8);
+    const long blocks = std::min<long>((pieces + 255) / 256, 65536);
+    if (gate_up)
+        hipLaunchKernelGGL(k_pack_skinny<true>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, W, Wp, E,
+                           N_out, K);
+    else
+        hipLaunchKernelGGL(k_pack_skinny<false>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, W, Wp, E,
+                           N_out, K);
     return hipGetLastError();
 }
 

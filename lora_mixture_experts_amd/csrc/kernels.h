@@ -83,6 +83,7 @@ struct GemmArgs {
     const int32_t* n_b_live;  // padded length of the base view (live blocks x bm_b), from the alignment
     int xcd_slots;            // direct-load kernel: workgroups resident per XCD (set by its launcher)
     const uint16_t* W;        // gate_up: [E][2I][H]; down: [E][H][I]
+    const uint16_t* Wp;       // 16-row kernel: W in its packed order (launch_pack_skinny), or null
     int N_out;                // gate_up: I (h columns); down: H
     int K;                    // gate_up: H; down: I
     // LoRA expand
@@ -132,6 +133,11 @@ struct GemmArgs {
 // computed the shrink of its own rows (output valid, slower)
 constexpr int32_t kStatusShrinkFallback = 1;
 constexpr int kMaxProducerPolls = 1 << 20;
+// W in the 16-row projection kernel's packed order (see k_pack_skinny);
+// false when the shape does not suit that kernel.
+bool pack_skinny_supported(int N_out, int K, int gate_up);
+hipError_t launch_pack_skinny(const uint16_t* W, uint16_t* Wp, int E, int N_out, int K, int gate_up,
+                              hipStream_t s);
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
 // Whether a tile configuration exists for these sizes.
 bool gemm_supported(int N_out, int K, int gate_up, int bm_b);

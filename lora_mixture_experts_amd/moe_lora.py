@@ -44,7 +44,8 @@ class PlanInfo(ctypes.Structure):
 
 class Weights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
-                ("w_gate_up", "w_down", "a_gate_up", "b_gate_up", "a_down", "b_down")]
+                ("w_gate_up", "w_down", "a_gate_up", "b_gate_up", "a_down", "b_down",
+                 "w_gate_up_packed", "w_down_packed")]
 
 
 _lib = None
@@ -70,6 +71,7 @@ def lib():
             "moe_lora_align_capacity": ([pD, pI32, pI32], ctypes.c_int),
             "moe_lora_route": ([pD, P, P, P, P], ctypes.c_int),
             "moe_lora_align": ([pD] + [P] * 9 + [P, SZ, P], ctypes.c_int),
+            "moe_lora_pack_weights": ([pD, P, P, P, P, P], ctypes.c_int),
             "moe_lora_forward": ([pD, pW, P, P, P, P, P, SZ, P], ctypes.c_int),
             "moe_lora_forward_noalloc": ([pD, pW, P, P, P, P, P], ctypes.c_int),
             "moe_lora_read_stages": ([pD, P, SZ, P, P, P, P, P, P, P], ctypes.c_int),
@@ -89,7 +91,8 @@ def lib():
 
 EXPORTED = ("moe_lora_strerror", "moe_lora_validate", "moe_lora_block_sizes", "moe_lora_plan",
             "moe_lora_workspace_bytes", "moe_lora_align_capacity", "moe_lora_route",
-            "moe_lora_align", "moe_lora_forward", "moe_lora_forward_noalloc", "moe_lora_read_stages",
+            "moe_lora_align", "moe_lora_pack_weights", "moe_lora_forward", "moe_lora_forward_noalloc",
+            "moe_lora_read_stages",
             "moe_lora_read_alignment",
             "moe_lora_read_status",
             "moe_lora_timing_enable", "moe_lora_timing_read", "moe_lora_kernel_name")
@@ -176,9 +179,18 @@ def align(desc, topk_ids, adapter_ids, sorted_b, blk_e_b, n_b, sorted_l, blk_e_l
                                 ctypes.c_size_t(ws_bytes), _stream(stream)), "align")
 
 
-def weights_struct(w_gate_up, w_down, a_gate_up=None, b_gate_up=None, a_down=None, b_down=None):
+def weights_struct(w_gate_up, w_down, a_gate_up=None, b_gate_up=None, a_down=None, b_down=None,
+                   w_gate_up_packed=None, w_down_packed=None):
     return Weights(*(None if t is None or t.numel() == 0 else t.data_ptr()
-                     for t in (w_gate_up, w_down, a_gate_up, b_gate_up, a_down, b_down)))
+                     for t in (w_gate_up, w_down, a_gate_up, b_gate_up, a_down, b_down,
+                               w_gate_up_packed, w_down_packed)))
+
+
+def pack_weights(desc, w_gate_up, w_down, w_gate_up_packed, w_down_packed, stream=None):
+    """Write the 16-row kernels' packed copies of the base weights (either
+    pair may be None)."""
+    _check(lib().moe_lora_pack_weights(ctypes.byref(desc), _ptr(w_gate_up), _ptr(w_down), _ptr(w_gate_up_packed),
+                                       _ptr(w_down_packed), _stream(stream)), "pack_weights")
 
 
 def forward(desc, weights: Weights, x, logits, adapter_ids, out, workspace, stream=None):
@@ -245,10 +257,14 @@ class Layer:
 
     def __init__(self, T, H, I, E, top_k, L, r, w_gate_up, w_down, a_gate_up=None, b_gate_up=None,
                  a_down=None, b_down=None, block_m_base=0, block_m_lora=0, out_bf16=False,
-                 shrink_launch=False, tuning=None, fused_combine=False, no_shrink_wait=False, **launch):
+                 shrink_launch=False, tuning=None, fused_combine=False, no_shrink_wait=False,
+                 packed_weights=False, **launch):
         """tuning: a tuning.Table; when it holds a choice for this shape and
         token count it sets the block sizes, the shrink placement and the
         launch tuning fields (only if none of them is given explicitly).
+        packed_weights: where the plan uses 16-row base blocks, also hold
+        packed copies of the base weights, which those kernels then read
+        (twice the base weight memory; self.packed says whether it did).
         launch: any of TUNING_FIELDS (0 = the library's choice)."""
         import torch
         bad = set(launch) - set(TUNING_FIELDS)
@@ -272,7 +288,14 @@ class Layer:
         # separate launch does the weighted combine
         self.keeps_down_rows = not fused_combine
         self.out_dtype = torch.bfloat16 if out_bf16 else torch.float32
-        self.tensors = (w_gate_up, w_down, a_gate_up, b_gate_up, a_down, b_down)
+        # packed copies only where the plan runs the 16-row kernels, which
+        # are the ones that read them
+        packed = (None, None)
+        self.packed = bool(packed_weights) and plan(self.desc)["block_m_base"] == 16
+        if self.packed:
+            packed = (torch.empty_like(w_gate_up), torch.empty_like(w_down))
+            pack_weights(self.desc, w_gate_up, w_down, *packed)
+        self.tensors = (w_gate_up, w_down, a_gate_up, b_gate_up, a_down, b_down) + packed
         self.weights = weights_struct(*self.tensors)
         _check(validate(self.desc, self.weights), "validate")
         self.workspace = torch.empty(workspace_bytes(self.desc), dtype=torch.uint8, device=w_gate_up.device)

@@ -93,6 +93,21 @@ def test_validate_checks_weight_pointers():
     assert ml.validate(ds, ml.Weights(4096, 4096, 4096, 4096, 4096, 4096)) == ml.OK
     ds0 = desc(L=0)
     assert ml.validate(ds0, ml.Weights(4096, 4096, None, None, None, None)) == ml.OK
+    # the optional packed copies: accepted when 16-byte aligned
+    assert ml.validate(ds, ml.Weights(4096, 4096, 4096, 4096, 4096, 4096, 8192, 8192)) == ml.OK
+    assert ml.validate(ds, ml.Weights(4096, 4096, 4096, 4096, 4096, 4096, 8200, None)) == ml.EINVAL
+    assert ml.validate(ds, ml.Weights(4096, 4096, 4096, 4096, 4096, 4096, None, 8200)) == ml.EINVAL
+
+
+def test_pack_weights_refuses_bad_pointers_on_the_host():
+    ds = desc()
+    f = ml.lib().moe_lora_pack_weights
+    P = ctypes.c_void_p
+    assert f(ctypes.byref(ds), P(4096), P(4096), P(8200), None, None) == ml.EINVAL   # misaligned output
+    assert f(ctypes.byref(ds), P(4104), None, P(8192), None, None) == ml.EINVAL      # misaligned input
+    assert f(ctypes.byref(ds), None, P(4096), P(8192), None, None) == ml.EINVAL      # output without input
+    assert f(ctypes.byref(desc(H=100)), P(4096), P(4096), P(8192), P(8192), None) == ml.EINVAL
+    assert f(ctypes.byref(ds), None, None, None, None, None) == ml.OK                # nothing to pack
 
 
 def test_zero_tokens_is_valid():

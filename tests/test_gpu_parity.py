@@ -56,12 +56,13 @@ def build_case(name, dims=None, seed=None, touched_only=True):
     return wl.make_case(name, seed=seed, dims=dims, experts=experts, lora_blocks=blocks)
 
 
-def run_gpu(case, dev, bm_b=0, bm_l=0, shrink_launch=False, tuning=None, fused_combine=False):
+def run_gpu(case, dev, bm_b=0, bm_l=0, shrink_launch=False, tuning=None, fused_combine=False,
+            packed_weights=False):
     t = wl.device_tensors(case, dev)
     layer = ml.Layer(case.T, case.H, case.I, case.E, case.top_k, case.L, case.r,
                      t["w_gate_up"], t["w_down"], t["a_gate_up"], t["b_gate_up"], t["a_down"],
                      t["b_down"], block_m_base=bm_b, block_m_lora=bm_l, shrink_launch=shrink_launch,
-                     tuning=tuning, fused_combine=fused_combine)
+                     tuning=tuning, fused_combine=fused_combine, packed_weights=packed_weights)
     out = layer(t["x"], t["logits"], t["adapter_ids"])
     torch.cuda.synchronize()
     return layer, t, out
@@ -187,7 +188,7 @@ def test_align_parity(dev, name, dims, bm):
 # ----------------------------------------------------------------------------- the layer
 
 def check_layer(case, dev, bm=(0, 0), stages=False, stage_tokens=64, shrink_launch=False,
-                tuning=None, expect_choice=None, fused_combine=False):
+                tuning=None, expect_choice=None, fused_combine=False, packed_weights=False):
     """Run the layer through the C ABI and compare EVERY output element with
     the oracle (max and mean bars over all T x H values); the alignment the
     call used is compared bit for bit. With stages=True the intermediates of
@@ -195,7 +196,7 @@ def check_layer(case, dev, bm=(0, 0), stages=False, stage_tokens=64, shrink_laun
     too."""
     ids, w = oracle.route(case.logits, case.top_k)
     layer, t, out = run_gpu(case, dev, *bm, shrink_launch=shrink_launch, tuning=tuning,
-                            fused_combine=fused_combine)
+                            fused_combine=fused_combine, packed_weights=packed_weights)
     got = out.cpu().numpy()
     assert layer.status() == 0
     if tuning is not None:
@@ -517,6 +518,35 @@ def test_layer_shapes(dev, i):
     log(f"layer shape {dims}")
     case = build_case(f"shape{i}", dims=dims, seed=40 + i)
     check_layer(case, dev, stages=True)
+
+
+# packed copies of the base weights: read by the 16-row kernels (decode-sized
+# batches), with every launch option they take; unused at larger blocks
+PACKED_CASES = [("decode", None, {}, False), ("dense", None, {}, False), ("tiny", None, {}, False),
+                ("odd", dict(T=5, H=320, I=448, E=3, top_k=2, L=2, r=16), {}, False),
+                ("decode", None, dict(down_ksplit=3, waves_gate_up=2, waves_down=2), False),
+                ("decode", None, {}, True),
+                ("wide", None, {}, False)]
+
+
+@pytest.mark.parametrize("name,dims,launch,shrink_launch", PACKED_CASES)
+def test_packed_weights_give_bitwise_equal_output(dev, name, dims, launch, shrink_launch):
+    log(f"packed weights {name} {dims or ''} {launch} shrink_launch={shrink_launch}")
+    case = build_case(name, dims=dims, touched_only=False)
+    t = wl.device_tensors(case, dev)
+    outs = []
+    for packed in (False, True):
+        layer = ml.Layer(case.T, case.H, case.I, case.E, case.top_k, case.L, case.r, t["w_gate_up"], t["w_down"],
+                         t["a_gate_up"], t["b_gate_up"], t["a_down"], t["b_down"], shrink_launch=shrink_launch,
+                         packed_weights=packed, **launch)
+        outs.append(layer(t["x"], t["logits"], t["adapter_ids"]))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1])
+
+
+def test_layer_parity_packed_weights(dev):
+    log("layer packed weights vs oracle")
+    check_layer(build_case("decode"), dev, packed_weights=True)
 
 
 def test_layer_many_experts_and_adapters(dev):

@@ -549,6 +549,68 @@ def test_layer_parity_packed_weights(dev):
     check_layer(build_case("decode"), dev, packed_weights=True)
 
 
+# A seeded sweep: random small shapes crossed with random launch options
+# (block sizes of both views, split fields, shrink placement, combine in the
+# down projection, bf16 output, packed weight copies), each against the oracle
+# on every output. Options the library rejects for a shape are dropped, in
+# that order, until the descriptor is valid.
+SWEEP_CASES = 40
+
+
+def _sweep_setup(i):
+    rng = np.random.default_rng(5000 + i)
+    E = int(rng.integers(1, 17))
+    dims = dict(T=int(rng.choice([1, 3, 16, 37, 130, 300])), H=64 * int(rng.integers(1, 13)),
+                I=64 * int(rng.integers(1, 13)), E=E, top_k=int(rng.integers(1, min(E, 8) + 1)),
+                L=int(rng.integers(0, 6)), r=int(rng.choice([8, 16, 32, 64])))
+    while dims["T"] > 1 and dims["T"] * dims["top_k"] * dims["H"] * dims["I"] > 2e8:
+        dims["T"] //= 2  # keeps the oracle within a few seconds
+    # every block height of both views in turn, the rest drawn
+    opts = dict(block_m_base=[0, 16, 32, 64, 128, 256][i % 6],
+                block_m_lora=[0, 16, 32, 64][(i // 6) % 4],
+                shrink_launch=bool(rng.integers(0, 2)), fused_combine=bool(rng.random() < 0.3),
+                out_bf16=bool(rng.random() < 0.2), packed_weights=bool(rng.integers(0, 2)))
+    launch = dict(down_ksplit=int(rng.choice([0, 0, 2, 3, 5])), shrink_ksplit=int(rng.choice([0, 0, 2, 4])),
+                  waves_gate_up=int(rng.choice([0, 0, 2, 4])), waves_down=int(rng.choice([0, 0, 2, 4])))
+
+    def valid(o, ln):
+        flags = ((ml.FLAG_OUT_BF16 if o["out_bf16"] else 0) | (ml.FLAG_SHRINK_LAUNCH if o["shrink_launch"] else 0) |
+                 (ml.FLAG_FUSED_COMBINE if o["fused_combine"] else 0))
+        d = ml.make_desc(dims["T"], dims["H"], dims["I"], dims["E"], dims["top_k"], dims["L"], dims["r"],
+                         o["block_m_base"], o["block_m_lora"], flags, **ln)
+        return ml.validate(d) == ml.OK
+
+    for drop in ("waves_down", "waves_gate_up", "shrink_ksplit", "down_ksplit"):
+        if valid(opts, launch):
+            break
+        launch[drop] = 0
+    if not valid(opts, launch):
+        opts["out_bf16"] = False
+    assert valid(opts, launch), (dims, opts, launch)
+    return dims, opts, launch
+
+
+@pytest.mark.parametrize("i", range(SWEEP_CASES))
+def test_layer_random_sweep(dev, i):
+    dims, opts, launch = _sweep_setup(i)
+    log(f"sweep {i}: {dims} {opts} {launch}")
+    case = build_case(f"sweep{i}", dims=dims, seed=6000 + i)
+    t = wl.device_tensors(case, dev)
+    layer = ml.Layer(case.T, case.H, case.I, case.E, case.top_k, case.L, case.r, t["w_gate_up"], t["w_down"],
+                     t["a_gate_up"], t["b_gate_up"], t["a_down"], t["b_down"], **opts, **launch)
+    out = layer(t["x"], t["logits"], t["adapter_ids"])
+    torch.cuda.synchronize()
+    assert layer.status() in (0, ml.STATUS_SHRINK_FALLBACK)
+    got = out.float().cpu().numpy()
+    ids, w = oracle.route(case.logits, case.top_k)
+    ref = oracle.forward(case, ids, w)
+    mx, mean = metrics(got, ref)
+    # bf16 output adds its own rounding (at most 2^-8 relative per element)
+    mean_tol = MEAN_TOL + (2e-3 if opts["out_bf16"] else 0.0)
+    assert np.all(np.isfinite(got))
+    assert mx <= MAX_TOL and mean <= mean_tol, (mx, mean)
+
+
 def test_layer_many_experts_and_adapters(dev):
     # 256 experts x 40 adapters (10496 keys): the alignment runs on the
     # multi-launch path inside the forward pass

@@ -954,11 +954,9 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <int FM, int FN, int A_PW, int B_PW>
+// where the wave's fragments sit in a stage's LDS tiles
 struct DmaCtx {
-    const uint16_t* const* asrc;
-    const uint16_t* const* bsrc;
-    int wave, arow0, brow0, kc, lrow;
+    int arow0, brow0, kc, lrow;
     bool wlive;
 };
 
@@ -988,16 +986,12 @@ __device__ __forceinline__ void dma_issue(const uint16_t* const* asrc, const uin
     for (int i = 0; i < B_PW; ++i) dma16(bsrc[i] + k0, bb + (wave * B_PW + i) * 512);
 }
 
-// Request the stage at K offset k_next (if >= 0) into (na, nb) and multiply
-// the stage held in (ca, cb). The restrict qualifiers tell the compiler that
-// the buffers being filled and the buffers being read do not overlap, so it
-// does not wait for the new requests before the LDS reads.
-template <int FM, int FN, int A_PW, int B_PW>
-__device__ __forceinline__ void dma_step(const DmaCtx<FM, FN, A_PW, B_PW>& c, f32x4 (&acc)[FM][FN],
+// Multiply the stage held in (ca, cb) into the accumulators: per 32-wide K
+// half, the wave's B and A fragments from LDS, then its FM x FN MFMAs.
+template <int FM, int FN>
+__device__ __forceinline__ void dma_step(const DmaCtx& c, f32x4 (&acc)[FM][FN],
                                          const uint16_t* __restrict__ ca,
-                                         const uint16_t* __restrict__ cb, uint16_t* __restrict__ na,
-                                         uint16_t* __restrict__ nb, int k_next) {
-    if (k_next >= 0) dma_issue<A_PW, B_PW>(c.asrc, c.bsrc, na, nb, c.wave, k_next);
+                                         const uint16_t* __restrict__ cb) {
     __builtin_amdgcn_sched_barrier(0);
     if (!c.wlive) return;
 #pragma unroll
@@ -1180,7 +1174,7 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_dma(GemmArgs a) {
         }
     };
 
-    DmaCtx<FM, FN, A_PW, B_PW> ctx{asrc, bsrc, wave, wm * (BM / WM), wn * (BNT / WN), kc, lrow, wlive};
+    const DmaCtx ctx{wm * (BM / WM), wn * (BNT / WN), kc, lrow, wlive};
     uint16_t* const abufs[3] = {As0, As1, As2};
     uint16_t* const bbufs[3] = {Bs0, Bs1, Bs2};
 #pragma unroll
@@ -1200,7 +1194,7 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_dma(GemmArgs a) {
                 wait_vmcnt<0>();
             bare_barrier();
             if (k + s + NS - 1 < nk_all) issue(k + s + NS - 1, abufs[(s + NS - 1) % NS], bbufs[(s + NS - 1) % NS]);
-            dma_step(ctx, acc, abufs[s], bbufs[s], abufs[(s + NS - 1) % NS], bbufs[(s + NS - 1) % NS], -1);
+            dma_step(ctx, acc, abufs[s], bbufs[s]);
         }
     }
 

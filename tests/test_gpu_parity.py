@@ -521,12 +521,17 @@ def test_layer_shapes(dev, i):
 
 
 # packed copies of the base weights: read by the 16-row kernels (decode-sized
-# batches), with every launch option they take; unused at larger blocks
+# batches), with every launch option they take; ignored at larger blocks
+# (32/64-row tiled with a down K split, 128/256-row direct loads)
 PACKED_CASES = [("decode", None, {}, False), ("dense", None, {}, False), ("tiny", None, {}, False),
                 ("odd", dict(T=5, H=320, I=448, E=3, top_k=2, L=2, r=16), {}, False),
                 ("decode", None, dict(down_ksplit=3, waves_gate_up=2, waves_down=2), False),
                 ("decode", None, {}, True),
-                ("wide", None, {}, False)]
+                ("wide", None, {}, False),
+                ("wide", None, dict(block_m_base=32, down_ksplit=4), False),
+                ("tiles", dict(T=300, H=320, I=448, E=4, top_k=2, L=3, r=32), dict(block_m_base=128), False),
+                ("tiles", dict(T=300, H=320, I=448, E=4, top_k=2, L=3, r=32), dict(block_m_base=256), False),
+                ("tiles", dict(T=300, H=320, I=448, E=4, top_k=2, L=3, r=32), dict(block_m_base=64), False)]
 
 
 @pytest.mark.parametrize("name,dims,launch,shrink_launch", PACKED_CASES)
@@ -534,14 +539,22 @@ def test_packed_weights_give_bitwise_equal_output(dev, name, dims, launch, shrin
     log(f"packed weights {name} {dims or ''} {launch} shrink_launch={shrink_launch}")
     case = build_case(name, dims=dims, touched_only=False)
     t = wl.device_tensors(case, dev)
-    outs = []
-    for packed in (False, True):
-        layer = ml.Layer(case.T, case.H, case.I, case.E, case.top_k, case.L, case.r, t["w_gate_up"], t["w_down"],
-                         t["a_gate_up"], t["b_gate_up"], t["a_down"], t["b_down"], shrink_launch=shrink_launch,
-                         packed_weights=packed, **launch)
-        outs.append(layer(t["x"], t["logits"], t["adapter_ids"]))
+    launch = dict(launch)
+    bm = launch.pop("block_m_base", 0)
+    layer = ml.Layer(case.T, case.H, case.I, case.E, case.top_k, case.L, case.r, t["w_gate_up"], t["w_down"],
+                     t["a_gate_up"], t["b_gate_up"], t["a_down"], t["b_down"], shrink_launch=shrink_launch,
+                     block_m_base=bm, **launch)
+    ref = layer(t["x"], t["logits"], t["adapter_ids"])
+    # the same call with packed copies in the weights struct
+    gp, dp = torch.empty_like(t["w_gate_up"]), torch.empty_like(t["w_down"])
+    ml.pack_weights(layer.desc, t["w_gate_up"], t["w_down"], gp, dp)
+    w = layer.weights
+    both = ml.Weights(w.w_gate_up, w.w_down, w.a_gate_up, w.b_gate_up, w.a_down, w.b_down, gp.data_ptr(),
+                      dp.data_ptr())
+    out = torch.empty_like(ref)
+    ml.forward(layer.desc, both, t["x"], t["logits"], t["adapter_ids"], out, layer.workspace)
     torch.cuda.synchronize()
-    assert torch.equal(outs[0], outs[1])
+    assert torch.equal(ref, out)
 
 
 def test_layer_parity_packed_weights(dev):

@@ -70,7 +70,7 @@ def label(kernel_name: str) -> str | None:
             "k_align_hist": "align_hist", "k_align_colscan": "align_colscan",
             "k_align_offsets": "align_offsets", "k_align_scatter_g": "align_scatter",
             "k_shrink": "shrink", "k_combine": "combine", "k_gather_f32": "gather_f32",
-            "k_gather_bf16": "gather_bf16"}.get(fn, fn)
+            "k_gather_bf16": "gather_bf16", "k_pack_skinny": "pack_weights (setup)"}.get(fn, fn)
 
 
 def _short(kernel_name: str) -> str:

@@ -48,7 +48,7 @@ def split_candidates(case, plan):
     return out
 
 
-def time_choice(case, copies, out, choice, steps, warmup, launch=None):
+def time_choice(case, copies, out, choice, steps, warmup, launch=None, packed=True):
     import torch
     bm_b, bm_l, sep = choice
     layers = []
@@ -56,7 +56,7 @@ def time_choice(case, copies, out, choice, steps, warmup, launch=None):
         layers.append(ml.Layer(case.T, case.H, case.I, case.E, case.top_k, case.L, case.r,
                                t["w_gate_up"], t["w_down"], t["a_gate_up"], t["b_gate_up"],
                                t["a_down"], t["b_down"], block_m_base=bm_b, block_m_lora=bm_l,
-                               shrink_launch=sep, **(launch or {})))
+                               shrink_launch=sep, packed_weights=packed, **(launch or {})))
 
     def step(i):
         t = copies[i % len(copies)]
@@ -85,7 +85,9 @@ def time_choice(case, copies, out, choice, steps, warmup, launch=None):
     return sorted(reps)[1]
 
 
-def tune_workload(name, folder, rotate=3, steps=None):
+def tune_workload(name, folder, rotate=3, steps=None, packed=True):
+    """packed: time every choice with packed weight copies (as the bench
+    runs the 16-row kernels); False: the row layout only."""
     import torch
     dev = torch.device("cuda:0")
     case = wl.make_case(name)
@@ -100,7 +102,7 @@ def tune_workload(name, folder, rotate=3, steps=None):
                          ml.FLAG_SHRINK_LAUNCH if choice[2] else 0)
         if ml.validate(d) != ml.OK:
             continue
-        us = time_choice(case, copies, out, choice, steps, warmup=2 if heavy else 5)
+        us = time_choice(case, copies, out, choice, steps, warmup=2 if heavy else 5, packed=packed)
         print(json.dumps({"workload": name, "block_m_base": choice[0], "block_m_lora": choice[1],
                           "shrink_launch": choice[2], "us": None if us is None else round(us, 2)}),
               flush=True)
@@ -124,7 +126,8 @@ def tune_workload(name, folder, rotate=3, steps=None):
                              flags, **trial)
             if ml.validate(d) != ml.OK:
                 continue
-            us_v = time_choice(case, copies, out, best, steps, warmup=2 if heavy else 5, launch=trial)
+            us_v = time_choice(case, copies, out, best, steps, warmup=2 if heavy else 5, launch=trial,
+                               packed=packed)
             print(json.dumps({"workload": name, "block_m_base": best[0], "block_m_lora": best[1],
                               "shrink_launch": best[2], **trial,
                               "us": None if us_v is None else round(us_v, 2)}), flush=True)
@@ -148,10 +151,12 @@ def main():
     ap.add_argument("--workload", action="append", choices=list(wl.CONFIGS), required=True)
     ap.add_argument("--out", default=tuning.DEFAULT_FOLDER)
     ap.add_argument("--steps", type=int, default=0)
+    ap.add_argument("--row-layout", action="store_true",
+                    help="time without packed weight copies (the bench gives them to 16-row plans)")
     args = ap.parse_args()
     t0 = time.time()
     for name in args.workload:
-        tune_workload(name, args.out, steps=args.steps or None)
+        tune_workload(name, args.out, steps=args.steps or None, packed=not args.row_layout)
     print(f"tuned {len(args.workload)} workload(s) in {time.time() - t0:.0f}s", file=sys.stderr)
 
 

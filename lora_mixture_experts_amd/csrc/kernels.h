@@ -26,9 +26,9 @@ hipError_t launch_align(const int32_t* topk_ids, const int32_t* adapter_ids, int
                         int32_t* sorted_l, int32_t* blk_e_l, int32_t* blk_a_l, int32_t* n_l,
                         int32_t* slot_of_pair, int32_t* lslot_of_pair, int32_t* slot_adapter,
                         int32_t* defer, hipStream_t s);
-// ints of workspace the alignment of P pairs may use: the one-workgroup path
-// to split its scatter off, the multi-launch path for its histograms and
-// segment starts (which it needs)
+// ints of workspace the alignment of P pairs uses: the per-range key counts
+// and each pair's key and rank, or the multi-launch path's histograms and
+// segment starts
 int align_defer_ints(int P, int E, int L);
 
 // ---- LoRA shrink ----------------------------------------------------------

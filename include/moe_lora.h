@@ -190,14 +190,16 @@ int moe_lora_route(const moe_lora_desc *d, const float *logits, int32_t *topk_id
  *   n_b      i32 [1]          used length of sorted_b
  *   sorted_l i32 [C_l], blk_e_l, blk_a_l i32 [C_l/BMl], n_l i32 [1]: LoRA view
  *   workspace  device buffer of >= moe_lora_workspace_bytes() bytes, 256-byte
- *              aligned, or NULL. Up to E*(L+1) = 9712 keys one workgroup does
- *              the counting and NULL is accepted (large batches then scatter
- *              in that workgroup too, more slowly). Above that, up to 36864
+ *              aligned, or NULL. Up to E*(L+1) = 9712 keys: with a workspace,
+ *              batches of more than 256 pairs count their keys per range on
+ *              many workgroups (the counts and each pair's rank live in the
+ *              workspace); NULL is accepted and one workgroup then does all
+ *              of it, more slowly for large batches. Above that, up to 36864
  *              keys (e.g. 256 experts x 128 adapters), the counting is spread
  *              over several launches whose histograms live in the workspace:
  *              NULL is then MOE_LORA_EWORKSPACE.
  * The result is deterministic (no order-dependent atomics) and the same on
- * both paths.
+ * every path.
  * Limit: E*(L+1) <= 36864 and T*top_k <= 2^24. */
 int moe_lora_align(const moe_lora_desc *d, const int32_t *topk_ids, const int32_t *adapter_ids,
                    int32_t *sorted_b, int32_t *blk_e_b, int32_t *n_b,

@@ -76,6 +76,11 @@ extern "C" {
  *                                   of its own rows (the path a wait that runs
  *                                   out takes; same results to rounding,
  *                                   slower; for tests of that path)
+ *     MOE_LORA_FLAG_ROUTE_LAUNCH    keep the routing and alignment launches
+ *                                   where the library would route the batch
+ *                                   inside the gate_up launch (decode-sized
+ *                                   batches, see moe_lora_plan_info; same
+ *                                   results to rounding; for comparison)
  *   any other bit is an error.
  *   Launch tuning (0 = the library's choice; any valid value computes the
  *   same layer up to the order of fp32 sums; these are what a per-shape
@@ -95,6 +100,7 @@ extern "C" {
 #define MOE_LORA_FLAG_SHRINK_LAUNCH 2
 #define MOE_LORA_FLAG_FUSED_COMBINE 4
 #define MOE_LORA_FLAG_NO_SHRINK_WAIT 8
+#define MOE_LORA_FLAG_ROUTE_LAUNCH 16
 typedef struct moe_lora_desc {
     int32_t T, H, I, E, top_k, L, r;
     int32_t block_m_base, block_m_lora;
@@ -151,11 +157,20 @@ int moe_lora_block_sizes(const moe_lora_desc *d, int32_t *block_m_base, int32_t 
 /* The launch choices the library makes for this descriptor (0 defaults
  * resolved): base / LoRA block rows, down K ranges, shrink K ranges (0 when
  * L == 0), waves per tile of the two 16-row projections (0 for other block
- * sizes), whether the shrinks run inside the projection launches, and
- * whether the combine runs in the down projection. Host only. */
+ * sizes), whether the shrinks run inside the projection launches, whether
+ * the combine runs in the down projection, and routing_in_gate_up: 0 = the
+ * routing and alignment have launches of their own; 1 = the gate_up launch
+ * aligns the batch itself from the routing launch's picks (no alignment
+ * launch); 2 = it also routes the batch from the logits (no routing launch
+ * either; where E top_k <= 32). 1 and 2 apply to decode-sized batches:
+ * T <= 16, E <= 32, top_k <= 8, T top_k <= 64, 16-row blocks, the shrinks
+ * inside the projections or no LoRA, one wave per gate_up tile. The routing
+ * and alignment are then written by that launch's first workgroup, in the
+ * same layouts. Host only. */
 typedef struct moe_lora_plan_info {
     int32_t block_m_base, block_m_lora, down_ksplit, shrink_ksplit;
     int32_t waves_gate_up, waves_down, shrinks_in_projections, combine_in_down;
+    int32_t routing_in_gate_up;
 } moe_lora_plan_info;
 int moe_lora_plan(const moe_lora_desc *d, moe_lora_plan_info *info);
 

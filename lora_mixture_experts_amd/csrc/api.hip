@@ -10,6 +10,7 @@
 
 #include "../../include/moe_lora.h"
 #include "kernels.h"
+#include "local_route.h"
 
 using namespace moelora;
 
@@ -28,6 +29,8 @@ struct Plan {
     int ksw_gu, ksw_dn;  // 16-row blocks: waves per tile of the two projections
     bool fused;  // the shrinks run as producer waves inside the projection launches
     bool fuse_combine;  // the down projection adds its weighted rows into out (no D, no combine launch)
+    bool local;  // the gate_up launch aligns the batch itself (no alignment launch)
+    bool local_route;  // ... and routes it too (no routing launch)
     size_t off_ids, off_w, off_sorted_b, off_blk_e_b, off_counts, off_sorted_l, off_blk_e_l,
         off_blk_a_l, off_slot, off_lslot, off_sad, off_defer, off_s1, off_s2, off_s1hl, off_s2hl,
         off_h, off_d, total;
@@ -35,6 +38,12 @@ struct Plan {
 };
 
 int roundup_i(long v, long m) { return static_cast<int>((v + m - 1) / m * m); }
+
+// Where a decode-sized batch is aligned inside the gate_up launch, that
+// launch also routes it when each wave's top-k scan (E x top_k steps per
+// token) is this short; longer scans cost the launch more than the routing
+// launch takes, and the routing launch stays.
+constexpr int kLocalRouteMaxWork = 32;
 
 int default_bm_base(int P, int E) {
     if (E == 1) {  // no routing: the one expert holds all P rows
@@ -71,7 +80,7 @@ int check_desc(const moe_lora_desc* d) {
     if (d->L > 0 && !(d->r == 8 || d->r == 16 || d->r == 32 || d->r == 64 || d->r == 128))
         return MOE_LORA_EINVAL;
     if (d->flags & ~(MOE_LORA_FLAG_OUT_BF16 | MOE_LORA_FLAG_SHRINK_LAUNCH | MOE_LORA_FLAG_FUSED_COMBINE |
-                     MOE_LORA_FLAG_NO_SHRINK_WAIT))
+                     MOE_LORA_FLAG_NO_SHRINK_WAIT | MOE_LORA_FLAG_ROUTE_LAUNCH))
         return MOE_LORA_EINVAL;
     if ((d->flags & MOE_LORA_FLAG_FUSED_COMBINE) && (d->flags & MOE_LORA_FLAG_OUT_BF16)) return MOE_LORA_EINVAL;
     if (d->block_m_base != 0 && !pow2_in(d->block_m_base, 16, 256)) return MOE_LORA_EINVAL;
@@ -127,6 +136,14 @@ int make_plan(const moe_lora_desc* d, Plan* p) {
         const long units = static_cast<long>(p->nblk_l) * ((p->r + 15) / 16) * ss;
         p->fused = units <= kMaxProducerUnits;
     }
+    // decode-sized batches with 16-row blocks: every wave of the gate_up
+    // launch routes the batch itself from the logits, so that the launch
+    // streams weights while the routing is worked out; the routing and
+    // alignment launches (about 11 us of a 300 us decode-shaped call) drop
+    // out
+    p->local = p->bm_b == 16 && p->bm_l == 16 && local_route_fits(p->T, p->E, p->k) && p->ksw_gu == 1 &&
+               (p->L == 0 || p->fused) && !(d->flags & MOE_LORA_FLAG_ROUTE_LAUNCH);
+    p->local_route = p->local && static_cast<long>(p->E) * p->k <= kLocalRouteMaxWork;
     if (p->fused) {
         p->ssplit = std::max(producer_ksplit(p->H), producer_ksplit(p->I));
         if (d->shrink_ksplit && d->shrink_ksplit != p->ssplit) return MOE_LORA_EINVAL;
@@ -246,6 +263,7 @@ int moe_lora_plan(const moe_lora_desc* d, moe_lora_plan_info* info) {
     info->waves_down = p.bm_b == 16 ? p.ksw_dn : 0;
     info->shrinks_in_projections = p.fused ? 1 : 0;
     info->combine_in_down = p.fuse_combine ? 1 : 0;
+    info->routing_in_gate_up = p.local_route ? 2 : p.local ? 1 : 0;
     return MOE_LORA_OK;
 }
 
@@ -358,6 +376,7 @@ int forward_planned(const Plan& p, const moe_lora_desc* d, const moe_lora_weight
         const bool shrink_launched = p.L > 0 && !p.fused;
         uint8_t* l = &g_timing.launched[static_cast<size_t>(call) * MOE_LORA_NKERNELS];
         l[2] = l[4] = shrink_launched ? 1 : 0;  // shrink_gate_up, shrink_down
+        l[1] = p.local ? 0 : 1;                 // align (with local routing, "route" times the clearing launch)
         l[6] = p.fuse_combine ? 0 : 1;          // combine
     }
 
@@ -367,12 +386,21 @@ int forward_planned(const Plan& p, const moe_lora_desc* d, const moe_lora_weight
     // counts[0..1]: n_b, n_l (alignment); counts[2..3]: producer counts of
     // the two projections; counts[4]: the call's status word; 2..4 are
     // zeroed by the routing launch
-    ok(launch_route(logits, p.T, p.E, p.k, ids, tw, s, counts + 2, 3,
-                    p.fuse_combine ? static_cast<float*>(out) : nullptr, p.H));
-    timing_mark(call, 1, s);
-    ok(launch_align(ids, adapter_ids, p.T, p.k, p.E, p.L, p.bm_b, p.bm_l, p.C_b, p.C_l, sorted_b,
-                    blk_e_b, counts, sorted_l, blk_e_l, blk_a_l, counts + 1, slot, lslot, sad,
-                    at<int32_t>(workspace, p.off_defer), s));
+    if (p.local_route) {
+        ok(launch_zero(counts + 2, 3, p.fuse_combine ? static_cast<float*>(out) : nullptr, p.T, p.H, s));
+        timing_mark(call, 1, s);
+    } else if (p.local) {
+        ok(launch_route(logits, p.T, p.E, p.k, ids, tw, s, counts + 2, 3,
+                        p.fuse_combine ? static_cast<float*>(out) : nullptr, p.H));
+        timing_mark(call, 1, s);
+    } else {
+        ok(launch_route(logits, p.T, p.E, p.k, ids, tw, s, counts + 2, 3,
+                        p.fuse_combine ? static_cast<float*>(out) : nullptr, p.H));
+        timing_mark(call, 1, s);
+        ok(launch_align(ids, adapter_ids, p.T, p.k, p.E, p.L, p.bm_b, p.bm_l, p.C_b, p.C_l, sorted_b,
+                        blk_e_b, counts, sorted_l, blk_e_l, blk_a_l, counts + 1, slot, lslot, sad,
+                        at<int32_t>(workspace, p.off_defer), s));
+    }
     timing_mark(call, 2, s);
 
     ShrinkArgs sa{};
@@ -408,7 +436,17 @@ int forward_planned(const Plan& p, const moe_lora_desc* d, const moe_lora_weight
         ga.status = counts + 4;
         ga.max_polls = (d->flags & MOE_LORA_FLAG_NO_SHRINK_WAIT) ? 0 : kMaxProducerPolls;
     }
+    if (p.local) {
+        // expert-indexed blocks; the launch's first workgroup writes the
+        // routing and alignment for the launches below
+        ga.local = 1; ga.adapter_ids = adapter_ids; ga.T = p.T; ga.n_blocks = p.E;
+        if (p.local_route) ga.logits = logits;
+        else ga.local_ids = ids;
+        ga.pub = LocalOut{ids, tw, sorted_b, blk_e_b, counts, sorted_l, blk_e_l, blk_a_l, counts + 1,
+                          slot, lslot, sad, p.C_b, p.C_l};
+    }
     ok(launch_gemm(ga, s));
+    ga.local = 0; ga.logits = nullptr; ga.local_ids = nullptr; ga.adapter_ids = nullptr; ga.n_blocks = p.nblk_b;
     timing_mark(call, 4, s);
 
     if (p.L > 0 && !p.fused) {

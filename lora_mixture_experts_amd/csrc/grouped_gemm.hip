@@ -23,6 +23,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "local_route.h"
 
 namespace moelora {
 
@@ -128,6 +129,41 @@ __device__ __forceinline__ u32x4 load_lora_b(const GemmArgs& a, int Nw, int ad, 
 // call's status word, so every wave ends and the output is valid whatever the
 // dispatch order.
 
+// 16 x 16 block of X . A^T over 64-wide K chunks [q0, q1): xrow / arow are
+// this lane's X row and A row at element 16 (lane / 16); two chunks in flight.
+__device__ __forceinline__ f32x4 producer_dot(const uint16_t* xrow, const uint16_t* arow, int q0, int q1) {
+    const int n = q1 - q0;
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    u32x4 xb[2][2], wb[2][2];
+    auto load = [&](int buf, int q) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            xb[buf][h] = ld16(xrow + q * 64 + 8 * h);
+            wb[buf][h] = ld16(arow + q * 64 + 8 * h);
+        }
+    };
+    auto compute = [&](int buf) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) acc = mfma16x16x32(xb[buf][h], wb[buf][h], acc);
+    };
+    if (n > 0) {
+        load(0, q0);
+        int q = q0;
+        for (int i = 0; i + 1 < n; i += 2, q += 2) {
+            load(1, q + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(0);
+            __builtin_amdgcn_sched_barrier(0);
+            load(0, min(q + 2, q1 - 1));
+            __builtin_amdgcn_sched_barrier(0);
+            compute(1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (n & 1) compute(0);
+    }
+    return acc;
+}
+
 // One producer unit: the 16 S columns cf of LoRA-view block bl over K range ks,
 // for every real row of the block. Once all of its stores have completed, the
 // unit counts itself in a.done.
@@ -146,7 +182,7 @@ __device__ __forceinline__ void shrink_producer(const GemmArgs& a, int unit) {
     const uint16_t* arow =
         a.Al + ((static_cast<size_t>(ad) * a.E + e) * a.r + (j < a.r ? j : j - 8)) * K + kc * 16;
     const int nqa = K / 64;
-    const int q0 = ks * nqa / a.s_split, q1 = (ks + 1) * nqa / a.s_split, n = q1 - q0;
+    const int q0 = ks * nqa / a.s_split, q1 = (ks + 1) * nqa / a.s_split;
     const int base = bl * a.bm_l;
     const int p_first = a.sorted_l[base];
     for (int fm = 0; fm < a.bm_l / 16; ++fm) {
@@ -157,34 +193,7 @@ __device__ __forceinline__ void shrink_producer(const GemmArgs& a, int unit) {
         const size_t xr = a.gather_token ? static_cast<size_t>(p / a.top_k)
                                          : static_cast<size_t>(a.slot_of_pair[p]);
         const uint16_t* xrow = a.X + xr * K + kc * 16;
-        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-        u32x4 xb[2][2], wb[2][2];
-        auto load = [&](int buf, int q) {
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                xb[buf][h] = ld16(xrow + q * 64 + 8 * h);
-                wb[buf][h] = ld16(arow + q * 64 + 8 * h);
-            }
-        };
-        auto compute = [&](int buf) {
-#pragma unroll
-            for (int h = 0; h < 2; ++h) acc = mfma16x16x32(xb[buf][h], wb[buf][h], acc);
-        };
-        if (n > 0) {
-            load(0, q0);
-            int q = q0;
-            for (int i = 0; i + 1 < n; i += 2, q += 2) {
-                load(1, q + 1);
-                __builtin_amdgcn_sched_barrier(0);
-                compute(0);
-                __builtin_amdgcn_sched_barrier(0);
-                load(0, min(q + 2, q1 - 1));
-                __builtin_amdgcn_sched_barrier(0);
-                compute(1);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            if (n & 1) compute(0);
-        }
+        const f32x4 acc = producer_dot(xrow, arow, q0, q1);
         if (j < a.r) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -200,6 +209,40 @@ __device__ __forceinline__ void shrink_producer(const GemmArgs& a, int unit) {
     // stores to complete orders them before the count. An agent-scope release
     // fence would also write back this XCD's whole L2; with 128 producer waves
     // that measured about 10 us more per decode-shaped layer call.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (lane == 0) __hip_atomic_fetch_add(a.done, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The same unit on a decode-sized gate_up launch that routes the batch itself
+// (GemmArgs::logits): the block's expert, adapter and rows come from the
+// wave's own routing and alignment of the batch (16-row LoRA blocks, one per
+// (expert, adapter) segment).
+__device__ __forceinline__ void shrink_producer_local(const GemmArgs& a, int unit, float* ls) {
+    const int lane = threadIdx.x & 63;
+    const int kc = lane >> 4;
+    const int cf = unit % a.prod_ncf, rest = unit / a.prod_ncf;
+    const int ks = rest % a.s_split, bl = rest / a.s_split;
+    int e = 0, ad = 0, row_p, row_slot;
+    if (!local_lora_rows(a.logits, a.adapter_ids, a.T, a.E, a.top_k, a.L, bl, ls, a.local_ids, e, ad, row_p,
+                         row_slot))
+        return;  // past the used blocks: not counted
+    const int K = a.K;
+    const int j = cf * 16 + (lane & 15);
+    const uint16_t* arow =
+        a.Al + ((static_cast<size_t>(ad) * a.E + e) * a.r + (j < a.r ? j : j - 8)) * K + kc * 16;
+    const int nqa = K / 64;
+    const int q0 = ks * nqa / a.s_split, q1 = (ks + 1) * nqa / a.s_split;
+    // padding rows re-read the block's first row (lane 0 holds row 0)
+    const int p = row_p >= 0 ? row_p : __builtin_amdgcn_readlane(row_p, 0);
+    const uint16_t* xrow = a.X + static_cast<size_t>(p / a.top_k) * K + kc * 16;
+    const f32x4 acc = producer_dot(xrow, arow, q0, q1);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int rp = __shfl(row_p, 4 * kc + i), rs = __shfl(row_slot, 4 * kc + i);
+        if (j < a.r && rp >= 0)
+            __hip_atomic_store(&a.S_out[(static_cast<size_t>(ks) * a.C_b + rs) * a.r + j], acc[i], __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     if (lane == 0) __hip_atomic_fetch_add(a.done, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -307,21 +350,37 @@ __device__ __forceinline__ void expand_own_shrink(const GemmArgs& a, int e, int 
 template <bool GATEUP, int FN, int NS, int KSW, bool PAIR>
 __global__ __launch_bounds__(64 * KSW) void k_gemm_skinny(GemmArgs a) {
     const int w = KSW > 1 ? wave_id() : 0;
-    // 1-D grid: producer workgroups first (one producer unit per wave), then
-    // (column tile, block, K range) with the tile fastest
+    // 1-D grid: [the routing workgroup,] producer workgroups (one producer
+    // unit per wave), then (column tile, block, K range) with the tile fastest.
+    // Local routing (one-wave workgroups only): every wave routes the batch
+    // itself, with the logits staged in LDS.
+    __shared__ float local_ls[GATEUP && KSW == 1 ? kLocalMaxT * kLocalMaxE : 1];
     int wg = blockIdx.x;
+    const bool local = GATEUP && KSW == 1 && a.local;
+    if (local) {
+        if (wg == 0) {
+            // routing and alignment for the launches after this one
+            local_publish(a.logits, a.adapter_ids, a.T, a.E, a.top_k, a.L, local_ls, a.local_ids, a.pub);
+            return;
+        }
+        --wg;
+    }
     const int prod_wgs = (a.prod_units + KSW - 1) / KSW;
     if (wg < prod_wgs) {
         const int unit = wg * KSW + w;
-        if (unit < a.prod_units) shrink_producer(a, unit);
+        if (unit < a.prod_units) {
+            if (local) shrink_producer_local(a, unit, local_ls);
+            else shrink_producer(a, unit);
+        }
         return;
     }
     wg -= prod_wgs;
     constexpr int kCols = GATEUP ? FN * 8 : FN * 16;  // output columns per wave
     const int n_tiles = a.N_out / kCols;
-    const int tile = wg % n_tiles, b = (wg / n_tiles) % a.n_blocks;
+    const int tile = wg % n_tiles, bidx = (wg / n_tiles) % a.n_blocks;
     const int z = wg / n_tiles / a.n_blocks;  // K range (down only)
-    const int e = a.blk_e_b[b];
+    // with local routing, block index = expert (its slots are found below)
+    const int e = local ? bidx : a.blk_e_b[bidx];
     if (e < 0) return;
     const int lane = threadIdx.x & 63;
     const int g = lane >> 4, lrow = lane & 15;
@@ -335,19 +394,23 @@ __global__ __launch_bounds__(64 * KSW) void k_gemm_skinny(GemmArgs a) {
     const int q0 = w * (Kp / 64) / KSW, q1 = (w + 1) * (Kp / 64) / KSW;
     const int kbeg = z * Kp + q0 * 64;
 
-    const int slot = b * 16 + lrow;
-    // Padding rows (sentinel P) re-read the block's first row, which is always
-    // a real row: the duplicate addresses merge into the same memory request,
-    // MFMA output rows depend only on their own A row, and padding rows are
-    // never consumed, so no masking is needed and every load is issued
-    // unconditionally (exact wait counts).
-    const uint16_t* xrow;
-    if (GATEUP) {
-        int p = a.sorted_b[slot];
-        if (p >= a.P) p = a.sorted_b[b * 16];
-        xrow = a.X + static_cast<size_t>(p / a.top_k) * K + kbeg + g * 16;
-    } else {
-        xrow = a.X + static_cast<size_t>(slot) * K + kbeg + g * 16;
+    // The block's first slot and this lane's activation row. Padding rows
+    // (sentinel P) re-read the block's first row, which is always a real row:
+    // the duplicate addresses merge into the same memory request, MFMA output
+    // rows depend only on their own A row, and padding rows are never
+    // consumed, so no masking is needed and every load is issued
+    // unconditionally (exact wait counts). With local routing both are known
+    // only after the routing below.
+    int b16 = bidx * 16, row_ad = 0, local_target = 0;
+    const uint16_t* xrow = nullptr;
+    if (!local) {
+        if (GATEUP) {
+            int p = a.sorted_b[b16 + lrow];
+            if (p >= a.P) p = a.sorted_b[b16];
+            xrow = a.X + static_cast<size_t>(p / a.top_k) * K + kbeg + g * 16;
+        } else {
+            xrow = a.X + static_cast<size_t>(b16 + lrow) * K + kbeg + g * 16;
+        }
     }
     // Weight operand: the 64 rows of the tile at the matrix pitch, or the
     // packed copy, where the tile's 64-wide K chunk q is one 8 KiB block
@@ -376,15 +439,37 @@ __global__ __launch_bounds__(64 * KSW) void k_gemm_skinny(GemmArgs a) {
 #pragma unroll
     for (int f = 0; f < FN; ++f) acc[f] = f32x4{0.f, 0.f, 0.f, 0.f};
     u32x4 xb[NS][2], wb[NS][FN][2];
-    auto load = [&](int buf, int q) {
-        const int k0 = q * 64;
+    auto loadx = [&](int buf, int q) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h) xb[buf][h] = ld16(xrow + k0 + 8 * h);
+        for (int h = 0; h < 2; ++h) xb[buf][h] = ld16(xrow + q * 64 + 8 * h);
+    };
+    auto loadw = [&](int buf, int q) {
 #pragma unroll
         for (int f = 0; f < FN; ++f)
 #pragma unroll
             for (int h = 0; h < 2; ++h) wb[buf][f][h] = ld16(wrow[f] + static_cast<size_t>(q) * wq + h * wh);
     };
+    auto load = [&](int buf, int q) {
+        loadx(buf, q);
+        loadw(buf, q);
+    };
+    const int nq = q1 - q0;
+    if (local) {
+        // the first weight chunks stream while the wave routes the batch
+#pragma unroll
+        for (int st = 0; st + 1 < NS; ++st) loadw(st, min(st, nq - 1));
+        int row_p, n_l;
+        b16 = local_expert_rows(a.logits, a.adapter_ids, a.T, a.E, a.top_k, a.L, e, local_ls, a.local_ids, row_p,
+                                row_ad, n_l);
+        local_target = (n_l / 16) * a.prod_ncf * a.s_split;
+        if (b16 < 0) {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no pair chose this expert
+            return;
+        }
+        const int p = row_p >= 0 ? row_p : __builtin_amdgcn_readlane(row_p, 0);
+        xrow = a.X + static_cast<size_t>(p / a.top_k) * K + kbeg + g * 16;
+    }
+    const int slot = b16 + lrow;
     auto compute = [&](int buf) {
 #pragma unroll
         for (int h = 0; h < 2; ++h)
@@ -392,9 +477,11 @@ __global__ __launch_bounds__(64 * KSW) void k_gemm_skinny(GemmArgs a) {
             for (int f = 0; f < FN; ++f) acc[f] = mfma16x16x32(xb[buf][h], wb[buf][f][h], acc[f]);
     };
 
-    const int nq = q1 - q0;
 #pragma unroll
-    for (int st = 0; st + 1 < NS; ++st) load(st, min(st, nq - 1));
+    for (int st = 0; st + 1 < NS; ++st) {
+        if (local) loadx(st, min(st, nq - 1));
+        else load(st, min(st, nq - 1));
+    }
     __builtin_amdgcn_sched_barrier(0);
 
     // LoRA expand: acc += S . B^T for every adapter present among the 16 rows
@@ -402,7 +489,7 @@ __global__ __launch_bounds__(64 * KSW) void k_gemm_skinny(GemmArgs a) {
     // separate launch it runs first, so its latency overlaps the first weight
     // loads; with the producers in this launch it runs after the base K loop.
     const bool lora = a.L > 0 && z == 0 && w == 0;
-    const int my_a = lora ? row_adapter(a, slot) : -1;
+    const int my_a = !lora ? -1 : local ? (row_ad < a.L ? row_ad : -1) : row_adapter(a, slot);
     // With the producers in this launch the expand runs part-way through or
     // after the base K loop, depending on when the producers finish; it then
     // accumulates into its own registers, added to the base result after the
@@ -496,7 +583,7 @@ __global__ __launch_bounds__(64 * KSW) void k_gemm_skinny(GemmArgs a) {
     // which set the launch's length, expand mid-stream (gate_up 191 -> 187 us).
     // The down projection expands after its loop: a poll half-way or three
     // quarters through measured 2-5 us slower there.
-    const int target = late ? producer_target(a) : 0;
+    const int target = !late ? 0 : local ? local_target : producer_target(a);
     const int q_mid = GATEUP ? nq / 2 / NS * NS : nq;
     bool expanded = !late;
 
@@ -551,7 +638,7 @@ __global__ __launch_bounds__(64 * KSW) void k_gemm_skinny(GemmArgs a) {
             for (int f = 0; f < FN; ++f) acc[f] += red[v][f][lane];
     }
 
-    const int orow0 = b * 16 + 4 * g;
+    const int orow0 = b16 + 4 * g;
     if (GATEUP) {
 #pragma unroll
         for (int u = 0; u < FN / 2; ++u) {
@@ -1365,7 +1452,11 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
         const int cols = a.gate_up ? kSkinnyFNGateUp * 8 : kSkinnyFNDown * 16;
         const int ksw = a.ksw;
         if (!(ksw == 1 || ksw == 2 || ksw == 4) || (a.K / a.ksplit) / 64 < ksw) return hipErrorInvalidValue;
-        const long total = static_cast<long>(a.N_out / cols) * a.n_blocks * a.ksplit + (a.prod_units + ksw - 1) / ksw;
+        if (a.local && (!a.gate_up || ksw != 1 || (a.L > 0 && a.bm_l != 16) || !local_route_fits(a.T, a.E, a.top_k) ||
+                        a.n_blocks != a.E || !a.adapter_ids || (!a.logits && !a.local_ids)))
+            return hipErrorInvalidValue;
+        const long total = static_cast<long>(a.N_out / cols) * a.n_blocks * a.ksplit +
+                           (a.prod_units + ksw - 1) / ksw + (a.local ? 1 : 0);
         if (total > 0x7fffffffL) return hipErrorInvalidValue;
         const dim3 grid(static_cast<unsigned>(total)), block(64 * ksw);
         // paired adapter runs where the grid holds at most two waves per SIMD

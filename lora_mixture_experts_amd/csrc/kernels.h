@@ -13,6 +13,11 @@ hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* ids, 
                         hipStream_t s, int32_t* zero_words = nullptr, int n_zero = 0,
                         float* zero_out = nullptr, int H = 0);
 
+// zero_words[0 .. n_zero) = 0 and, with zero_out, rows 0..T-1 of zero_out
+// [T][H] (fp32) = 0: what the routing launch clears, for calls that route
+// inside the gate_up launch.
+hipError_t launch_zero(int32_t* zero_words, int n_zero, float* zero_out, int T, int H, hipStream_t s);
+
 // Whether the alignment handles E experts x (L adapters + none) keys: in one
 // workgroup (its LDS holds the key counts with at least one histogram row),
 // or spread over several launches (up to 36864 keys).
@@ -73,6 +78,17 @@ inline int producer_ksplit(int K) {
     return s < 1 ? 1 : (s > kMaxProducerSplit ? kMaxProducerSplit : s);
 }
 
+// Where a launch that routes a decode-sized batch itself writes the routing
+// and alignment for the launches after it (the layouts of the routing and
+// alignment kernels' outputs).
+struct LocalOut {
+    int32_t* ids;
+    float* tw;
+    int32_t *sorted_b, *blk_e_b, *n_b, *sorted_l, *blk_e_l, *blk_a_l, *n_l;
+    int32_t *slot_of_pair, *lslot_of_pair, *slot_adapter;
+    int C_b, C_l;
+};
+
 // ---- grouped expert GEMM with fused LoRA expand (+ SwiGLU) ---------------
 struct GemmArgs {
     const uint16_t* X;        // gate_up: x [T][K]; down: h [C_b][K]
@@ -128,6 +144,19 @@ struct GemmArgs {
     const int32_t* n_l;           // padded LoRA-view length (live LoRA blocks x bm_l)
     int32_t* status;              // the call's status word (kStatus* bits), zero at launch
     int max_polls;                // polls of a projection wave waiting for the producers
+    // gate_up with 16-row blocks on a decode-sized batch (local_route_fits):
+    // with local set, every wave aligns the batch itself instead of reading
+    // the alignment: from local_ids (the routing launch's picks) when given,
+    // else routing it first from logits [T][E]; adapters from adapter_ids [T].
+    // Block b of the grid is expert b (n_blocks = E); workgroup 0 writes the
+    // alignment (and, from logits, the routing) to pub for the launches that
+    // follow
+    int local;
+    const float* logits;
+    const int32_t* local_ids;
+    const int32_t* adapter_ids;
+    int T;
+    LocalOut pub;
 };
 // status bit: a projection wave stopped waiting for the producers and
 // computed the shrink of its own rows (output valid, slower)

@@ -101,6 +101,24 @@ hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* ids, 
     return hipGetLastError();
 }
 
+__global__ __launch_bounds__(256) void k_zero(int32_t* __restrict__ zero_words, int n_zero,
+                                              float* __restrict__ zero_out, int T, int H) {
+    if (blockIdx.x == 0 && static_cast<int>(threadIdx.x) < n_zero) zero_words[threadIdx.x] = 0;
+    if (zero_out) {
+        const int t0 = blockIdx.x * 4, nt = min(4, T - t0);
+        f32x4* o = reinterpret_cast<f32x4*>(zero_out + static_cast<size_t>(t0) * H);
+        for (int i = threadIdx.x; i < nt * H / 4; i += 256) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+}
+
+hipError_t launch_zero(int32_t* zero_words, int n_zero, float* zero_out, int T, int H, hipStream_t s) {
+    if (n_zero < 0 || n_zero > 256 || (n_zero > 0 && !zero_words)) return hipErrorInvalidValue;
+    if (zero_out && (T <= 0 || H <= 0 || H % 4)) return hipErrorInvalidValue;
+    const int blocks = zero_out ? (T + 3) / 4 : 1;
+    hipLaunchKernelGGL(k_zero, dim3(blocks), dim3(256), 0, s, zero_words, n_zero, zero_out, T, H);
+    return hipGetLastError();
+}
+
 // ---------------------------------------------------------------------------
 // Align. key(p) = e * (L+1) + a',  a' = adapter if in [0,L) else L.
 // The result is a stable counting sort of the pairs by key: within a key the

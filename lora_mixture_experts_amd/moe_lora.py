@@ -18,6 +18,7 @@ FLAG_OUT_BF16 = 1
 FLAG_SHRINK_LAUNCH = 2
 FLAG_FUSED_COMBINE = 4
 FLAG_NO_SHRINK_WAIT = 8
+FLAG_ROUTE_LAUNCH = 16
 NKERNELS = 7
 
 
@@ -36,7 +37,7 @@ class Desc(ctypes.Structure):
 class PlanInfo(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("block_m_base", "block_m_lora", "down_ksplit", "shrink_ksplit", "waves_gate_up",
-                 "waves_down", "shrinks_in_projections", "combine_in_down")]
+                 "waves_down", "shrinks_in_projections", "combine_in_down", "routing_in_gate_up")]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}
@@ -258,13 +259,15 @@ class Layer:
     def __init__(self, T, H, I, E, top_k, L, r, w_gate_up, w_down, a_gate_up=None, b_gate_up=None,
                  a_down=None, b_down=None, block_m_base=0, block_m_lora=0, out_bf16=False,
                  shrink_launch=False, tuning=None, fused_combine=False, no_shrink_wait=False,
-                 packed_weights=False, **launch):
+                 packed_weights=False, route_launch=False, **launch):
         """tuning: a tuning.Table; when it holds a choice for this shape and
         token count it sets the block sizes, the shrink placement and the
         launch tuning fields (only if none of them is given explicitly).
         packed_weights: where the plan uses 16-row base blocks, also hold
         packed copies of the base weights, which those kernels then read
         (twice the base weight memory; self.packed says whether it did).
+        route_launch: keep the routing and alignment launches where the
+        library would route a decode-sized batch inside the gate_up launch.
         launch: any of TUNING_FIELDS (0 = the library's choice)."""
         import torch
         bad = set(launch) - set(TUNING_FIELDS)
@@ -283,7 +286,8 @@ class Layer:
                               (FLAG_OUT_BF16 if out_bf16 else 0) |
                               (FLAG_SHRINK_LAUNCH if shrink_launch else 0) |
                               (FLAG_FUSED_COMBINE if fused_combine else 0) |
-                              (FLAG_NO_SHRINK_WAIT if no_shrink_wait else 0), **launch)
+                              (FLAG_NO_SHRINK_WAIT if no_shrink_wait else 0) |
+                              (FLAG_ROUTE_LAUNCH if route_launch else 0), **launch)
         # the down projection's rows are kept (and readable) only when a
         # separate launch does the weighted combine
         self.keeps_down_rows = not fused_combine

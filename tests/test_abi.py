@@ -42,7 +42,7 @@ def desc(**over):
 @pytest.mark.parametrize("over", [dict(H=2881), dict(I=100), dict(top_k=0), dict(top_k=33, E=40),
                                   dict(top_k=5, E=4), dict(r=24), dict(E=0), dict(T=-1), dict(L=-1),
                                   dict(bm_b=48), dict(bm_b=8), dict(bm_l=512), dict(E=1025),
-                                  dict(E=128, L=300), dict(E=1024, L=36, top_k=8), dict(flags=16), dict(flags=5),
+                                  dict(E=128, L=300), dict(E=1024, L=36, top_k=8), dict(flags=32), dict(flags=5),
                                   dict(flags=-1), dict(flags=31)])
 def test_validate_rejects(over):
     assert ml.validate(desc(**over)) == ml.EINVAL
@@ -189,9 +189,23 @@ def test_plan_resolves_the_library_defaults():
     p = ml.plan(ml.make_desc(d["T"], d["H"], d["I"], d["E"], d["top_k"], d["L"], d["r"]))
     assert p["block_m_base"] == 16 and p["down_ksplit"] == 1 and p["waves_gate_up"] == 1
     assert p["shrinks_in_projections"] == 1 and p["combine_in_down"] == 0
+    # the decode-shaped batch is aligned inside the gate_up launch (its
+    # 4 x 32 top-k scan stays in the routing launch), unless the routing
+    # launch or separate shrink launches are asked for; the tiny layer's
+    # 2 x 8 scan runs inside the gate_up launch too
+    assert p["routing_in_gate_up"] == 1
+    tny = wl.CONFIGS["tiny"]
+    assert ml.plan(ml.make_desc(tny["T"], tny["H"], tny["I"], tny["E"], tny["top_k"], tny["L"],
+                                tny["r"]))["routing_in_gate_up"] == 2
+    args = (d["T"], d["H"], d["I"], d["E"], d["top_k"], d["L"], d["r"])
+    assert ml.plan(ml.make_desc(*args, flags=ml.FLAG_ROUTE_LAUNCH))["routing_in_gate_up"] == 0
+    assert ml.plan(ml.make_desc(*args, flags=ml.FLAG_SHRINK_LAUNCH))["routing_in_gate_up"] == 0
+    assert ml.plan(ml.make_desc(*args, waves_gate_up=2))["routing_in_gate_up"] == 0
+    assert ml.plan(ml.make_desc(17, *args[1:]))["routing_in_gate_up"] == 0  # T > 16
     d = wl.CONFIGS["prefill"]
     p = ml.plan(ml.make_desc(d["T"], d["H"], d["I"], d["E"], d["top_k"], d["L"], d["r"]))
     assert p["block_m_base"] == 128 and p["waves_down"] == 0 and p["shrinks_in_projections"] == 0
+    assert p["routing_in_gate_up"] == 0
 
 
 @pytest.mark.parametrize("over", [

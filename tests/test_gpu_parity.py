@@ -247,6 +247,56 @@ def check_layer(case, dev, bm=(0, 0), stages=False, stage_tokens=64, shrink_laun
     return out
 
 
+# Decode-sized batches are aligned inside the gate_up launch (every wave
+# derives its rows from the routing launch's picks, or routes the batch from
+# the logits itself where the top-k scan is short; the launch's first
+# workgroup writes the alignment, and then the routing). The same call with
+# the routing and alignment launches must give the same routing, alignment,
+# intermediates and output, bit for bit.
+LOCAL_CASES = [("tiny", {}, {}), ("decode", {}, {}), ("dense", {}, {}),
+               ("decode", {}, dict(fused_combine=True)), ("decode", {}, dict(no_shrink_wait=True)),
+               ("k8", dict(T=8, H=128, I=128, E=32, top_k=8, L=5, r=16), {}),
+               ("noL", dict(T=16, H=128, I=192, E=20, top_k=4, L=0, r=8), {}),
+               ("t1", dict(T=1, H=64, I=64, E=3, top_k=2, L=2, r=8), {}),
+               ("t13", dict(T=13, H=64, I=128, E=32, top_k=3, L=40, r=32), {}),
+               ("ties", dict(T=16, H=64, I=64, E=24, top_k=4, L=3, r=8), dict(ties=True))]
+
+
+@pytest.mark.parametrize("name,dims,opts", LOCAL_CASES)
+def test_routing_inside_gate_up_matches_routing_launches(dev, name, dims, opts):
+    log(f"local routing {name} {opts}")
+    opts = dict(opts)
+    ties = opts.pop("ties", False)
+    case = wl.make_case(name, dims=dims) if dims else wl.make_case(name)
+    if ties:  # coarse logits: many equal values, the lower expert id must win
+        case.logits[:] = np.round(case.logits * 2) / 2
+    t = wl.device_tensors(case, dev)
+    layers = [ml.Layer(case.T, case.H, case.I, case.E, case.top_k, case.L, case.r, t["w_gate_up"], t["w_down"],
+                       t["a_gate_up"], t["b_gate_up"], t["a_down"], t["b_down"], route_launch=rl, **opts)
+              for rl in (False, True)]
+    modes = [ml.plan(l.desc)["routing_in_gate_up"] for l in layers]
+    assert modes[0] in (1, 2) and modes[1] == 0
+    assert (modes[0] == 2) == (case.E * case.top_k <= 32)
+    outs = [l(t["x"], t["logits"], t["adapter_ids"]).cpu().numpy() for l in layers]
+    torch.cuda.synchronize()
+    assert all(l.status() == 0 for l in layers) or opts.get("no_shrink_wait")
+    if not opts.get("fused_combine"):  # fp32 atomics: the order of adds varies
+        np.testing.assert_array_equal(outs[0], outs[1])
+    st = [{k: (v.view(torch.int16) if v.dtype == torch.bfloat16 else v).cpu().numpy() for k, v in l.stages().items()}
+          for l in layers]
+    for key in st[1]:
+        np.testing.assert_array_equal(st[0][key].view(np.uint8), st[1][key].view(np.uint8), err_msg=key)
+    al = [{k: v.cpu().numpy() for k, v in l.alignment().items()} for l in layers]
+    for key in al[1]:
+        np.testing.assert_array_equal(al[0][key], al[1][key], err_msg=key)
+    # and the oracle's routing
+    ids, _ = oracle.route(case.logits, case.top_k)
+    np.testing.assert_array_equal(st[0]["topk_ids"].reshape(case.T, case.top_k), ids)
+    ref = oracle.forward(case, ids, oracle.route(case.logits, case.top_k)[1])
+    mx, mean = metrics(outs[0], ref)
+    assert mx <= MAX_TOL and mean <= MEAN_TOL, (mx, mean)
+
+
 def _table():
     from lora_mixture_experts_amd import tuning
     return tuning.load(tuning.DEFAULT_FOLDER)

@@ -224,8 +224,13 @@ __device__ __forceinline__ void shrink_producer_local(const GemmArgs& a, int uni
     const int ks = rest % a.s_split, bl = rest / a.s_split;
     int e = 0, ad = 0, row_p, row_slot;
     if (!local_lora_rows(a.logits, a.adapter_ids, a.T, a.E, a.top_k, a.L, bl, ls, a.local_ids, e, ad, row_p,
-                         row_slot))
-        return;  // past the used blocks: not counted
+                         row_slot)) {
+        // past the used blocks: counted all the same (the projection waves of
+        // such a launch wait for every unit, so that they need not know how
+        // many blocks are used)
+        if (lane == 0) __hip_atomic_fetch_add(a.done, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return;
+    }
     const int K = a.K;
     const int j = cf * 16 + (lane & 15);
     const uint16_t* arow =
@@ -458,10 +463,10 @@ __global__ __launch_bounds__(64 * KSW) void k_gemm_skinny(GemmArgs a) {
         // the first weight chunks stream while the wave routes the batch
 #pragma unroll
         for (int st = 0; st + 1 < NS; ++st) loadw(st, min(st, nq - 1));
-        int row_p, n_l;
+        int row_p;
         b16 = local_expert_rows(a.logits, a.adapter_ids, a.T, a.E, a.top_k, a.L, e, local_ls, a.local_ids, row_p,
-                                row_ad, n_l);
-        local_target = (n_l / 16) * a.prod_ncf * a.s_split;
+                                row_ad);
+        local_target = a.prod_units;  // every unit counts itself in this mode
         if (b16 < 0) {
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no pair chose this expert
             return;

@@ -178,34 +178,47 @@ __device__ __forceinline__ int local_row_in_expert(const TokenPicks& tp, int e, 
     return below;
 }
 
+// OR of x over the 64 lanes of a wave (DPP moves as in wave_prefix).
+__device__ __forceinline__ uint32_t wave_or(uint32_t x) {
+    int v = static_cast<int>(x);
+    v |= __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+    v |= __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+    v |= __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+    v |= __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+    v |= __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+    v |= __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31
+    return static_cast<uint32_t>(__builtin_amdgcn_readlane(v, 63));
+}
+
 // A gate_up projection wave on expert e (wave-uniform): the first slot of
 // e's base block (-1 if no token chose e); lane l gets the pair in row l & 15
-// and its adapter' (-1 and L for a padding row); n_l = LoRA-view length.
+// and its adapter' (-1 and L for a padding row). With at most 16 tokens
+// every used expert holds exactly one 16-row block, so e's block follows
+// those of the used experts below e. The rows pass through LDS (ls, also
+// the logits' staging area, no longer read by then).
 __device__ __forceinline__ int local_expert_rows(const float* logits, const int32_t* adapter_ids, int T, int E,
                                                  int k, int L, int e, float* ls, const int32_t* ids, int& row_p,
-                                                 int& row_ad, int& n_l) {
+                                                 int& row_ad) {
+    const int lane = threadIdx.x & 63;
     const TokenPicks tp = local_picks(logits, adapter_ids, T, E, k, L, ls, ids);
-    int cnt, n_b;
-    const int ebase = __builtin_amdgcn_readlane(local_expert_starts(tp.mask, T, E, cnt, n_b), e);
-    const uint32_t firsts = local_segment_firsts(tp, T, L);
-    n_l = 16 * __builtin_amdgcn_readlane(wave_prefix(__popc(firsts)), 63);
+    const uint32_t used = wave_or(tp.mask);
+    row_p = -1;
+    row_ad = L;
+    if (!((used >> e) & 1u)) return -1;
+    const int ebase = 16 * __popc(used & ((1u << e) - 1u));
     bool in_e;
     int j_of_e;
     const int row = local_row_in_expert(tp, e, L, in_e, j_of_e);
-    row_p = -1;
-    row_ad = L;
-    const uint64_t m = ballot64(in_e);
-    if (m == 0) return -1;
-    const int lrow = threadIdx.x & 15;
-#pragma unroll 1
-    for (uint64_t mm = m; mm; mm &= mm - 1) {
-        const int q = __ffsll(static_cast<long long>(mm)) - 1;
-        const int rq = __builtin_amdgcn_readlane(row, q), jq = __builtin_amdgcn_readlane(j_of_e, q);
-        const int aq = __builtin_amdgcn_readlane(tp.ad, q);
-        if (rq == lrow) {
-            row_p = q * k + jq;
-            row_ad = aq;
-        }
+    const int ne = popc64(ballot64(in_e));
+    int* rows = reinterpret_cast<int*>(ls);
+    if (in_e) {
+        rows[2 * row] = lane * k + j_of_e;
+        rows[2 * row + 1] = tp.ad;
+    }
+    const int lrow = lane & 15;
+    if (lrow < ne) {
+        row_p = rows[2 * lrow];
+        row_ad = rows[2 * lrow + 1];
     }
     return ebase;
 }

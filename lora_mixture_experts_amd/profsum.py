@@ -70,7 +70,9 @@ def label(kernel_name: str) -> str | None:
             "k_align_hist": "align_hist", "k_align_colscan": "align_colscan",
             "k_align_offsets": "align_offsets", "k_align_scatter_g": "align_scatter",
             "k_shrink": "shrink", "k_combine": "combine", "k_gather_f32": "gather_f32",
-            "k_gather_bf16": "gather_bf16", "k_pack_skinny": "pack_weights (setup)"}.get(fn, fn)
+            "k_gather_bf16": "gather_bf16", "k_pack_skinny": "pack_weights (setup)",
+            "k_align_one": "align", "k_align_count": "align_count", "k_align_place": "align_place",
+            "k_zero": "clear (routing in gate_up)"}.get(fn, fn)
 
 
 def _short(kernel_name: str) -> str:

@@ -459,22 +459,29 @@ __global__ __launch_bounds__(64 * KSW) void k_gemm_skinny(GemmArgs a) {
         loadw(buf, q);
     };
     const int nq = q1 - q0;
+    // With local routing the wave's 16 rows are the batch's tokens (row r =
+    // token r; rows past T re-read token 0): the loads start at once, and the
+    // routing, worked out while the first chunks stream, only decides which
+    // rows are stored and where (row_slot, -1 for a token that did not choose
+    // this expert).
+    int row_slot = -1;
     if (local) {
-        // the first weight chunks stream while the wave routes the batch
+        xrow = a.X + static_cast<size_t>(min(lrow, a.T - 1)) * K + kbeg + g * 16;
 #pragma unroll
-        for (int st = 0; st + 1 < NS; ++st) loadw(st, min(st, nq - 1));
-        int row_p;
-        b16 = local_expert_rows(a.logits, a.adapter_ids, a.T, a.E, a.top_k, a.L, e, local_ls, a.local_ids, row_p,
-                                row_ad);
+        for (int st = 0; st + 1 < NS; ++st) load(st, min(st, nq - 1));
+        bool in_row;
+        int s;
+        const bool any = local_token_rows(a.logits, a.adapter_ids, a.T, a.E, a.top_k, a.L, e, local_ls,
+                                          a.local_ids, in_row, s, row_ad);
         local_target = a.prod_units;  // every unit counts itself in this mode
-        if (b16 < 0) {
+        if (!any) {
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no pair chose this expert
             return;
         }
-        const int p = row_p >= 0 ? row_p : __builtin_amdgcn_readlane(row_p, 0);
-        xrow = a.X + static_cast<size_t>(p / a.top_k) * K + kbeg + g * 16;
+        if (in_row) row_slot = s;
+        else row_ad = a.L;
     }
-    const int slot = b16 + lrow;
+    const int slot = local ? max(row_slot, 0) : b16 + lrow;
     auto compute = [&](int buf) {
 #pragma unroll
         for (int h = 0; h < 2; ++h)
@@ -482,10 +489,9 @@ __global__ __launch_bounds__(64 * KSW) void k_gemm_skinny(GemmArgs a) {
             for (int f = 0; f < FN; ++f) acc[f] = mfma16x16x32(xb[buf][h], wb[buf][f][h], acc[f]);
     };
 
+    if (!local) {
 #pragma unroll
-    for (int st = 0; st + 1 < NS; ++st) {
-        if (local) loadx(st, min(st, nq - 1));
-        else load(st, min(st, nq - 1));
+        for (int st = 0; st + 1 < NS; ++st) load(st, min(st, nq - 1));
     }
     __builtin_amdgcn_sched_barrier(0);
 
@@ -645,13 +651,25 @@ __global__ __launch_bounds__(64 * KSW) void k_gemm_skinny(GemmArgs a) {
 
     const int orow0 = b16 + 4 * g;
     if (GATEUP) {
+        // output rows 4 g .. 4 g + 3 of this lane: their slots (local routing:
+        // the slots of those tokens' pairs, -1 for tokens that did not choose
+        // this expert; their rows are not stored)
+        int orow[4];
+        if (local) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) orow[i] = __shfl(row_slot, 4 * g + i);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) orow[i] = orow0 + i;
+        }
 #pragma unroll
         for (int u = 0; u < FN / 2; ++u) {
             const int col = c0 + 16 * u + lrow;
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                a.h_out[static_cast<size_t>(orow0 + i) * a.N_out + col] =
-                    f32_to_bf16_rne(silu(acc[2 * u][i]) * acc[2 * u + 1][i]);
+                if (orow[i] >= 0)
+                    a.h_out[static_cast<size_t>(orow[i]) * a.N_out + col] =
+                        f32_to_bf16_rne(silu(acc[2 * u][i]) * acc[2 * u + 1][i]);
         }
     } else if (a.out_acc) {
 #pragma unroll

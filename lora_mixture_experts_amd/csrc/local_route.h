@@ -223,6 +223,31 @@ __device__ __forceinline__ int local_expert_rows(const float* logits, const int3
     return ebase;
 }
 
+// A gate_up projection wave on expert e (wave-uniform) whose 16 MFMA rows
+// are the batch's tokens (row r = token r): lane l learns whether token l & 15
+// chose e, that pair's slot in e's base block and the token's adapter'.
+// Returns false when no token chose e. The activation loads do not wait for
+// this: the routing only decides which rows are stored, and where.
+__device__ __forceinline__ bool local_token_rows(const float* logits, const int32_t* adapter_ids, int T, int E,
+                                                 int k, int L, int e, float* ls, const int32_t* ids, bool& in_row,
+                                                 int& slot, int& ad) {
+    const TokenPicks tp = local_picks(logits, adapter_ids, T, E, k, L, ls, ids);
+    const uint32_t used = wave_or(tp.mask);
+    in_row = false;
+    slot = 0;
+    ad = L;
+    if (!((used >> e) & 1u)) return false;
+    const int ebase = 16 * __popc(used & ((1u << e) - 1u));
+    bool in_e;
+    int j_of_e;
+    const int row = local_row_in_expert(tp, e, L, in_e, j_of_e);
+    const int src = threadIdx.x & 15;
+    in_row = __shfl(in_e ? 1 : 0, src) != 0;  // tokens >= T have an empty mask
+    slot = ebase + __shfl(row, src);
+    ad = __shfl(tp.ad, src);
+    return true;
+}
+
 // LoRA-view block bl (wave-uniform): false past the used blocks; else its
 // expert and adapter, and lane l gets the pair in row l & 15 (-1: padding)
 // and that pair's base-view slot.

@@ -266,8 +266,8 @@ int moe_lora_forward(const moe_lora_desc *d, const moe_lora_weights *w, const vo
  *    batches of the hidden = intermediate = 2880, 32-expert layer fit up to
  *    about 100 tokens; a 6400-token prefill batch does not).
  *  - Every call on one GPU shares that GPU's array, which keeps the last
- *    call's contents (each call re-initialises what it reads: the routing
- *    launch clears its counters and status word, the alignment fills both
+ *    call's contents (each call re-initialises what it reads: its first
+ *    launch clears the counters and status word, the alignment fills both
  *    views to capacity). Calls that may overlap on one GPU (different
  *    streams, or host threads without ordering) RACE on the array: order
  *    them on one stream. The read-back calls below do not apply to it. */

@@ -57,6 +57,8 @@ __device__ __forceinline__ u32x4 ld16(const void* p) {
     return *reinterpret_cast<const u32x4*>(p);
 }
 
+// The same load with the non-temporal (streaming) cache policy, for data that
+// the launch reads exactly once.
 __device__ __forceinline__ u32x4 ld16_nt(const void* p) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }

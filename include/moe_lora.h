@@ -95,7 +95,11 @@ extern "C" {
  *     waves_gate_up, waves_down
  *                    16-row base blocks: waves per tile that split its K range
  *                    (1, 2 or 4; each wave keeps >= 4 chunks of 64); other
- *                    block sizes take only 1 */
+ *                    block sizes take only 1
+ *     frags_gate_up  16-row base blocks: 16-column weight fragments per gate_up
+ *                    wave, 4 (32 h columns) or 8 (64 h columns: half the
+ *                    waves, each with twice the bytes in flight; needs 16-row
+ *                    base blocks, one wave per tile and I a multiple of 64) */
 #define MOE_LORA_FLAG_OUT_BF16 1
 #define MOE_LORA_FLAG_SHRINK_LAUNCH 2
 #define MOE_LORA_FLAG_FUSED_COMBINE 4
@@ -106,6 +110,7 @@ typedef struct moe_lora_desc {
     int32_t block_m_base, block_m_lora;
     int32_t flags;
     int32_t down_ksplit, shrink_ksplit, waves_gate_up, waves_down;
+    int32_t frags_gate_up;
 } moe_lora_desc;
 
 /* Weights (device pointers, bf16 bits, 16-byte aligned).
@@ -166,11 +171,13 @@ int moe_lora_block_sizes(const moe_lora_desc *d, int32_t *block_m_base, int32_t 
  * T <= 16, E <= 32, top_k <= 8, T top_k <= 64, 16-row blocks, the shrinks
  * inside the projections or no LoRA, one wave per gate_up tile. The routing
  * and alignment are then written by that launch's first workgroup, in the
- * same layouts. Host only. */
+ * same layouts. frags_gate_up: fragments per 16-row gate_up wave (0 for
+ * other block sizes). Host only. */
 typedef struct moe_lora_plan_info {
     int32_t block_m_base, block_m_lora, down_ksplit, shrink_ksplit;
     int32_t waves_gate_up, waves_down, shrinks_in_projections, combine_in_down;
     int32_t routing_in_gate_up;
+    int32_t frags_gate_up;
 } moe_lora_plan_info;
 int moe_lora_plan(const moe_lora_desc *d, moe_lora_plan_info *info);
 

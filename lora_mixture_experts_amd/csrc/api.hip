@@ -27,6 +27,7 @@ struct Plan {
     int ksplit;  // K ranges of the down projection (partial sums summed by the combine)
     int ssplit;  // K ranges of the two shrinks (partials summed by the projection kernels)
     int ksw_gu, ksw_dn;  // 16-row blocks: waves per tile of the two projections
+    int fn_gu;           // 16-row blocks: 16-column fragments per gate_up wave
     bool fused;  // the shrinks run as producer waves inside the projection launches
     bool fuse_combine;  // the down projection adds its weighted rows into out (no D, no combine launch)
     bool local;  // the gate_up launch aligns the batch itself (no alignment launch)
@@ -108,7 +109,8 @@ int make_plan(const moe_lora_desc* d, Plan* p) {
     p->nblk_l = p->C_l / p->bm_l;
     // launch tuning: 0 = the library's choice; results do not depend on any
     // of these beyond the order of fp32 sums
-    if (d->down_ksplit < 0 || d->shrink_ksplit < 0 || d->waves_gate_up < 0 || d->waves_down < 0)
+    if (d->down_ksplit < 0 || d->shrink_ksplit < 0 || d->waves_gate_up < 0 || d->waves_down < 0 ||
+        d->frags_gate_up < 0)
         return MOE_LORA_EINVAL;
     p->ksplit = d->down_ksplit ? d->down_ksplit : gemm_down_ksplit(p->H, p->I, p->bm_b, p->nblk_b);
     // the direct-load kernels take the whole K range
@@ -118,6 +120,11 @@ int make_plan(const moe_lora_desc* d, Plan* p) {
     p->ksw_dn = d->waves_down ? d->waves_down : 1;
     if (p->bm_b != 16 && (p->ksw_gu != 1 || p->ksw_dn != 1)) return MOE_LORA_EINVAL;
     if (p->bm_b == 16 && (!skinny_waves_ok(p->H, 1, p->ksw_gu) || !skinny_waves_ok(p->I, p->ksplit, p->ksw_dn)))
+        return MOE_LORA_EINVAL;
+    // 8 fragments per gate_up wave: 16-row blocks, one wave per tile, I a
+    // multiple of 64 (whole 64-column tiles)
+    p->fn_gu = d->frags_gate_up ? d->frags_gate_up : 4;
+    if (p->fn_gu != 4 && (p->fn_gu != 8 || p->bm_b != 16 || p->ksw_gu != 1 || p->I % 64))
         return MOE_LORA_EINVAL;
     // the weighted combine runs in the down projection's epilogue (fp32
     // atomic adds into out) only on request: the atomics cost the down
@@ -260,6 +267,7 @@ int moe_lora_plan(const moe_lora_desc* d, moe_lora_plan_info* info) {
     info->down_ksplit = p.ksplit;
     info->shrink_ksplit = p.L > 0 ? p.ssplit : 0;
     info->waves_gate_up = p.bm_b == 16 ? p.ksw_gu : 0;
+    info->frags_gate_up = p.bm_b == 16 ? p.fn_gu : 0;
     info->waves_down = p.bm_b == 16 ? p.ksw_dn : 0;
     info->shrinks_in_projections = p.fused ? 1 : 0;
     info->combine_in_down = p.fuse_combine ? 1 : 0;
@@ -426,7 +434,7 @@ int forward_planned(const Plan& p, const moe_lora_desc* d, const moe_lora_weight
     ga.W = static_cast<const uint16_t*>(w->w_gate_up); ga.N_out = p.I; ga.K = p.H;
     ga.Wp = p.bm_b == 16 ? static_cast<const uint16_t*>(w->w_gate_up_packed) : nullptr;
     ga.S = s1; ga.Bl = static_cast<const uint16_t*>(w->b_gate_up);
-    ga.S_hl = s1hl; ga.s_hl_stride = s_hl_stride_of(p.r); ga.ksw = p.ksw_gu;
+    ga.S_hl = s1hl; ga.s_hl_stride = s_hl_stride_of(p.r); ga.ksw = p.ksw_gu; ga.frags = p.fn_gu;
     if (p.fused) {
         ga.prod_ncf = (p.r + 15) / 16;
         ga.prod_units = p.nblk_l * ga.prod_ncf * p.ssplit;

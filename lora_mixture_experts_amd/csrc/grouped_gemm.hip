@@ -103,6 +103,11 @@ __device__ __forceinline__ u32x4 load_lora_b(const GemmArgs& a, int Nw, int ad, 
 // ===========================================================================
 // Skinny variant: 16-row blocks (few rows per expert: the weights are
 // streamed from HBM once and each byte feeds at most 16 rows).
+
+// 16-column fragments per block of the packed weight copies (both
+// projections). A wave with more fragments (the 8-fragment gate_up form)
+// reads that many adjacent blocks per K chunk.
+constexpr int kPackFrags = 4;
 //
 // One wave is one workgroup and owns a 16-row x (16 FN)-column output tile
 // over the whole K range, so there is no cross-wave reduction, no LDS and no
@@ -418,18 +423,25 @@ __global__ __launch_bounds__(64 * KSW) void k_gemm_skinny(GemmArgs a) {
         }
     }
     // Weight operand: the 64 rows of the tile at the matrix pitch, or the
-    // packed copy, where the tile's 64-wide K chunk q is one 8 KiB block
-    // [fragment][half][lane][8] (lane = 16 g + lrow) and the blocks of
-    // consecutive chunks follow each other. wq, wh: elements per K chunk and
-    // per 16-byte half.
+    // packed copy, where a kPackFrags-fragment column tile's 64-wide K chunk q
+    // is one 8 KiB block [fragment][half][lane][8] (lane = 16 g + lrow) and
+    // the blocks of consecutive chunks follow each other; a wave of FN
+    // fragments reads FN / kPackFrags such tiles. wq, wh: elements per K
+    // chunk and per 16-byte half.
+    static_assert(FN % kPackFrags == 0, "whole packed tiles per wave");
     const uint16_t* wrow[FN];
     int wq, wh;
     if (a.Wp) {
-        const uint16_t* wt =
-            a.Wp + (static_cast<size_t>(e * n_tiles + tile) * (K / 64) + kbeg / 64) * (FN * 1024) + lane * 8;
+        constexpr int kTiles = FN / kPackFrags;
+        const uint16_t* wt = a.Wp +
+                             (static_cast<size_t>((e * n_tiles + tile) * kTiles) * (K / 64) + kbeg / 64) *
+                                 (kPackFrags * 1024) +
+                             lane * 8;
 #pragma unroll
-        for (int f = 0; f < FN; ++f) wrow[f] = wt + f * 1024;
-        wq = FN * 1024;
+        for (int f = 0; f < FN; ++f)
+            wrow[f] = wt + static_cast<size_t>(f / kPackFrags) * (K / 64) * (kPackFrags * 1024) +
+                      (f % kPackFrags) * 1024;
+        wq = kPackFrags * 1024;
         wh = 512;
     } else {
 #pragma unroll
@@ -1328,8 +1340,11 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_dma(GemmArgs a) {
 // leave a partial last tile.
 // 16-column weight fragments per skinny wave and register pipeline stages,
 // per projection (gate_up: fragments pair gate and up rows, so a wave writes
-// FN * 8 h columns; down: FN * 16 D columns)
+// FN * 8 h columns; down: FN * 16 D columns). The gate_up projection also has
+// an 8-fragment form (GemmArgs::frags, one wave per tile): half the waves,
+// each with twice the bytes per K chunk in flight.
 constexpr int kSkinnyFNGateUp = 4;
+constexpr int kSkinnyFNGateUpWide = 8;
 constexpr int kSkinnyNSGateUp = 2;
 constexpr int kSkinnyFNDown = 4;
 constexpr int kSkinnyNSDown = 2;
@@ -1387,7 +1402,7 @@ static hipError_t launch_tiled(const GemmArgs& a, hipStream_t s) {
 template <bool GATEUP>
 __global__ __launch_bounds__(256) void k_pack_skinny(const uint16_t* __restrict__ W, uint16_t* __restrict__ Wp,
                                                      int E, int N_out, int K) {
-    constexpr int FN = GATEUP ? kSkinnyFNGateUp : kSkinnyFNDown;
+    constexpr int FN = kPackFrags;
     constexpr int kCols = GATEUP ? FN * 8 : FN * 16;
     const int n_tiles = N_out / kCols, nq = K / 64;
     const int I = GATEUP ? N_out : 0;
@@ -1413,7 +1428,7 @@ __global__ __launch_bounds__(256) void k_pack_skinny(const uint16_t* __restrict_
 }
 
 bool pack_skinny_supported(int N_out, int K, int gate_up) {
-    const int cols = gate_up ? kSkinnyFNGateUp * 8 : kSkinnyFNDown * 16;
+    const int cols = gate_up ? kPackFrags * 8 : kPackFrags * 16;
     return N_out > 0 && K > 0 && N_out % cols == 0 && K % 64 == 0;
 }
 
@@ -1477,9 +1492,12 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
     if (a.L > 0 && a.S_hl && (a.s_split != 1 || a.s_hl_stride != s_hl_stride_of(a.r)))
         return hipErrorInvalidValue;
     if (a.bm_b == 16) {
-        const int cols = a.gate_up ? kSkinnyFNGateUp * 8 : kSkinnyFNDown * 16;
+        const bool wide = a.gate_up && a.frags == kSkinnyFNGateUpWide;
+        const int cols = a.gate_up ? a.frags * 8 : kSkinnyFNDown * 16;
         const int ksw = a.ksw;
         if (!(ksw == 1 || ksw == 2 || ksw == 4) || (a.K / a.ksplit) / 64 < ksw) return hipErrorInvalidValue;
+        if ((a.gate_up && a.frags != kSkinnyFNGateUp && !(wide && ksw == 1)) || a.N_out % cols)
+            return hipErrorInvalidValue;
         if (a.local && (!a.gate_up || ksw != 1 || (a.L > 0 && a.bm_l != 16) || !local_route_fits(a.T, a.E, a.top_k) ||
                         a.n_blocks != a.E || !a.adapter_ids || (!a.logits && !a.local_ids)))
             return hipErrorInvalidValue;
@@ -1494,7 +1512,9 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
         if (pair) hipLaunchKernelGGL((k_gemm_skinny<G, FN, NS, W, true>), grid, block, 0, s, a);     \
         else hipLaunchKernelGGL((k_gemm_skinny<G, FN, NS, W, false>), grid, block, 0, s, a);         \
     } while (0)
-        if (a.gate_up) {
+        if (wide) {
+            MOELORA_SKINNY(true, kSkinnyFNGateUpWide, kSkinnyNSGateUp, 1);
+        } else if (a.gate_up) {
             if (ksw == 1) MOELORA_SKINNY(true, kSkinnyFNGateUp, kSkinnyNSGateUp, 1);
             if (ksw == 2) MOELORA_SKINNY(true, kSkinnyFNGateUp, kSkinnyNSGateUp, 2);
             if (ksw == 4) MOELORA_SKINNY(true, kSkinnyFNGateUp, kSkinnyNSGateUp, 4);

@@ -119,6 +119,7 @@ struct GemmArgs {
     const float* topk_w;
     int ksplit;               // down only: the K range is cut into ksplit equal parts
     int ksw;                  // 16-row blocks: waves per tile splitting its K range (1, 2 or 4)
+    int frags;                // 16-row gate_up: 16-column fragments per wave (4, or 8 with ksw 1)
     // optional bf16 hi/lo copy of S (see ShrinkArgs); the direct-load kernel
     // then runs the expand as extra stages of its LDS pipeline
     const uint16_t* S_hl;

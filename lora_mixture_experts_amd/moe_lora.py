@@ -31,13 +31,14 @@ class MoeLoraError(RuntimeError):
 class Desc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("T", "H", "I", "E", "top_k", "L", "r", "block_m_base", "block_m_lora", "flags",
-                 "down_ksplit", "shrink_ksplit", "waves_gate_up", "waves_down")]
+                 "down_ksplit", "shrink_ksplit", "waves_gate_up", "waves_down", "frags_gate_up")]
 
 
 class PlanInfo(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("block_m_base", "block_m_lora", "down_ksplit", "shrink_ksplit", "waves_gate_up",
-                 "waves_down", "shrinks_in_projections", "combine_in_down", "routing_in_gate_up")]
+                 "waves_down", "shrinks_in_projections", "combine_in_down", "routing_in_gate_up",
+                 "frags_gate_up")]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}
@@ -109,13 +110,13 @@ def _check(rc: int, what: str):
 
 
 # launch tuning fields of the descriptor (0 = the library's choice)
-TUNING_FIELDS = ("down_ksplit", "shrink_ksplit", "waves_gate_up", "waves_down")
+TUNING_FIELDS = ("down_ksplit", "shrink_ksplit", "waves_gate_up", "waves_down", "frags_gate_up")
 
 
 def make_desc(T, H, I, E, top_k, L, r, block_m_base=0, block_m_lora=0, flags=0, down_ksplit=0,
-              shrink_ksplit=0, waves_gate_up=0, waves_down=0) -> Desc:
+              shrink_ksplit=0, waves_gate_up=0, waves_down=0, frags_gate_up=0) -> Desc:
     return Desc(T, H, I, E, top_k, L, r, block_m_base, block_m_lora, flags, down_ksplit, shrink_ksplit,
-                waves_gate_up, waves_down)
+                waves_gate_up, waves_down, frags_gate_up)
 
 
 def plan(desc: Desc) -> dict:

@@ -45,6 +45,8 @@ def split_candidates(case, plan):
                             if case.L > 0 and not plan["shrinks_in_projections"] else [])
     for f in ("waves_gate_up", "waves_down"):
         out[f] = [v for v in (1, 2, 4) if v != plan[f]] if plan["block_m_base"] == 16 else []
+    out["frags_gate_up"] = ([v for v in (4, 8) if v != plan["frags_gate_up"]]
+                            if plan["block_m_base"] == 16 and case.I % 64 == 0 else [])
     return out
 
 

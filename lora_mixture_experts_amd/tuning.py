@@ -7,8 +7,9 @@ kernels per shape and loads the tuned configurations from a user-supplied
 folder. Here a configuration is what the C ABI lets a caller choose without
 changing results: the row blocks of the two alignment views (which also pick
 each projection's tile shape), whether the LoRA shrinks get launches of their
-own, and the split-K factors: K ranges of the down projection and of the
-shrinks, and waves per tile of the 16-row projections. Any valid choice
+own, the split-K factors (K ranges of the down projection and of the
+shrinks, waves per tile of the 16-row projections) and the weight fragments
+per 16-row gate_up wave. Any valid choice
 computes the same layer (up to fp32 summation order); the table only decides
 speed.
 
@@ -19,9 +20,11 @@ A folder holds one JSON file per layer shape (written by
      "device": "gfx950",
      "entries": [{"T_max": 16, "block_m_base": 16, "block_m_lora": 16,
                   "shrink_launch": false, "down_ksplit": 0, "shrink_ksplit": 0,
-                  "waves_gate_up": 0, "waves_down": 0, "us": 307.9}, ...]}
+                  "waves_gate_up": 0, "waves_down": 0, "frags_gate_up": 0,
+                  "us": 307.9}, ...]}
 
-The four split-K keys are optional (0 or absent = the library's choice).
+The five launch keys after shrink_launch are optional (0 or absent = the
+library's choice).
 
 An entry covers the token counts ``T_min <= T <= T_max``; ``T_min`` is
 optional and defaults to ``T_max // 2 + 1``, so a choice tuned at one batch
@@ -38,7 +41,7 @@ from dataclasses import dataclass
 
 SHAPE_KEYS = ("H", "I", "E", "top_k", "L", "r")
 POW2_BLOCKS = (16, 32, 64, 128, 256)
-SPLIT_KEYS = ("down_ksplit", "shrink_ksplit", "waves_gate_up", "waves_down")
+SPLIT_KEYS = ("down_ksplit", "shrink_ksplit", "waves_gate_up", "waves_down", "frags_gate_up")
 
 
 @dataclass(frozen=True)
@@ -50,6 +53,7 @@ class Choice:
     shrink_ksplit: int = 0
     waves_gate_up: int = 0
     waves_down: int = 0
+    frags_gate_up: int = 0
 
 
 def choice_of(e) -> Choice:
@@ -90,6 +94,8 @@ def _check_entry(e, where):
     for key in ("waves_gate_up", "waves_down"):
         if e.get(key, 0) not in (0, 1, 2, 4):
             raise ValueError(f"{where}: {key} must be 0, 1, 2 or 4: {e}")
+    if e.get("frags_gate_up", 0) not in (0, 4, 8):
+        raise ValueError(f"{where}: frags_gate_up must be 0, 4 or 8: {e}")
 
 
 class Table:

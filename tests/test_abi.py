@@ -188,6 +188,7 @@ def test_plan_resolves_the_library_defaults():
     d = wl.CONFIGS["decode"]
     p = ml.plan(ml.make_desc(d["T"], d["H"], d["I"], d["E"], d["top_k"], d["L"], d["r"]))
     assert p["block_m_base"] == 16 and p["down_ksplit"] == 1 and p["waves_gate_up"] == 1
+    assert p["frags_gate_up"] == 4
     assert p["shrinks_in_projections"] == 1 and p["combine_in_down"] == 0
     # the decode-shaped batch is aligned inside the gate_up launch (its
     # 4 x 32 top-k scan stays in the routing launch), unless the routing
@@ -216,6 +217,9 @@ def test_plan_resolves_the_library_defaults():
     dict(waves_gate_up=3), dict(waves_down=8),
     dict(waves_down=2, bm_b=32),                          # waves per tile only for 16-row blocks
     dict(waves_down=4, down_ksplit=3),                    # 15 chunks per range < 4 per wave x 4
+    dict(frags_gate_up=6), dict(frags_gate_up=-4),        # 4 or 8 fragments per gate_up wave
+    dict(frags_gate_up=8, bm_b=32),                       # only the 16-row kernel has them
+    dict(frags_gate_up=8, waves_gate_up=2),               # 8 only with one wave per tile
 ])
 def test_validate_rejects_bad_split_fields(over):
     over = dict(over)
@@ -223,6 +227,18 @@ def test_validate_rejects_bad_split_fields(over):
     d = wl.CONFIGS["decode"]
     ds = ml.make_desc(d["T"], d["H"], d["I"], d["E"], d["top_k"], d["L"], d["r"], bm_b, 0, **over)
     assert ml.validate(ds) == ml.EINVAL
+
+
+def test_gate_up_fragments_follow_the_shape():
+    # the plan reports the fragments per gate_up wave only for 16-row blocks
+    # (8 of them cover 64 h columns; I is always a multiple of 64, the down
+    # projection's K chunk)
+    d = wl.CONFIGS["decode"]
+    args = (d["T"], d["H"], d["I"], d["E"], d["top_k"], d["L"], d["r"])
+    assert ml.plan(ml.make_desc(*args, frags_gate_up=8))["frags_gate_up"] == 8
+    assert ml.plan(ml.make_desc(*args, frags_gate_up=4))["frags_gate_up"] == 4
+    assert ml.plan(ml.make_desc(*args, block_m_base=64))["frags_gate_up"] == 0
+    assert ml.validate(ml.make_desc(*args, block_m_base=64, frags_gate_up=4)) == ml.OK
 
 
 def test_split_fields_change_only_the_plan_and_workspace():

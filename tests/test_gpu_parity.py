@@ -259,7 +259,9 @@ LOCAL_CASES = [("tiny", {}, {}), ("decode", {}, {}), ("dense", {}, {}),
                ("noL", dict(T=16, H=128, I=192, E=20, top_k=4, L=0, r=8), {}),
                ("t1", dict(T=1, H=64, I=64, E=3, top_k=2, L=2, r=8), {}),
                ("t13", dict(T=13, H=64, I=128, E=32, top_k=3, L=40, r=32), {}),
-               ("ties", dict(T=16, H=64, I=64, E=24, top_k=4, L=3, r=8), dict(ties=True))]
+               ("ties", dict(T=16, H=64, I=64, E=24, top_k=4, L=3, r=8), dict(ties=True)),
+               ("dense", {}, dict(frags_gate_up=8)),
+               ("t13", dict(T=13, H=64, I=128, E=32, top_k=3, L=40, r=32), dict(frags_gate_up=8))]
 
 
 @pytest.mark.parametrize("name,dims,opts", LOCAL_CASES)
@@ -356,6 +358,9 @@ SPLIT_CASES = [
     ("decode", None, (16, 16), dict(waves_gate_up=2, waves_down=2)),
     ("decode", None, (16, 16), dict(waves_gate_up=4, waves_down=2, down_ksplit=3)),
     ("decode", None, (16, 16), dict(down_ksplit=5)),
+    # 8 weight fragments per gate_up wave (64 h columns per tile)
+    ("decode", None, (16, 16), dict(frags_gate_up=8)),
+    ("dense", None, (16, 16), dict(frags_gate_up=8)),
     # 32- and 64-row blocks: down K ranges and separate shrinks split over K
     ("wide", None, (32, 16), dict(down_ksplit=4, shrink_ksplit=2)),
     ("kdown", dict(T=40, H=256, I=1024, E=3, top_k=2, L=2, r=16), (64, 16), dict(down_ksplit=16, shrink_ksplit=3)),
@@ -577,6 +582,9 @@ PACKED_CASES = [("decode", None, {}, False), ("dense", None, {}, False), ("tiny"
                 ("odd", dict(T=5, H=320, I=448, E=3, top_k=2, L=2, r=16), {}, False),
                 ("decode", None, dict(down_ksplit=3, waves_gate_up=2, waves_down=2), False),
                 ("decode", None, {}, True),
+                ("decode", None, dict(frags_gate_up=8), False),
+                ("dense", None, dict(frags_gate_up=8), False),
+                ("odd", dict(T=5, H=320, I=448, E=3, top_k=2, L=2, r=16), dict(frags_gate_up=8), False),
                 ("wide", None, {}, False),
                 ("wide", None, dict(block_m_base=32, down_ksplit=4), False),
                 ("tiles", dict(T=300, H=320, I=448, E=4, top_k=2, L=3, r=32), dict(block_m_base=128), False),
@@ -634,7 +642,8 @@ def _sweep_setup(i):
                 shrink_launch=bool(rng.integers(0, 2)), fused_combine=bool(rng.random() < 0.3),
                 out_bf16=bool(rng.random() < 0.2), packed_weights=bool(rng.integers(0, 2)))
     launch = dict(down_ksplit=int(rng.choice([0, 0, 2, 3, 5])), shrink_ksplit=int(rng.choice([0, 0, 2, 4])),
-                  waves_gate_up=int(rng.choice([0, 0, 2, 4])), waves_down=int(rng.choice([0, 0, 2, 4])))
+                  waves_gate_up=int(rng.choice([0, 0, 2, 4])), waves_down=int(rng.choice([0, 0, 2, 4])),
+                  frags_gate_up=int(rng.choice([0, 0, 8])))
 
     def valid(o, ln):
         flags = ((ml.FLAG_OUT_BF16 if o["out_bf16"] else 0) | (ml.FLAG_SHRINK_LAUNCH if o["shrink_launch"] else 0) |
@@ -643,7 +652,7 @@ def _sweep_setup(i):
                          o["block_m_base"], o["block_m_lora"], flags, **ln)
         return ml.validate(d) == ml.OK
 
-    for drop in ("waves_down", "waves_gate_up", "shrink_ksplit", "down_ksplit"):
+    for drop in ("frags_gate_up", "waves_down", "waves_gate_up", "shrink_ksplit", "down_ksplit"):
         if valid(opts, launch):
             break
         launch[drop] = 0

@@ -35,6 +35,10 @@ MIN_OCCUPANCY = {
     "k_gemm_skinny<true, 4, 2, 4, true>": 2,
     "k_gemm_skinny<false, 4, 2, 2, true>": 2,
     "k_gemm_skinny<false, 4, 2, 4, true>": 2,
+    # the 8-fragment gate_up form: one wave per SIMD, for grids of fewer
+    # tiles than SIMDs (a tuning option)
+    "k_gemm_skinny<true, 8, 2, 1, false>": 1,
+    "k_gemm_skinny<true, 8, 2, 1, true>": 1,
     "k_gemm_tiled<32, 128, 1, 4, true>": 4,
     "k_gemm_tiled<32, 128, 1, 4, false>": 4,
     "k_gemm_tiled<64, 128, 2, 2, true>": 3,

@@ -28,6 +28,7 @@ struct Plan {
     int ssplit;  // K ranges of the two shrinks (partials summed by the projection kernels)
     int ksw_gu, ksw_dn;  // 16-row blocks: waves per tile of the two projections
     int fn_gu;           // 16-row blocks: 16-column fragments per gate_up wave
+    bool w_stream;       // direct-load kernels: weights read with the non-temporal policy
     bool fused;  // the shrinks run as producer waves inside the projection launches
     bool fuse_combine;  // the down projection adds its weighted rows into out (no D, no combine launch)
     bool local;  // the gate_up launch aligns the batch itself (no alignment launch)
@@ -126,6 +127,13 @@ int make_plan(const moe_lora_desc* d, Plan* p) {
     p->fn_gu = d->frags_gate_up ? d->frags_gate_up : 4;
     if (p->fn_gu != 4 && (p->fn_gu != 8 || p->bm_b != 16 || p->ksw_gu != 1 || p->I % 64))
         return MOE_LORA_EINVAL;
+    // 128- and 256-row blocks with at most half a block of rows per expert on
+    // average: nearly every expert has one block, whose column tiles read
+    // each weight tile once, and those loads take the non-temporal policy
+    // (many-adapter layer, 64 rows per expert: 619 -> 609 us). With more rows
+    // per expert the blocks of an expert share its weight tiles through the
+    // L2 (the prefill-shaped layer with the policy: 1516 -> 1996 us).
+    p->w_stream = p->bm_b >= 128 && static_cast<long>(p->P) * 2 <= static_cast<long>(p->E) * p->bm_b;
     // the weighted combine runs in the down projection's epilogue (fp32
     // atomic adds into out) only on request: the atomics cost the down
     // projection more than the fixed-order combine launch takes at every
@@ -435,6 +443,7 @@ int forward_planned(const Plan& p, const moe_lora_desc* d, const moe_lora_weight
     ga.Wp = p.bm_b == 16 ? static_cast<const uint16_t*>(w->w_gate_up_packed) : nullptr;
     ga.S = s1; ga.Bl = static_cast<const uint16_t*>(w->b_gate_up);
     ga.S_hl = s1hl; ga.s_hl_stride = s_hl_stride_of(p.r); ga.ksw = p.ksw_gu; ga.frags = p.fn_gu;
+    ga.w_stream = p.w_stream;
     if (p.fused) {
         ga.prod_ncf = (p.r + 15) / 16;
         ga.prod_units = p.nblk_l * ga.prod_ncf * p.ssplit;

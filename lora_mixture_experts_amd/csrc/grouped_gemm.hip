@@ -1099,18 +1099,34 @@ __device__ __forceinline__ void dma16(const void* g, const uint16_t* lds) {
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(l), "v"(g) : "m0", "memory");
 }
 
+// The same with the non-temporal cache policy (data the launch reads once).
+__device__ __forceinline__ void dma16_nt(const void* g, const uint16_t* lds) {
+    const uint32_t l = static_cast<uint32_t>(
+        reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)(lds)));
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off nt" ::"s"(l), "v"(g) : "m0", "memory");
+}
+
 // workgroup barrier without the memory fence of __syncthreads (that fence
 // would wait for the stages requested ahead); the memory clobber keeps the
 // compiler from moving LDS accesses across it
 __device__ __forceinline__ void bare_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
+// One stage's activation (A) and weight (B) tiles. w_once: each weight tile
+// is read by about one block of rows (GemmArgs::w_stream), so its loads
+// carry the non-temporal policy; the activation rows, which every column
+// tile reads again, keep the default one.
 template <int A_PW, int B_PW>
 __device__ __forceinline__ void dma_issue(const uint16_t* const* asrc, const uint16_t* const* bsrc,
-                                          uint16_t* ab, uint16_t* bb, int wave, int k0) {
+                                          uint16_t* ab, uint16_t* bb, int wave, int k0, bool w_once) {
 #pragma unroll
     for (int i = 0; i < A_PW; ++i) dma16(asrc[i] + k0, ab + (wave * A_PW + i) * 512);
+    if (w_once) {
 #pragma unroll
-    for (int i = 0; i < B_PW; ++i) dma16(bsrc[i] + k0, bb + (wave * B_PW + i) * 512);
+        for (int i = 0; i < B_PW; ++i) dma16_nt(bsrc[i] + k0, bb + (wave * B_PW + i) * 512);
+    } else {
+#pragma unroll
+        for (int i = 0; i < B_PW; ++i) dma16(bsrc[i] + k0, bb + (wave * B_PW + i) * 512);
+    }
 }
 
 // Multiply the stage held in (ca, cb) into the accumulators: per 32-wide K
@@ -1277,7 +1293,7 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_dma(GemmArgs a) {
     const int nk_all = nk + nruns * spr;
     auto issue = [&](int stage, uint16_t* ab, uint16_t* bb) {
         if (stage < nk) {
-            dma_issue<A_PW, B_PW>(asrc, bsrc, ab, bb, wave, stage * 64);
+            dma_issue<A_PW, B_PW>(asrc, bsrc, ab, bb, wave, stage * 64, a.w_stream != 0);
             return;
         }
         const int t = stage - nk, q = t / spr, sub = t - q * spr;

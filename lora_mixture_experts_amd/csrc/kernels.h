@@ -120,6 +120,7 @@ struct GemmArgs {
     int ksplit;               // down only: the K range is cut into ksplit equal parts
     int ksw;                  // 16-row blocks: waves per tile splitting its K range (1, 2 or 4)
     int frags;                // 16-row gate_up: 16-column fragments per wave (4, or 8 with ksw 1)
+    int w_stream;             // 128/256-row blocks: weight tiles read by about one block each (nt loads)
     // optional bf16 hi/lo copy of S (see ShrinkArgs); the direct-load kernel
     // then runs the expand as extra stages of its LDS pipeline
     const uint16_t* S_hl;

@@ -190,39 +190,6 @@ __device__ __forceinline__ uint32_t wave_or(uint32_t x) {
     return static_cast<uint32_t>(__builtin_amdgcn_readlane(v, 63));
 }
 
-// A gate_up projection wave on expert e (wave-uniform): the first slot of
-// e's base block (-1 if no token chose e); lane l gets the pair in row l & 15
-// and its adapter' (-1 and L for a padding row). With at most 16 tokens
-// every used expert holds exactly one 16-row block, so e's block follows
-// those of the used experts below e. The rows pass through LDS (ls, also
-// the logits' staging area, no longer read by then).
-__device__ __forceinline__ int local_expert_rows(const float* logits, const int32_t* adapter_ids, int T, int E,
-                                                 int k, int L, int e, float* ls, const int32_t* ids, int& row_p,
-                                                 int& row_ad) {
-    const int lane = threadIdx.x & 63;
-    const TokenPicks tp = local_picks(logits, adapter_ids, T, E, k, L, ls, ids);
-    const uint32_t used = wave_or(tp.mask);
-    row_p = -1;
-    row_ad = L;
-    if (!((used >> e) & 1u)) return -1;
-    const int ebase = 16 * __popc(used & ((1u << e) - 1u));
-    bool in_e;
-    int j_of_e;
-    const int row = local_row_in_expert(tp, e, L, in_e, j_of_e);
-    const int ne = popc64(ballot64(in_e));
-    int* rows = reinterpret_cast<int*>(ls);
-    if (in_e) {
-        rows[2 * row] = lane * k + j_of_e;
-        rows[2 * row + 1] = tp.ad;
-    }
-    const int lrow = lane & 15;
-    if (lrow < ne) {
-        row_p = rows[2 * lrow];
-        row_ad = rows[2 * lrow + 1];
-    }
-    return ebase;
-}
-
 // A gate_up projection wave on expert e (wave-uniform) whose 16 MFMA rows
 // are the batch's tokens (row r = token r): lane l learns whether token l & 15
 // chose e, that pair's slot in e's base block and the token's adapter'.

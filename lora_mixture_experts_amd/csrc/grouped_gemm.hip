@@ -603,16 +603,16 @@ __global__ __launch_bounds__(64 * KSW) void k_gemm_skinny(GemmArgs a) {
     };
     if (lora && !late) expand(std::false_type{}, acc);
 
-    // With the producers in this launch, the gate_up expand runs half-way
-    // through the K loop if they are done by then (one poll), so that its
-    // load latency is hidden while the other waves keep HBM busy; otherwise
-    // after the loop. On the decode-shaped layer the producers finish within
-    // the first 45 % of the gate_up launch, so the waves that finish last,
-    // which set the launch's length, expand mid-stream (gate_up 191 -> 187 us).
-    // The down projection expands after its loop: a poll half-way or three
-    // quarters through measured 2-5 us slower there.
+    // With the producers in this launch, the expand runs half-way through
+    // the K loop if they are done by then (one poll), so that its load
+    // latency is hidden while the other waves keep HBM busy; otherwise after
+    // the loop. On the decode-shaped layer the producers finish within the
+    // first 45 % of the gate_up launch, so the waves that finish last, which
+    // set the launch's length, expand mid-stream (gate_up 191 -> 187 us). With
+    // the non-temporal weight loads the same holds for the down projection
+    // (down 91.5 -> 90.0 us; a poll three quarters through: 100 us).
     const int target = !late ? 0 : local ? local_target : producer_target(a);
-    const int q_mid = GATEUP ? nq / 2 / NS * NS : nq;
+    const int q_mid = nq / 2 / NS * NS;
     bool expanded = !late;
 
     // NS-stage register pipeline: chunk c sits in buffer c % NS and is

@@ -603,16 +603,17 @@ __global__ __launch_bounds__(64 * KSW) void k_gemm_skinny(GemmArgs a) {
     };
     if (lora && !late) expand(std::false_type{}, acc);
 
-    // With the producers in this launch, the expand runs half-way through
-    // the K loop if they are done by then (one poll), so that its load
-    // latency is hidden while the other waves keep HBM busy; otherwise after
-    // the loop. On the decode-shaped layer the producers finish within the
-    // first 45 % of the gate_up launch, so the waves that finish last, which
-    // set the launch's length, expand mid-stream (gate_up 191 -> 187 us). With
-    // the non-temporal weight loads the same holds for the down projection
-    // (down 91.5 -> 90.0 us; a poll three quarters through: 100 us).
+    // With the producers in this launch, the expand runs a third of the way
+    // through the K loop if they are done by then (one poll), so that its
+    // load latency is hidden while the other waves keep HBM busy; otherwise
+    // after the loop. The waves that finish last, which set the launch's
+    // length, then expand mid-stream. Measured on the decode-shaped layer
+    // with the non-temporal weight loads (µs per call): poll after the loop
+    // in the down projection and half-way in gate_up 262.5, half-way in both
+    // 260.8, a third 258.6, a quarter 259.4, a sixth 261.8 (dense layer
+    // 143.5 -> 150.1 there), three quarters in the down projection 271.
     const int target = !late ? 0 : local ? local_target : producer_target(a);
-    const int q_mid = nq / 2 / NS * NS;
+    const int q_mid = nq / 3 / NS * NS;
     bool expanded = !late;
 
     // NS-stage register pipeline: chunk c sits in buffer c % NS and is
